@@ -1,0 +1,363 @@
+/*
+ * ja_oracle.c -- plain fp64 CPU oracle for jagged attention.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the product path. It shares no code
+ * with the HIP library. The definitions it follows are quoted by section in
+ * ja_oracle.h; every loop below is the textbook definition written out, with
+ * no blocking, fusion or reordering.
+ */
+#include "ja_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ---- element decoding (exact widening to double) ---------------------- */
+
+static double elem(const void* p, int dtype, int64_t idx) {
+    if (dtype == ORA_F64) return ((const double*)p)[idx];
+    if (dtype == ORA_F32) return (double)((const float*)p)[idx];
+    /* bf16: the 16 stored bits are the upper half of an IEEE binary32. */
+    uint32_t bits = (uint32_t)((const uint16_t*)p)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ---- activations ---------------------------------------------------------
+ * GDPA section: an element-wise activation (GELU or SiLU) replaces softmax.
+ * SiLU is x * sigmoid(x); GELU is the tanh form named in the same section. */
+
+static double act_silu(double x) { return x / (1.0 + exp(-x)); }
+
+static double act_gelu_tanh(double x) {
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+}
+
+/* Derivatives, used by the pointwise backward. */
+static double dact_silu(double x) {
+    double s = 1.0 / (1.0 + exp(-x));
+    return s + x * s * (1.0 - s);
+}
+
+static double dact_gelu_tanh(double x) {
+    const double c = sqrt(2.0 / M_PI);
+    double u = c * (x + 0.044715 * x * x * x);
+    double t = tanh(u);
+    double du = c * (1.0 + 3.0 * 0.044715 * x * x);
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * du;
+}
+
+static double act_apply(int act, double x) {
+    return act == ORA_SILU ? act_silu(x) : act_gelu_tanh(x);
+}
+
+static double act_deriv(int act, double x) {
+    return act == ORA_SILU ? dact_silu(x) : dact_gelu_tanh(x);
+}
+
+/* ---- visibility ----------------------------------------------------------
+ * Query i sees key j (both local to their sequence) iff j < Lk, and
+ * causal => j <= i, and window W > 0 => (causal ? i - j < W : |i - j| < W). */
+static int visible(int64_t i, int64_t j, int64_t Lk, int causal, int32_t window) {
+    if (j < 0 || j >= Lk) return 0;
+    if (causal && j > i) return 0;
+    if (window > 0) {
+        int64_t diff = i - j;
+        if (!causal && diff < 0) diff = -diff;
+        if (diff >= window) return 0;
+    }
+    return 1;
+}
+
+/* ---- work distribution over (b, h) pairs ------------------------------ */
+
+typedef struct {
+    const void *q, *k, *v, *dout;
+    int dtype;
+    const int32_t *q_off, *k_off;
+    int32_t B, H, d;
+    int act, causal;
+    int32_t window;
+    double scale;
+    const uint8_t* pair_mask;
+    double *out, *lse, *dq, *dk, *dv;
+    int64_t next; /* next pair to claim */
+    int status;
+} job_t;
+
+static int64_t claim(job_t* J) { return __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED); }
+
+/* s_ij = scale * sum_c Q[qo+i,h,c] K[ko+j,h,c], summed in ascending c. */
+static double score(const job_t* J, int64_t qrow, int64_t krow, int32_t h) {
+    const int64_t H = J->H, d = J->d;
+    double acc = 0.0;
+    for (int64_t c = 0; c < d; ++c)
+        acc += elem(J->q, J->dtype, (qrow * H + h) * d + c) *
+               elem(J->k, J->dtype, (krow * H + h) * d + c);
+    return J->scale * acc;
+}
+
+/* Forward of one (b, h) pair: the plain definition, row by row. */
+static void fwd_pair(job_t* J, int32_t b, int32_t h) {
+    const int64_t H = J->H, d = J->d;
+    const int64_t qo = J->q_off[b], ko = J->k_off[b];
+    const int64_t Lq = J->q_off[b + 1] - qo, Lk = J->k_off[b + 1] - ko;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    for (int64_t i = 0; i < Lq; ++i) {
+        for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+        double lse_i = NAN;
+        if (J->act == ORA_SOFTMAX) {
+            double m = -INFINITY;
+            int64_t n = 0;
+            for (int64_t j = 0; j < Lk; ++j) {
+                if (!visible(i, j, Lk, J->causal, J->window)) continue;
+                s[j] = score(J, qo + i, ko + j, (int32_t)h);
+                if (s[j] > m) m = s[j];
+                ++n;
+            }
+            if (n == 0) {
+                lse_i = -INFINITY;
+            } else {
+                double l = 0.0;
+                for (int64_t j = 0; j < Lk; ++j)
+                    if (visible(i, j, Lk, J->causal, J->window)) l += exp(s[j] - m);
+                for (int64_t j = 0; j < Lk; ++j) {
+                    if (!visible(i, j, Lk, J->causal, J->window)) continue;
+                    double p = exp(s[j] - m);
+                    for (int64_t c = 0; c < d; ++c)
+                        o[c] += p * elem(J->v, J->dtype, ((ko + j) * H + h) * d + c);
+                }
+                for (int64_t c = 0; c < d; ++c) o[c] /= l;
+                lse_i = m + log(l);
+            }
+        } else {
+            for (int64_t j = 0; j < Lk; ++j) {
+                if (!visible(i, j, Lk, J->causal, J->window)) continue;
+                double a = act_apply(J->act, score(J, qo + i, ko + j, (int32_t)h));
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] += a * elem(J->v, J->dtype, ((ko + j) * H + h) * d + c);
+            }
+            if (Lk > 0)
+                for (int64_t c = 0; c < d; ++c) o[c] /= (double)Lk;
+        }
+        for (int64_t c = 0; c < d; ++c) J->out[((qo + i) * H + h) * d + c] = o[c];
+        if (J->lse) J->lse[(qo + i) * H + h] = lse_i;
+    }
+    free(s);
+    free(o);
+}
+
+/* Backward of one (b, h) pair. Softmax: P_ij = exp(s_ij - lse_i),
+ * D_i = sum_c dO_ic O_ic, dV_j = sum_i P_ij dO_i, dP_ij = dO_i . V_j,
+ * dS_ij = P_ij (dP_ij - D_i), dQ_i = scale sum_j dS_ij K_j,
+ * dK_j = scale sum_i dS_ij Q_i. Pointwise: the weight is act(s_ij)/Lk, and
+ * dS_ij = act'(s_ij) dP_ij / Lk. O and lse are the oracle's own. */
+static void bwd_pair(job_t* J, int32_t b, int32_t h) {
+    const int64_t H = J->H, d = J->d;
+    const int64_t qo = J->q_off[b], ko = J->k_off[b];
+    const int64_t Lq = J->q_off[b + 1] - qo, Lk = J->k_off[b + 1] - ko;
+    fwd_pair(J, b, h); /* writes out and lse rows of this pair */
+    double* lse_local = (double*)malloc(sizeof(double) * (size_t)(Lq > 0 ? Lq : 1));
+    /* The softmax backward needs lse; when the caller passed no lse buffer
+     * recompute it row by row here. */
+    for (int64_t i = 0; i < Lq; ++i) {
+        if (J->act != ORA_SOFTMAX) { lse_local[i] = NAN; continue; }
+        if (J->lse) { lse_local[i] = J->lse[(qo + i) * H + h]; continue; }
+        double m = -INFINITY;
+        for (int64_t j = 0; j < Lk; ++j)
+            if (visible(i, j, Lk, J->causal, J->window)) {
+                double sj = score(J, qo + i, ko + j, (int32_t)h);
+                if (sj > m) m = sj;
+            }
+        double l = 0.0;
+        for (int64_t j = 0; j < Lk; ++j)
+            if (visible(i, j, Lk, J->causal, J->window))
+                l += exp(score(J, qo + i, ko + j, (int32_t)h) - m);
+        lse_local[i] = (m == -INFINITY) ? -INFINITY : m + log(l);
+    }
+    for (int64_t i = 0; i < Lq; ++i)
+        for (int64_t c = 0; c < d; ++c) J->dq[((qo + i) * H + h) * d + c] = 0.0;
+    for (int64_t j = 0; j < Lk; ++j)
+        for (int64_t c = 0; c < d; ++c) {
+            J->dk[((ko + j) * H + h) * d + c] = 0.0;
+            J->dv[((ko + j) * H + h) * d + c] = 0.0;
+        }
+    for (int64_t i = 0; i < Lq; ++i) {
+        const int64_t qi = ((qo + i) * H + h) * d;
+        double Di = 0.0;
+        if (J->act == ORA_SOFTMAX)
+            for (int64_t c = 0; c < d; ++c) Di += elem(J->dout, J->dtype, qi + c) * J->out[qi + c];
+        for (int64_t j = 0; j < Lk; ++j) {
+            if (!visible(i, j, Lk, J->causal, J->window)) continue;
+            const int64_t kj = ((ko + j) * H + h) * d;
+            double sij = score(J, qo + i, ko + j, (int32_t)h);
+            double p, dsfac;
+            double dp = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                dp += elem(J->dout, J->dtype, qi + c) * elem(J->v, J->dtype, kj + c);
+            if (J->act == ORA_SOFTMAX) {
+                p = exp(sij - lse_local[i]);
+                dsfac = p * (dp - Di);
+            } else {
+                p = act_apply(J->act, sij) / (double)Lk;
+                dsfac = act_deriv(J->act, sij) * dp / (double)Lk;
+            }
+            for (int64_t c = 0; c < d; ++c) {
+                J->dv[kj + c] += p * elem(J->dout, J->dtype, qi + c);
+                J->dq[qi + c] += J->scale * dsfac * elem(J->k, J->dtype, kj + c);
+                J->dk[kj + c] += J->scale * dsfac * elem(J->q, J->dtype, qi + c);
+            }
+        }
+    }
+    free(lse_local);
+}
+
+static void* worker(void* arg) {
+    job_t* J = (job_t*)arg;
+    const int64_t npairs = (int64_t)J->B * J->H;
+    for (;;) {
+        int64_t p = claim(J);
+        if (p >= npairs) break;
+        if (J->pair_mask && !J->pair_mask[p]) continue;
+        int32_t b = (int32_t)(p / J->H), h = (int32_t)(p % J->H);
+        if (J->dq) bwd_pair(J, b, h);
+        else fwd_pair(J, b, h);
+    }
+    return NULL;
+}
+
+int ora_num_threads(void) {
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+static int run(job_t* J, int nthreads) {
+    if (nthreads <= 0) nthreads = ora_num_threads();
+    if ((int64_t)nthreads > (int64_t)J->B * J->H) nthreads = (int)((int64_t)J->B * J->H);
+    if (nthreads < 1) return 0;
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t)
+        if (pthread_create(&th[t], NULL, worker, J) == 0) ++started;
+    if (started == 0) worker(J);
+    for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    free(th);
+    return 0;
+}
+
+static int check_common(const int32_t* q_off, const int32_t* k_off, int32_t B, int32_t H,
+                        int32_t d, int act, int32_t window) {
+    if (!q_off || !k_off || B < 0 || H < 1 || d < 1 || window < 0) return -1;
+    if (act != ORA_SOFTMAX && act != ORA_SILU && act != ORA_GELU_TANH) return -1;
+    if (q_off[0] != 0 || k_off[0] != 0) return -1;
+    for (int32_t b = 0; b < B; ++b)
+        if (q_off[b + 1] < q_off[b] || k_off[b + 1] < k_off[b]) return -1;
+    return 0;
+}
+
+int ora_fwd(const void* q, const void* k, const void* v, int dtype,
+            const int32_t* q_off, const int32_t* k_off,
+            int32_t B, int32_t H, int32_t d,
+            int act, int causal, int32_t window, double scale,
+            const uint8_t* pair_mask, double* out, double* lse, int nthreads) {
+    if (check_common(q_off, k_off, B, H, d, act, window) || !out) return -1;
+    if (dtype != ORA_F32 && dtype != ORA_BF16 && dtype != ORA_F64) return -1;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dtype = dtype;
+    J.q_off = q_off; J.k_off = k_off; J.B = B; J.H = H; J.d = d;
+    J.act = act; J.causal = causal != 0; J.window = window; J.scale = scale;
+    J.pair_mask = pair_mask; J.out = out; J.lse = lse;
+    return run(&J, nthreads);
+}
+
+int ora_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+            const int32_t* q_off, const int32_t* k_off,
+            int32_t B, int32_t H, int32_t d,
+            int act, int causal, int32_t window, double scale,
+            const uint8_t* pair_mask, double* out, double* lse,
+            double* dq, double* dk, double* dv, int nthreads) {
+    if (check_common(q_off, k_off, B, H, d, act, window)) return -1;
+    if (!out || !dq || !dk || !dv || !dout) return -1;
+    if (dtype != ORA_F32 && dtype != ORA_BF16 && dtype != ORA_F64) return -1;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dout = dout; J.dtype = dtype;
+    J.q_off = q_off; J.k_off = k_off; J.B = B; J.H = H; J.d = d;
+    J.act = act; J.causal = causal != 0; J.window = window; J.scale = scale;
+    J.pair_mask = pair_mask; J.out = out; J.lse = lse;
+    J.dq = dq; J.dk = dk; J.dv = dv;
+    return run(&J, nthreads);
+}
+
+/* ---- reference work list ---------------------------------------------- */
+
+typedef struct { int32_t b, t, cost, key; } item_t;
+
+static int item_cmp(const void* pa, const void* pb) {
+    const item_t* a = (const item_t*)pa;
+    const item_t* c = (const item_t*)pb;
+    if (a->key != c->key) return a->key > c->key ? -1 : 1; /* descending */
+    if (a->b != c->b) return a->b < c->b ? -1 : 1;
+    if (a->t != c->t) return a->t < c->t ? -1 : 1;
+    return 0;
+}
+
+int64_t ora_tile_list(const int32_t* row_off, const int32_t* col_off, int32_t B,
+                      int32_t BM, int32_t BN, int causal, int32_t window,
+                      int transposed, int32_t cap,
+                      int32_t* items, int32_t* costs, int64_t max_items) {
+    if (!row_off || !col_off || B < 0 || BM < 1 || BN < 1 || window < 0 || cap < 1) return -1;
+    int64_t n = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        int64_t L = row_off[b + 1] - row_off[b];
+        if (L < 0) return -1;
+        n += (L + BM - 1) / BM;
+    }
+    if (n > max_items) return -1;
+    item_t* it = (item_t*)malloc(sizeof(item_t) * (size_t)(n > 0 ? n : 1));
+    int64_t m = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        int64_t Lr = row_off[b + 1] - row_off[b], Lc = col_off[b + 1] - col_off[b];
+        for (int64_t t = 0; t * BM < Lr; ++t) {
+            int64_t r0 = t * BM, r1 = r0 + BM < Lr ? r0 + BM : Lr; /* rows [r0, r1) */
+            /* Visible columns of any row in [r0, r1): brute force over the
+             * definition, so this reference does not rely on a closed form. */
+            int64_t lo = -1, hi = -1;
+            for (int64_t c = 0; c < Lc; ++c) {
+                int any = 0;
+                for (int64_t r = r0; r < r1 && !any; ++r) {
+                    /* not transposed: rows are queries i, columns keys j;
+                     * transposed: rows are keys j, columns queries i. */
+                    any = transposed ? visible(c, r, Lr, causal, window)
+                                     : visible(r, c, Lc, causal, window);
+                }
+                if (any) {
+                    if (lo < 0) lo = c;
+                    hi = c + 1;
+                }
+            }
+            int32_t cost = 0;
+            if (lo >= 0) cost = (int32_t)((hi + BN - 1) / BN - lo / BN);
+            it[m].b = b;
+            it[m].t = (int32_t)t;
+            it[m].cost = cost;
+            it[m].key = cost < cap ? cost : cap;
+            ++m;
+        }
+    }
+    qsort(it, (size_t)m, sizeof(item_t), item_cmp);
+    for (int64_t i = 0; i < m; ++i) {
+        items[2 * i] = it[i].b;
+        items[2 * i + 1] = it[i].t;
+        costs[i] = it[i].cost;
+    }
+    free(it);
+    return m;
+}

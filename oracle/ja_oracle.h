@@ -1,0 +1,93 @@
+/*
+ * ja_oracle.h -- fp64 CPU oracle for jagged attention (test infrastructure).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this library: only the tests, the package's smoke check and the
+ * benchmark's CPU-baseline leg use it. It shares no source with the HIP
+ * library and is written from the definitions on the pages, not from any
+ * kernel.
+ *
+ * Source: "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads
+ * Foundation Model" (engineering post, indiaaifounders.com copy):
+ *   - section "Jagged Sequence Flash Attention": attention computed directly on
+ *     variable-length (jagged) sequences, with asymmetric query/key-value
+ *     lengths, reaching what padded scaled-dot-product attention reaches
+ *     without the padding;
+ *   - section "Generalized Dot-Product Attention (GDPA)": two matrix products
+ *     with an element-wise activation (GELU or SiLU) in place of softmax,
+ *     covering self-attention, PMA and cross-attention;
+ *   - section "BlockAttention": sliding-window attention that limits each
+ *     token to nearby events.
+ *
+ * Readings where the pages are silent (each one also listed in the design
+ * notes of the repository):
+ *   - the pointwise activations are normalised by 1/Lk_b, Lk_b being the key
+ *     count of the sequence;
+ *   - GELU is the tanh form (the pages name GELU's tanh);
+ *   - causal is top-left aligned: key j is visible to query i iff j <= i;
+ *   - a window W > 0 keeps W keys including the query's own position:
+ *     causal: 0 <= i - j < W; non-causal: |i - j| < W; W == 0 means no window;
+ *   - a row with no visible key outputs 0 (softmax: lse = -inf).
+ *
+ * Pins: every function here is checked, in the CPU test suite, against
+ * library routines (torch scaled_dot_product_attention / autograd in float64
+ * on padded dense tensors), closed forms (identical keys, zero queries,
+ * constant values, single visible key), invariants (sequence permutation) and
+ * central finite differences. The work-list function is pinned by brute-force
+ * enumeration.
+ */
+#ifndef JA_ORACLE_H
+#define JA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_F64 = 2 };
+enum { ORA_SOFTMAX = 0, ORA_SILU = 1, ORA_GELU_TANH = 2 };
+
+/* Forward. q: [Tq,H,d], k/v: [Tk,H,d] token-major, element type `dtype`
+ * (bf16 given as raw uint16 bits). Offsets: [B+1], non-decreasing from 0.
+ * pair_mask: [B*H] bytes, index b*H+h; NULL computes every pair. Rows of
+ * unselected pairs are not written. out: [Tq,H,d] doubles; lse: [Tq,H]
+ * doubles or NULL (softmax only; GDPA writes NaN there).
+ * nthreads <= 0 uses every online core. Returns 0, or -1 on bad arguments. */
+int ora_fwd(const void* q, const void* k, const void* v, int dtype,
+            const int32_t* q_off, const int32_t* k_off,
+            int32_t B, int32_t H, int32_t d,
+            int act, int causal, int32_t window, double scale,
+            const uint8_t* pair_mask, double* out, double* lse, int nthreads);
+
+/* Backward of the softmax forward (act must be ORA_SOFTMAX) or of the
+ * normalised pointwise forward (ORA_SILU / ORA_GELU_TANH). The oracle
+ * recomputes its own O and LSE. dout: [Tq,H,d] in `dtype`. Writes out, lse
+ * (may be NULL), dq [Tq,H,d], dk and dv [Tk,H,d] for the selected pairs. */
+int ora_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+            const int32_t* q_off, const int32_t* k_off,
+            int32_t B, int32_t H, int32_t d,
+            int act, int causal, int32_t window, double scale,
+            const uint8_t* pair_mask, double* out, double* lse,
+            double* dq, double* dk, double* dv, int nthreads);
+
+/* Reference work list of (sequence, row-tile) items for a row-tiled pass over
+ * a jagged batch: rows of sequence b are `row_off`, columns `col_off`. Each
+ * row tile of BM rows has a column range of visible columns (causal / window
+ * as above, `transposed` = 1 when rows are keys and columns are queries, as in
+ * a key-stationary backward pass); its cost is the number of BN-wide column
+ * tiles that range touches. Items are sorted by min(cost, cap) descending,
+ * then b ascending, then tile ascending. Writes items[2*n] = b, items[2*n+1]
+ * = tile, costs[n] = cost. Returns the item count, or -1 if max_items is too
+ * small or an argument is bad. */
+int64_t ora_tile_list(const int32_t* row_off, const int32_t* col_off, int32_t B,
+                      int32_t BM, int32_t BN, int causal, int32_t window,
+                      int transposed, int32_t cap,
+                      int32_t* items, int32_t* costs, int64_t max_items);
+
+/* Number of online cores the oracle uses when nthreads <= 0. */
+int ora_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
