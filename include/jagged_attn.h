@@ -1,0 +1,157 @@
+/*
+ * jagged_attn.h -- C ABI of the MI355X (gfx950) jagged attention library.
+ *
+ * What is computed. For a batch of B variable-length ("jagged") sequences stored
+ * back to back with no padding, each sequence b and head h computes
+ *     out = act(scale * Q K^T, masks) V
+ * over its own rows only. The engineering post "GEM Training: How Meta Doubled
+ * the Efficiency of Its LLM-Scale Ads Foundation Model" defines the operations:
+ *   - "Jagged Sequence Flash Attention" section: FlashAttention run directly on
+ *     variable-length jagged tensors addressed per sequence, with asymmetric
+ *     query / key-value lengths and a backward pass whose dQ is computed in its
+ *     own pass (no atomic dQ accumulation, no recomputation across passes);
+ *   - "Generalized Dot-Product Attention (GDPA)" section: the same two matrix
+ *     products with an element-wise GELU or SiLU in place of softmax, for
+ *     self-attention, cross-attention (long queries, short keys/values) and
+ *     pooled multi-head attention (short queries, long keys/values); valid tiles
+ *     are enumerated by a software tile scheduler and empty tiles skipped;
+ *   - "BlockAttention" section: sliding-window attention that limits each token
+ *     to nearby events and skips tiles outside the window.
+ *
+ * Conventions this library fixes where the post is silent:
+ *   - SiLU(x) = x * sigmoid(x); GELU is the tanh form
+ *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); both are normalised by
+ *     1/Lk_b, Lk_b being the key count of the sequence (all keys, not the
+ *     visible ones). Softmax is normalised by its own row sum.
+ *   - causal is top-left aligned: query i (local index) sees key j iff j <= i;
+ *   - window W > 0 keeps W keys including the query's own position:
+ *     causal: 0 <= i - j < W; non-causal: |i - j| < W. W == 0: no window.
+ *   - a row with no visible key gets out = 0 and (softmax) lse = -inf.
+ *
+ * Layout. Q, out, dQ: [Tq, H, d]; K, V, dK, dV: [Tk, H, d]; token-major, d
+ * contiguous, element type `dtype`. lse: [Tq, H] float32, natural log. Offsets
+ * are int32 [B+1], non-decreasing, offsets[0] = 0, offsets[B] = T. K and V share
+ * k_offsets. Sequence b owns rows [q_offsets[b], q_offsets[b+1]) of Q and
+ * [k_offsets[b], k_offsets[b+1]) of K and V.
+ *
+ * Ownership and asynchrony. Every pointer argument except the host-side size
+ * queries is device memory owned by the caller, including the workspace; the
+ * library allocates nothing per call and keeps no pointer after returning. All
+ * work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ * the call returns without synchronising: inputs must stay valid and outputs
+ * untouched until the stream has passed the call.
+ *
+ * Errors. Status codes only: no exceptions cross the ABI, nothing aborts or
+ * prints. Problems visible on the host (null pointers, unsupported d or dtype,
+ * negative window, non-finite scale, misaligned pointers, a workspace that is
+ * too small) return before anything is enqueued. Offsets are not read on the
+ * host; malformed offsets are undefined behaviour on the device side, and
+ * ja_validate_offsets exists to check them (synchronously) in tests.
+ */
+#ifndef JAGGED_ATTN_H
+#define JAGGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    JA_OK = 0,
+    JA_ERR_INVALID_ARG = 1,     /* null pointer, bad size, window < 0, scale not finite, misalignment */
+    JA_ERR_UNSUPPORTED = 2,     /* d not in {32, 64, 128}, unknown dtype/act, bwd of an unsupported act */
+    JA_ERR_WORKSPACE = 3,       /* workspace smaller than the matching *_workspace_size() */
+    JA_ERR_INVALID_OFFSETS = 4, /* ja_validate_offsets found malformed offsets */
+    JA_ERR_HIP = 5              /* a HIP runtime call or kernel launch failed */
+} ja_status_t;
+
+typedef enum {
+    JA_ACT_SOFTMAX = 0,  /* online softmax over the visible keys (JFA) */
+    JA_ACT_SILU = 1,     /* x*sigmoid(x), times 1/Lk_b (GDPA) */
+    JA_ACT_GELU_TANH = 2 /* tanh-form GELU, times 1/Lk_b (GDPA) */
+} ja_act_t;
+
+typedef enum {
+    JA_F32 = 0,  /* fp32 in, fp32 out, fp32 matrix-core products */
+    JA_BF16 = 1  /* bf16 in, bf16 out, fp32 accumulation */
+} ja_dtype_t;
+
+/* Bytes of device workspace jagged_attn_fwd needs for these sizes. Host only. */
+size_t ja_fwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                             int32_t act, int32_t causal, int32_t window, int32_t dtype);
+
+/* Forward (the whole hot path: tile scheduling, then the fused attention kernel).
+ *   q [Tq,H,d], k/v [Tk,H,d]: inputs, 16-byte aligned.
+ *   q_offsets, k_offsets: device int32 [B+1].
+ *   B >= 0, H >= 1, d in {32, 64, 128}; Tq, Tk: first dimensions of q and k.
+ *   act: ja_act_t; causal: 0/1; window >= 0 (0 = none); scale: finite, applied
+ *   to Q K^T before the activation (usually 1/sqrt(d)).
+ *   out [Tq,H,d]: written for every row of every sequence.
+ *   lse [Tq,H] fp32: softmax log-sum-exp per row, natural log; may be NULL;
+ *   ignored for SiLU/GELU.
+ *   workspace: at least ja_fwd_workspace_size() bytes, 256-byte aligned; its
+ *   contents on entry do not matter and are clobbered. */
+ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v,
+                            const int32_t* q_offsets, const int32_t* k_offsets,
+                            int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                            int32_t act, int32_t causal, int32_t window, float scale,
+                            int32_t dtype, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace jagged_attn_bwd needs. Host only. */
+size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                             int32_t act, int32_t causal, int32_t window, int32_t dtype);
+
+/* Backward of the softmax forward (act must be JA_ACT_SOFTMAX, dtype JA_BF16).
+ * Needs the forward's out and lse. Computes Di = rowsum(dO * O) inside the dQ
+ * pass, writes dq once per row from that pass, then dk and dv once per row from
+ * a key-stationary pass; no atomics on any gradient.
+ *   dout [Tq,H,d]: upstream gradient; dq [Tq,H,d], dk/dv [Tk,H,d]: outputs,
+ *   every row written (rows no query sees get zeros). */
+ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v,
+                            const void* out, const void* dout, const float* lse,
+                            const int32_t* q_offsets, const int32_t* k_offsets,
+                            int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                            int32_t act, int32_t causal, int32_t window, float scale,
+                            int32_t dtype, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Runs only the tile scheduler that jagged_attn_fwd runs first ("software tile
+ * scheduling for jagged tensors", GDPA section) and copies its work list out:
+ * items (device int32 [2*max_items]) receives (sequence, query-tile) pairs in the
+ * order the persistent attention grid consumes them (each pair expands to H
+ * work items, head fastest); count (device int32 [1]) receives the number of
+ * pairs. Pairs are ordered by min(cost, 511) descending, then sequence, then
+ * tile ascending, cost being the number of key tiles the query tile visits.
+ * Returns JA_ERR_INVALID_ARG if max_items < ceil(Tq/BM) + B (BM from
+ * ja_fwd_tile_shape). */
+ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets,
+                            int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                            int32_t act, int32_t causal, int32_t window, int32_t dtype,
+                            int32_t* items, int32_t* count, int64_t max_items,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tile shape the forward uses for these sizes: bm query rows per work item, bn
+ * keys per scheduler cost unit. Host only; returns JA_ERR_UNSUPPORTED for
+ * unsupported d / dtype / act. */
+ja_status_t ja_fwd_tile_shape(int32_t B, int32_t d, int64_t Tq, int32_t act, int32_t dtype,
+                              int32_t* bm, int32_t* bn);
+
+/* Checks offsets on the device (non-decreasing, [0] == 0, [B] == T) and waits
+ * for the result: synchronous, meant for tests and debugging. Uses no
+ * workspace. Returns JA_OK or JA_ERR_INVALID_OFFSETS. */
+ja_status_t ja_validate_offsets(const int32_t* offsets, int32_t B, int64_t T, void* stream);
+
+/* Static string for a status code. */
+const char* ja_status_string(ja_status_t status);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int32_t ja_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JAGGED_ATTN_H */

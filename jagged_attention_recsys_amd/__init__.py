@@ -1,0 +1,24 @@
+"""MI355X (gfx950) jagged attention: JFA softmax and GDPA SiLU/GELU forward, softmax backward.
+
+The computation runs in ``libjagged_attn.so`` (hand-written HIP kernels behind the C
+ABI of ``include/jagged_attn.h``); this package only marshals torch tensors into it.
+"""
+from .ops import (  # noqa: F401
+    bwd_workspace_size,
+    fwd_schedule,
+    fwd_tile_shape,
+    fwd_workspace_size,
+    jagged_attn_bwd,
+    jagged_attn_fwd,
+    validate_offsets,
+)
+
+__all__ = [
+    "jagged_attn_fwd",
+    "jagged_attn_bwd",
+    "fwd_workspace_size",
+    "bwd_workspace_size",
+    "fwd_schedule",
+    "fwd_tile_shape",
+    "validate_offsets",
+]

@@ -1,0 +1,235 @@
+// ja_api.cpp -- the C ABI declared in include/jagged_attn.h.
+//
+// Host side only: argument validation (everything checkable without reading
+// device memory), workspace layout, kernel selection and launches. No call
+// allocates, frees or synchronises, except ja_validate_offsets, which is
+// synchronous by contract.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "jagged_attn.h"
+#include "ja_internal.h"
+
+using namespace ja;
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct FwdPlan {
+    bool split;
+    FwdShape shape;
+    int64_t max_pairs;
+    size_t off_tbase, off_items, bytes;
+};
+
+// Short-query batches (mean query length <= 48, e.g. pooled attention seeds) use
+// the split layout; the choice depends only on sizes, never on device data.
+bool use_split(int32_t B, int64_t Tq, int32_t dtype) {
+    return dtype == JA_BF16 && B > 0 && Tq <= 48LL * B;
+}
+
+ja_status_t check_common(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
+                         int32_t window, float scale, int32_t dtype) {
+    if (B < 0 || H < 1 || Tq < 0 || Tk < 0 || window < 0) return JA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return JA_ERR_INVALID_ARG;
+    if (Tq > INT32_MAX || Tk > INT32_MAX) return JA_ERR_UNSUPPORTED;
+    if (!fwd_supported(dtype, d, act)) return JA_ERR_UNSUPPORTED;
+    return JA_OK;
+}
+
+ja_status_t plan_fwd(int32_t B, int32_t H, int32_t d, int64_t Tq, int32_t act, int32_t dtype, FwdPlan* p) {
+    p->split = use_split(B, Tq, dtype);
+    p->shape = fwd_shape(dtype, d, act, p->split);
+    if (p->shape.bm <= 0) return JA_ERR_UNSUPPORTED;
+    p->max_pairs = (Tq + p->shape.bm - 1) / p->shape.bm + B;
+    if (p->max_pairs * (int64_t)H >= INT32_MAX) return JA_ERR_UNSUPPORTED;
+    p->off_tbase = align_up(sizeof(int32_t) * kCtrCount);
+    p->off_items = align_up(p->off_tbase + sizeof(int32_t) * ((size_t)B + 1));
+    p->bytes = align_up(p->off_items + sizeof(int32_t) * 2 * (size_t)p->max_pairs);
+    return JA_OK;
+}
+
+int device_cus() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int fwd_occupancy(int dtype, int d, int act, bool split) {
+    static std::atomic<int> cache[2][3][3][2];
+    const int di = d == 32 ? 0 : d == 64 ? 1 : 2;
+    std::atomic<int>& slot = cache[dtype][di][act][split ? 1 : 0];
+    int n = slot.load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    n = fwd_blocks_per_cu(dtype, d, act, split);
+    slot.store(n, std::memory_order_relaxed);
+    return n;
+}
+
+SchedArgs sched_args(const FwdPlan& p, const int32_t* q_offsets, const int32_t* k_offsets, int32_t B,
+                     int32_t H, int32_t causal, int32_t window, void* workspace) {
+    char* ws = static_cast<char*>(workspace);
+    SchedArgs s;
+    s.row_off = q_offsets;
+    s.col_off = k_offsets;
+    s.B = B;
+    s.H = H;
+    s.bm = p.shape.bm;
+    s.bn = p.shape.bn;
+    s.causal = causal ? 1 : 0;
+    s.window = window;
+    s.transposed = 0;
+    s.max_pairs = p.max_pairs;
+    s.tbase = reinterpret_cast<int32_t*>(ws + p.off_tbase);
+    s.items = reinterpret_cast<int32_t*>(ws + p.off_items);
+    s.counters = reinterpret_cast<int32_t*>(ws);
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ja_fwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
+                             int32_t causal, int32_t window, int32_t dtype) {
+    (void)causal;
+    if (check_common(B, H, d, Tq, Tk, act, window, 1.0f, dtype) != JA_OK) return 0;
+    FwdPlan p;
+    if (plan_fwd(B, H, d, Tq, act, dtype, &p) != JA_OK) return 0;
+    return p.bytes;
+}
+
+ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                            const int32_t* k_offsets, int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                            int32_t act, int32_t causal, int32_t window, float scale, int32_t dtype, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    ja_status_t st = check_common(B, H, d, Tq, Tk, act, window, scale, dtype);
+    if (st != JA_OK) return st;
+    if (B == 0 || Tq == 0) return JA_OK;  // no query rows: nothing to write
+    if (!q || !out || !q_offsets || !k_offsets || !workspace) return JA_ERR_INVALID_ARG;
+    if (Tk > 0 && (!k || !v)) return JA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+        !aligned(q_offsets, 4) || !aligned(k_offsets, 4) || !aligned(workspace, 16))
+        return JA_ERR_INVALID_ARG;
+    FwdPlan p;
+    st = plan_fwd(B, H, d, Tq, act, dtype, &p);
+    if (st != JA_OK) return st;
+    if (workspace_bytes < p.bytes) return JA_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SchedArgs sa = sched_args(p, q_offsets, k_offsets, B, H, causal, window, workspace);
+    if (launch_sched(sa, s) != hipSuccess) return JA_ERR_HIP;
+
+    FwdArgs fa;
+    fa.q = q;
+    fa.k = k;
+    fa.v = v;
+    fa.out = out;
+    fa.lse = act == JA_ACT_SOFTMAX ? lse : nullptr;
+    fa.q_off = q_offsets;
+    fa.k_off = k_offsets;
+    fa.items = sa.items;
+    fa.counters = sa.counters;
+    fa.H = H;
+    fa.Tq = (int32_t)Tq;
+    fa.Tk = (int32_t)Tk;
+    fa.causal = causal ? 1 : 0;
+    fa.window = window;
+    fa.scale = scale;
+    const int64_t max_items = p.max_pairs * H;
+    int64_t grid = (int64_t)device_cus() * fwd_occupancy(dtype, d, act, p.split);
+    if (grid > max_items) grid = max_items;
+    if (grid < 1) grid = 1;
+    if (launch_fwd(fa, dtype, d, act, p.split, (int)grid, s) != hipSuccess) return JA_ERR_HIP;
+    return JA_OK;
+}
+
+size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
+                             int32_t causal, int32_t window, int32_t dtype) {
+    (void)B; (void)H; (void)d; (void)Tq; (void)Tk; (void)act; (void)causal; (void)window; (void)dtype;
+    return 0;
+}
+
+ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                            const float* lse, const int32_t* q_offsets, const int32_t* k_offsets, int32_t B,
+                            int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t causal,
+                            int32_t window, float scale, int32_t dtype, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    (void)q; (void)k; (void)v; (void)out; (void)dout; (void)lse; (void)q_offsets; (void)k_offsets;
+    (void)B; (void)H; (void)d; (void)Tq; (void)Tk; (void)act; (void)causal; (void)window; (void)scale;
+    (void)dtype; (void)dq; (void)dk; (void)dv; (void)workspace; (void)workspace_bytes; (void)stream;
+    return JA_ERR_UNSUPPORTED;
+}
+
+ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets, int32_t B, int32_t H, int32_t d,
+                            int64_t Tq, int64_t Tk, int32_t act, int32_t causal, int32_t window, int32_t dtype,
+                            int32_t* items, int32_t* count, int64_t max_items, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    ja_status_t st = check_common(B, H, d, Tq, Tk, act, window, 1.0f, dtype);
+    if (st != JA_OK) return st;
+    if (!q_offsets || !k_offsets || !items || !count || !workspace) return JA_ERR_INVALID_ARG;
+    FwdPlan p;
+    st = plan_fwd(B, H, d, Tq, act, dtype, &p);
+    if (st != JA_OK) return st;
+    if (max_items < p.max_pairs) return JA_ERR_INVALID_ARG;
+    if (workspace_bytes < p.bytes) return JA_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SchedArgs sa = sched_args(p, q_offsets, k_offsets, B, H, causal, window, workspace);
+    if (launch_sched(sa, s) != hipSuccess) return JA_ERR_HIP;
+    if (launch_copy_items(sa.counters, sa.items, items, count, max_items, s) != hipSuccess) return JA_ERR_HIP;
+    return JA_OK;
+}
+
+ja_status_t ja_fwd_tile_shape(int32_t B, int32_t d, int64_t Tq, int32_t act, int32_t dtype, int32_t* bm,
+                              int32_t* bn) {
+    if (!bm || !bn || B < 0 || Tq < 0) return JA_ERR_INVALID_ARG;
+    if (!fwd_supported(dtype, d, act)) return JA_ERR_UNSUPPORTED;
+    FwdShape s = fwd_shape(dtype, d, act, use_split(B, Tq, dtype));
+    *bm = s.bm;
+    *bn = s.bn;
+    return JA_OK;
+}
+
+ja_status_t ja_validate_offsets(const int32_t* offsets, int32_t B, int64_t T, void* stream) {
+    if (!offsets || B < 0 || T < 0) return JA_ERR_INVALID_ARG;
+    std::vector<int32_t> h((size_t)B + 1);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(h.data(), offsets, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return JA_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return JA_ERR_HIP;
+    if (h[0] != 0 || (int64_t)h[B] != T) return JA_ERR_INVALID_OFFSETS;
+    for (int32_t b = 0; b < B; ++b)
+        if (h[b + 1] < h[b]) return JA_ERR_INVALID_OFFSETS;
+    return JA_OK;
+}
+
+const char* ja_status_string(ja_status_t status) {
+    switch (status) {
+        case JA_OK: return "ok";
+        case JA_ERR_INVALID_ARG: return "invalid argument";
+        case JA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case JA_ERR_WORKSPACE: return "workspace too small";
+        case JA_ERR_INVALID_OFFSETS: return "malformed offsets";
+        case JA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t ja_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// ja_common.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Matrix-core conventions (CDNA3/CDNA4 32x32 MFMA, wave64):
+//   A operand (32 rows x K): lane l supplies row l%32; lane group g = l/32 supplies
+//     KPACK consecutive k slots.
+//   B operand (K x 32 cols): lane l supplies column l%32, the same k slots.
+//   C/D (32x32 fp32, 16 registers): lane l holds column l%32, register r holds
+//     row 8*(r/4) + 4*g + r%4.
+// The kernels only rely on A and B pairing the same (group, slot) with the same k,
+// so the k-order inside one instruction never matters to them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ja {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// One 32x32xK matrix-core step for element type T.
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+    static constexpr int KPACK = 8;  // elements per lane per operand
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ floatx16 run(frag a, frag b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int KPACK = 1;
+    typedef float frag;
+    static __device__ __forceinline__ floatx16 run(frag a, frag b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// Row of the C tile held by register r of a lane in group g.
+__device__ __forceinline__ constexpr int c_row(int g, int r) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// Key permutation inside a 32-key block. The score tile S^T = K Q^T puts keys on
+// C rows; loading A-row rho with key kappa(rho) makes register r of group g hold key
+// 2*KPACK*(r/KPACK) + KPACK*g + r%KPACK, so that a lane's KPACK keys for one P*V
+// step are contiguous (one vector LDS read of V^T).
+template <int KPACK>
+__device__ __forceinline__ constexpr int key_of_reg(int g, int r) {
+    return 2 * KPACK * (r / KPACK) + KPACK * g + (r % KPACK);
+}
+
+template <int KPACK>
+__device__ __forceinline__ constexpr int key_of_arow(int rho) {
+    return key_of_reg<KPACK>((rho >> 2) & 1, 4 * (rho >> 3) + (rho & 3));
+}
+
+// Reductions across the two halves of a wave (lanes l and l^32 hold the same
+// column of a C tile).
+__device__ __forceinline__ float xhalf_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float xhalf_sum(float x) { return x + __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Pointwise activations in the GDPA form: x * sigmoid(z), with z = x for SiLU and
+// z = 2 sqrt(2/pi) (x + 0.044715 x^3) for tanh-GELU (0.5 (1 + tanh u) = sigmoid(2u)).
+enum { ACT_SOFTMAX = 0, ACT_SILU = 1, ACT_GELU = 2 };
+
+template <int ACT>
+__device__ __forceinline__ float pointwise(float x) {
+    float z;
+    if (ACT == ACT_SILU) {
+        z = x;
+    } else {
+        const float c2 = 1.5957691216057308f;  // 2 * sqrt(2/pi)
+        z = c2 * fmaf(0.044715f * x, x * x, x);
+    }
+    return x * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+// Block-uniform scalar broadcast helpers.
+__device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace ja

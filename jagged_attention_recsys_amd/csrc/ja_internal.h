@@ -1,0 +1,62 @@
+// ja_internal.h -- interfaces between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ja {
+
+// Scheduler cost bins: costs at or above kSchedBins-1 share the last bin.
+constexpr int kSchedBins = 512;
+
+// Slots of the counter block at the start of every workspace.
+enum { kCtrTotal = 0, kCtrPop = 1, kCtrPairs = 2, kCtrCount = 16 };
+
+struct SchedArgs {
+    const int32_t* row_off;  // [B+1] offsets of the tiled dimension
+    const int32_t* col_off;  // [B+1] offsets of the visited dimension
+    int32_t B, H;
+    int32_t bm, bn;          // row tile, column tile (cost unit)
+    int32_t causal, window, transposed;
+    int64_t max_pairs;       // capacity of items; a larger enumeration schedules nothing
+    int32_t* tbase;          // [B+1] scratch: first flat tile of each sequence
+    int32_t* items;          // [2 * max_pairs] (sequence, tile) pairs
+    int32_t* counters;       // kCtrCount ints
+};
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
+hipError_t launch_copy_items(const int32_t* counters, const int32_t* items, int32_t* out,
+                             int32_t* count, int64_t max_items, hipStream_t stream);
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;                // may be null
+    const int32_t* q_off;
+    const int32_t* k_off;
+    const int32_t* items;      // (sequence, q-tile) pairs
+    int32_t* counters;
+    int32_t H;
+    int32_t Tq, Tk;            // tensor extents: rows outside [0, T) are never touched
+    int32_t causal, window;
+    float scale;               // applied to Q K^T
+};
+
+// Forward kernel family. `split` selects the short-query layout (one 32-row query
+// tile per workgroup, the four waves splitting the keys) instead of four 32-row
+// query slices sharing each key tile.
+struct FwdShape {
+    int bm;  // query rows per work item
+    int bn;  // keys per stage (scheduler cost unit)
+};
+bool fwd_supported(int dtype, int d, int act);
+FwdShape fwd_shape(int dtype, int d, int act, bool split);
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, int act, bool split, int grid,
+                      hipStream_t stream);
+// Workgroups per CU the forward kernel reaches (from the occupancy query).
+int fwd_blocks_per_cu(int dtype, int d, int act, bool split);
+
+}  // namespace ja

@@ -1,0 +1,198 @@
+// ja_sched.hip -- device-side tile scheduler for jagged batches.
+//
+// The GDPA section of the GEM training post enumerates the valid tiles of a jagged
+// batch, skips empty ones and spreads them over the GPU's compute units to remove
+// load skew. Here the enumeration runs on the GPU itself (no host round trip):
+// one workgroup reads the offsets, counts row tiles per sequence, gives each tile a
+// cost (the number of column tiles it visits) and writes the (sequence, tile) list
+// in longest-first order for a persistent grid that pops items with one atomic.
+//
+// Order: min(cost, kBins-1) descending, then sequence, then tile ascending. It is a
+// stable counting sort: wave w of the workgroup owns a contiguous slice of the
+// (sequence, tile) enumeration, so bins are laid out as (bin descending, wave
+// ascending) and each wave places its items in enumeration order.
+#include "ja_common.h"
+#include "ja_internal.h"
+#include "ja_tiles.h"
+
+namespace ja {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+// Inclusive scan of one int per thread over the whole workgroup. `tmp` holds
+// kWaves+1 ints of LDS. Returns the inclusive prefix; *total gets the sum.
+__device__ int block_scan(int x, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int v = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(v, o);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) tmp[w] = v;
+    __syncthreads();
+    if (w == 0) {
+        int t = lane < kWaves ? tmp[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < kWaves; o <<= 1) {
+            int y = __shfl_up(t, o);
+            if (lane >= o) t += y;
+        }
+        if (lane < kWaves) tmp[lane] = t;  // inclusive wave totals
+    }
+    __syncthreads();
+    int before = w > 0 ? tmp[w - 1] : 0;
+    *total = tmp[kWaves - 1];
+    __syncthreads();  // tmp may be reused right after
+    return before + v;
+}
+
+// Sequence b owning flat tile f: the last b with tbase[b] <= f (tbase[B] = F > f).
+__device__ int find_seq(const int32_t* tbase, int B, int f) {
+    int lo = 0, hi = B;  // invariant: tbase[lo] <= f < tbase[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (tbase[mid] <= f) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
+    __shared__ int cnt[kWaves * kSchedBins];  // [wave][bin] counts, then offsets
+    __shared__ int tmp[kWaves + 1];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+    // Phase 0: row tiles per sequence and their exclusive prefix (tbase[0..B]).
+    int carry = 0;
+    for (int c0 = 0; c0 <= a.B; c0 += kThreads) {
+        const int b = c0 + tid;
+        int n = 0;
+        if (b < a.B) {
+            const int64_t L = (int64_t)a.row_off[b + 1] - a.row_off[b];
+            n = L > 0 ? (int)((L + a.bm - 1) / a.bm) : 0;
+        }
+        int total;
+        int incl = block_scan(n, tmp, &total);
+        if (b <= a.B) a.tbase[b] = carry + incl - n;
+        carry += total;
+    }
+    // An enumeration larger than the item buffer (offsets inconsistent with the
+    // sizes the host was given) schedules nothing rather than writing past it.
+    const int F = (int64_t)carry <= a.max_pairs ? carry : 0;
+    for (int i = tid; i < kWaves * kSchedBins; i += kThreads) cnt[i] = 0;
+    __threadfence_block();
+    __syncthreads();
+
+    // Each wave owns the enumeration slice [f_lo, f_hi).
+    const int f_lo = (int)(((int64_t)F * w) / kWaves);
+    const int f_hi = (int)(((int64_t)F * (w + 1)) / kWaves);
+
+    auto bin_of = [&](int f, int* pb, int* pt) {
+        const int b = find_seq(a.tbase, a.B, f);
+        const int t = f - a.tbase[b];
+        const int64_t Lr = (int64_t)a.row_off[b + 1] - a.row_off[b];
+        const int64_t Lc = (int64_t)a.col_off[b + 1] - a.col_off[b];
+        const ColRange cr = visible_cols(Lr, Lc, (int64_t)t * a.bm, a.bm, a.causal, a.window, a.transposed);
+        const int cost = tile_cost(cr, a.bn);
+        *pb = b;
+        *pt = t;
+        return cost < kSchedBins - 1 ? cost : kSchedBins - 1;
+    };
+
+    // Phase 1: per-wave histograms.
+    for (int f = f_lo + lane; f < f_hi; f += 64) {
+        int b, t;
+        const int bin = bin_of(f, &b, &t);
+        atomicAdd(&cnt[w * kSchedBins + bin], 1);
+    }
+    __syncthreads();
+
+    // Phase 2: exclusive offsets in (bin descending, wave ascending) order. Thread
+    // tid owns flat positions [8 tid, 8 tid + 8) of that order.
+    {
+        constexpr int per = kWaves * kSchedBins / kThreads;
+        int vals[per];
+        int s = 0;
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            const int x = tid * per + i;
+            const int bin = kSchedBins - 1 - x / kWaves, ww = x % kWaves;
+            vals[i] = cnt[ww * kSchedBins + bin];
+            s += vals[i];
+        }
+        int total;
+        int incl = block_scan(s, tmp, &total);
+        int run = incl - s;
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            const int x = tid * per + i;
+            const int bin = kSchedBins - 1 - x / kWaves, ww = x % kWaves;
+            cnt[ww * kSchedBins + bin] = run;
+            run += vals[i];
+        }
+    }
+    __syncthreads();
+
+    // Phase 3: stable scatter, one wave per slice, 64 items at a time in order.
+    for (int f0 = f_lo; f0 < f_hi; f0 += 64) {
+        const int f = f0 + lane;
+        const bool valid = f < f_hi;
+        int b = 0, t = 0, bin = -1;
+        if (valid) bin = bin_of(f, &b, &t);
+        uint64_t pending = __ballot(valid);
+        int pos = 0;
+        while (pending) {
+            const int leader = __ffsll((unsigned long long)pending) - 1;
+            const int lbin = __shfl(bin, leader);
+            const uint64_t same = __ballot(valid && bin == lbin);
+            const int base = cnt[w * kSchedBins + lbin];
+            if (valid && bin == lbin) {
+                const uint64_t below = same & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
+                pos = base + __popcll(below);
+            }
+            if (lane == leader) cnt[w * kSchedBins + lbin] = base + __popcll(same);
+            pending &= ~same;
+        }
+        if (valid) {
+            a.items[2 * pos] = b;
+            a.items[2 * pos + 1] = t;
+        }
+    }
+
+    if (tid == 0) {
+        a.counters[kCtrTotal] = F * a.H;
+        a.counters[kCtrPop] = 0;
+        a.counters[kCtrPairs] = F;
+    }
+}
+
+__global__ void ja_copy_items_kernel(const int32_t* counters, const int32_t* items, int32_t* out,
+                                     int32_t* count, int64_t max_items) {
+    const int F = counters[kCtrPairs];
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < F && i < max_items;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        out[2 * i] = items[2 * i];
+        out[2 * i + 1] = items[2 * i + 1];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *count = F;
+}
+
+}  // namespace
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(ja_sched_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_items(const int32_t* counters, const int32_t* items, int32_t* out,
+                             int32_t* count, int64_t max_items, hipStream_t stream) {
+    hipLaunchKernelGGL(ja_copy_items_kernel, dim3(64), dim3(256), 0, stream, counters, items, out,
+                       count, max_items);
+    return hipGetLastError();
+}
+
+}  // namespace ja

@@ -1,0 +1,163 @@
+"""torch-facing binding of the C ABI: argument marshalling only.
+
+Every step of the computation runs in the HIP library; torch only provides device
+memory (outputs, workspace) and the current stream. Names mirror the C entry
+points in include/jagged_attn.h.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+ACT = {"softmax": 0, "silu": 1, "gelu": 2, "gelu_tanh": 2}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+
+
+def _act(act) -> int:
+    if isinstance(act, str):
+        if act not in ACT:
+            raise ValueError(f"unknown activation {act!r}")
+        return ACT[act]
+    return int(act)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _check_tensor(name: str, t: torch.Tensor, dtype=None, dim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims")
+
+
+def fwd_workspace_size(B, H, d, Tq, Tk, act="softmax", causal=False, window=0, dtype=torch.bfloat16) -> int:
+    return int(_lib.load().ja_fwd_workspace_size(B, H, d, Tq, Tk, _act(act), int(bool(causal)), int(window),
+                                                 DTYPE[dtype]))
+
+
+def jagged_attn_fwd(q, k, v, q_offsets, k_offsets, act="softmax", causal=False, window=0, scale=None,
+                    out=None, lse=None, workspace=None, stream=None):
+    """Jagged attention forward. q: [Tq,H,d]; k, v: [Tk,H,d]; offsets: int32 [B+1] on the GPU.
+
+    Returns (out [Tq,H,d], lse [Tq,H] float32 or None for pointwise activations).
+    """
+    lib = _lib.load()
+    _check_tensor("q", q, dim=3)
+    dtype = q.dtype
+    if dtype not in DTYPE:
+        raise ValueError(f"unsupported dtype {dtype}")
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, dtype, 3)
+    _check_tensor("q_offsets", q_offsets, torch.int32, 1)
+    _check_tensor("k_offsets", k_offsets, torch.int32, 1)
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    if k.shape[1:] != (H, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [Tk, H, d] with q's H and d")
+    B = q_offsets.numel() - 1
+    if k_offsets.numel() != B + 1:
+        raise ValueError("q_offsets and k_offsets must both have B+1 entries")
+    a = _act(act)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, dtype)
+    if a == 0 and lse is None:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
+    ws_bytes = int(lib.ja_fwd_workspace_size(B, H, d, Tq, Tk, a, int(bool(causal)), int(window), DTYPE[dtype]))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    status = lib.jagged_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(k_offsets), B, H, d, Tq, Tk,
+                                 a, int(bool(causal)), int(window), float(scale), DTYPE[dtype], _ptr(out),
+                                 _ptr(lse) if a == 0 else None, _ptr(workspace), workspace.numel(),
+                                 _stream(q.device, stream))
+    _lib.check("jagged_attn_fwd", status)
+    return out, (lse if a == 0 else None)
+
+
+def bwd_workspace_size(B, H, d, Tq, Tk, act="softmax", causal=False, window=0, dtype=torch.bfloat16) -> int:
+    return int(_lib.load().ja_bwd_workspace_size(B, H, d, Tq, Tk, _act(act), int(bool(causal)), int(window),
+                                                 DTYPE[dtype]))
+
+
+def jagged_attn_bwd(q, k, v, out, dout, lse, q_offsets, k_offsets, act="softmax", causal=False, window=0,
+                    scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of the softmax forward. Returns (dq, dk, dv)."""
+    lib = _lib.load()
+    _check_tensor("q", q, dim=3)
+    dtype = q.dtype
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_tensor(name, t, dtype, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    B = q_offsets.numel() - 1
+    a = _act(act)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = int(lib.ja_bwd_workspace_size(B, H, d, Tq, Tk, a, int(bool(causal)), int(window), DTYPE[dtype]))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    status = lib.jagged_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(q_offsets),
+                                 _ptr(k_offsets), B, H, d, Tq, Tk, a, int(bool(causal)), int(window),
+                                 float(scale), DTYPE[dtype], _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 workspace.numel(), _stream(q.device, stream))
+    _lib.check("jagged_attn_bwd", status)
+    return dq, dk, dv
+
+
+def fwd_tile_shape(B, d, Tq, act="softmax", dtype=torch.bfloat16):
+    import ctypes
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    status = _lib.load().ja_fwd_tile_shape(B, d, Tq, _act(act), DTYPE[dtype], ctypes.byref(bm), ctypes.byref(bn))
+    _lib.check("ja_fwd_tile_shape", status)
+    return bm.value, bn.value
+
+
+def fwd_schedule(q_offsets, k_offsets, H, d, Tq, Tk, act="softmax", causal=False, window=0,
+                 dtype=torch.bfloat16, stream=None):
+    """Run only the forward's tile scheduler; returns the (sequence, tile) pairs as an int32 [n,2] GPU tensor."""
+    lib = _lib.load()
+    B = q_offsets.numel() - 1
+    bm, _ = fwd_tile_shape(B, d, Tq, act, dtype)
+    max_items = (Tq + bm - 1) // bm + B
+    items = torch.empty((max(max_items, 1), 2), dtype=torch.int32, device=q_offsets.device)
+    count = torch.zeros(1, dtype=torch.int32, device=q_offsets.device)
+    a = _act(act)
+    ws_bytes = int(lib.ja_fwd_workspace_size(B, H, d, Tq, Tk, a, int(bool(causal)), int(window), DTYPE[dtype]))
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q_offsets.device)
+    status = lib.ja_fwd_schedule(_ptr(q_offsets), _ptr(k_offsets), B, H, d, Tq, Tk, a, int(bool(causal)),
+                                 int(window), DTYPE[dtype], _ptr(items), _ptr(count), max_items, _ptr(workspace),
+                                 workspace.numel(), _stream(q_offsets.device, stream))
+    _lib.check("ja_fwd_schedule", status)
+    n = int(count.item())
+    return items[:n]
+
+
+def validate_offsets(offsets, T, stream=None) -> bool:
+    status = _lib.load().ja_validate_offsets(_ptr(offsets), offsets.numel() - 1, int(T),
+                                             _stream(offsets.device, stream))
+    if status == 4:
+        return False
+    _lib.check("ja_validate_offsets", status)
+    return True

@@ -86,8 +86,8 @@ typedef struct {
     double scale;
     const uint8_t* pair_mask;
     double *out, *lse, *dq, *dk, *dv;
-    int64_t next; /* next pair to claim */
-    int status;
+    int64_t next; /* next work unit to claim */
+    int64_t* rbase; /* forward: [B+1] first 64-row block of each sequence */
 } job_t;
 
 static int64_t claim(job_t* J) { return __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED); }
@@ -102,14 +102,14 @@ static double score(const job_t* J, int64_t qrow, int64_t krow, int32_t h) {
     return J->scale * acc;
 }
 
-/* Forward of one (b, h) pair: the plain definition, row by row. */
-static void fwd_pair(job_t* J, int32_t b, int32_t h) {
+/* Forward of rows [i0, i1) of one (b, h) pair: the plain definition, row by row. */
+static void fwd_rows(job_t* J, int32_t b, int32_t h, int64_t i0, int64_t i1) {
     const int64_t H = J->H, d = J->d;
     const int64_t qo = J->q_off[b], ko = J->k_off[b];
-    const int64_t Lq = J->q_off[b + 1] - qo, Lk = J->k_off[b + 1] - ko;
+    const int64_t Lk = J->k_off[b + 1] - ko;
     double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
     double* o = (double*)malloc(sizeof(double) * (size_t)d);
-    for (int64_t i = 0; i < Lq; ++i) {
+    for (int64_t i = i0; i < i1; ++i) {
         for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
         double lse_i = NAN;
         if (J->act == ORA_SOFTMAX) {
@@ -151,6 +151,10 @@ static void fwd_pair(job_t* J, int32_t b, int32_t h) {
     }
     free(s);
     free(o);
+}
+
+static void fwd_pair(job_t* J, int32_t b, int32_t h) {
+    fwd_rows(J, b, h, 0, (int64_t)J->q_off[b + 1] - J->q_off[b]);
 }
 
 /* Backward of one (b, h) pair. Softmax: P_ij = exp(s_ij - lse_i),
@@ -218,16 +222,46 @@ static void bwd_pair(job_t* J, int32_t b, int32_t h) {
     free(lse_local);
 }
 
+/* Forward work units are (head, 64-row block of the batch); rbase[b] is the first
+ * row block of sequence b. Backward units are whole (b, h) pairs, since dK and dV
+ * of a key gather over every row of its sequence. */
+#define ORA_ROWS 64
+
+static int32_t seq_of_block(const int64_t* rbase, int32_t B, int64_t rb) {
+    int32_t lo = 0, hi = B; /* rbase[lo] <= rb < rbase[hi] */
+    while (hi - lo > 1) {
+        int32_t mid = (lo + hi) / 2;
+        if (rbase[mid] <= rb) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
 static void* worker(void* arg) {
     job_t* J = (job_t*)arg;
-    const int64_t npairs = (int64_t)J->B * J->H;
+    if (J->dq) {
+        const int64_t npairs = (int64_t)J->B * J->H;
+        for (;;) {
+            int64_t p = claim(J);
+            if (p >= npairs) break;
+            if (J->pair_mask && !J->pair_mask[p]) continue;
+            bwd_pair(J, (int32_t)(p / J->H), (int32_t)(p % J->H));
+        }
+        return NULL;
+    }
+    const int64_t nrb = J->rbase[J->B];
+    const int64_t nunits = nrb * J->H;
     for (;;) {
-        int64_t p = claim(J);
-        if (p >= npairs) break;
-        if (J->pair_mask && !J->pair_mask[p]) continue;
-        int32_t b = (int32_t)(p / J->H), h = (int32_t)(p % J->H);
-        if (J->dq) bwd_pair(J, b, h);
-        else fwd_pair(J, b, h);
+        int64_t u = claim(J);
+        if (u >= nunits) break;
+        const int32_t h = (int32_t)(u / nrb);
+        const int64_t rb = u % nrb;
+        const int32_t b = seq_of_block(J->rbase, J->B, rb);
+        if (J->pair_mask && !J->pair_mask[(int64_t)b * J->H + h]) continue;
+        const int64_t Lq = (int64_t)J->q_off[b + 1] - J->q_off[b];
+        const int64_t i0 = (rb - J->rbase[b]) * ORA_ROWS;
+        const int64_t i1 = i0 + ORA_ROWS < Lq ? i0 + ORA_ROWS : Lq;
+        fwd_rows(J, b, h, i0, i1);
     }
     return NULL;
 }
@@ -239,8 +273,17 @@ int ora_num_threads(void) {
 
 static int run(job_t* J, int nthreads) {
     if (nthreads <= 0) nthreads = ora_num_threads();
-    if ((int64_t)nthreads > (int64_t)J->B * J->H) nthreads = (int)((int64_t)J->B * J->H);
-    if (nthreads < 1) return 0;
+    if (nthreads < 1) nthreads = 1;
+    int64_t* rbase = NULL;
+    if (!J->dq) {
+        rbase = (int64_t*)malloc(sizeof(int64_t) * ((size_t)J->B + 1));
+        rbase[0] = 0;
+        for (int32_t b = 0; b < J->B; ++b) {
+            int64_t Lq = (int64_t)J->q_off[b + 1] - J->q_off[b];
+            rbase[b + 1] = rbase[b] + (Lq + ORA_ROWS - 1) / ORA_ROWS;
+        }
+        J->rbase = rbase;
+    }
     pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
     int started = 0;
     for (int t = 0; t < nthreads; ++t)
@@ -248,6 +291,7 @@ static int run(job_t* J, int nthreads) {
     if (started == 0) worker(J);
     for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
     free(th);
+    free(rbase);
     return 0;
 }
 

@@ -1,0 +1,80 @@
+"""Helpers for GPU parity tests: upload seeded workloads, run the HIP path through
+its C ABI binding, compare against the fp64 oracle with the stated tolerances.
+
+Tolerances:
+  * fp32 inputs: max|x - y| / max|y| <= 1e-5 over all compared elements;
+  * bf16 in / fp32 accumulate: max|x - y| <= 2e-2 and mean|x - y| <= 2e-3.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+F32_REL = 1e-5
+BF16_MAX = 2e-2
+BF16_MEAN = 2e-3
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if arr.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def to_host64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rows_of_pairs(offsets: np.ndarray, H: int, pair_mask: np.ndarray | None):
+    """Boolean [T, H] mask of the rows belonging to selected (b, h) pairs."""
+    T = int(offsets[-1])
+    sel = np.zeros((T, H), dtype=bool)
+    B = offsets.shape[0] - 1
+    for b in range(B):
+        for h in range(H):
+            if pair_mask is None or pair_mask[b, h]:
+                sel[offsets[b]:offsets[b + 1], h] = True
+    return sel
+
+
+def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.ndarray | None = None) -> dict:
+    """Assert the tolerance for `dtype` ("f32" or "bf16"); returns the error statistics."""
+    if sel is not None:
+        got, ref = got[sel], ref[sel]
+    got = got.reshape(-1)
+    ref = ref.reshape(-1)
+    if got.size == 0:
+        return {"n": 0}
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values in the HIP output"
+    err = np.abs(got - ref)
+    stats = {"n": int(got.size), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+             "max_ref": float(np.abs(ref).max())}
+    if dtype == "f32":
+        rel = stats["max_abs"] / max(stats["max_ref"], 1e-30)
+        stats["rel"] = rel
+        assert rel <= F32_REL, f"{what}: relative error {rel:.3e} > {F32_REL} ({stats})"
+    else:
+        assert stats["max_abs"] <= BF16_MAX, f"{what}: max abs error {stats['max_abs']:.4e} > {BF16_MAX} ({stats})"
+        assert stats["mean_abs"] <= BF16_MEAN, f"{what}: mean abs error {stats['mean_abs']:.4e} > {BF16_MEAN}"
+    return stats
+
+
+def sample_pairs(w, n_pairs: int, seed: int = 0) -> np.ndarray:
+    """Pick (b, h) pairs for the oracle: the longest sequence, the shortest, and random others."""
+    rng = np.random.default_rng(seed)
+    B, H = w.B, w.H
+    mask = np.zeros((B, H), dtype=bool)
+    cost = w.lq * np.maximum(w.lk, 1)
+    mask[int(np.argmax(cost)), 0] = True
+    mask[int(np.argmin(cost)), H - 1] = True
+    while mask.sum() < min(n_pairs, B * H):
+        mask[rng.integers(B), rng.integers(H)] = True
+    return mask

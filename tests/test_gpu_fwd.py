@@ -1,0 +1,220 @@
+"""GPU parity of the jagged attention forward against the fp64 oracle.
+
+Every case calls the HIP library through its C ABI (Python binding) and compares
+element by element with the oracle on the same seeded inputs:
+  * small ragged batches spanning several tiles and ragged tails, every mask and
+    activation, d in {32, 64, 128}, bf16 and fp32, both kernel layouts;
+  * the five named workloads at full size, on sampled (sequence, head) pairs;
+  * closed forms (zero queries under SiLU/GELU give exactly 0; identical keys give
+    the mean of the visible values), bitwise invariance to sequence order,
+    bitwise run-to-run determinism, untouched guard bands around the outputs;
+  * the device tile scheduler against the oracle's reference work list (exact).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import jagged_attention_recsys_amd as ja
+import oracle
+from jagged_attention_recsys_amd import workloads as W
+from _parity import compare, rows_of_pairs, sample_pairs, say, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 3
+
+
+def run_fwd(w, act=None, causal=None, window=None, guard=True):
+    act = w.act if act is None else act
+    causal = w.causal if causal is None else causal
+    window = w.window if window is None else window
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    qo, ko = to_dev(w.q_offsets), to_dev(w.k_offsets)
+    Tq = q.shape[0]
+    out_full = torch.full((Tq + 2 * GUARD, w.H, w.d), float("nan"), dtype=q.dtype, device=q.device)
+    lse_full = torch.full((Tq + 2 * GUARD, w.H), float("nan"), dtype=torch.float32, device=q.device)
+    out = out_full[GUARD:GUARD + Tq]
+    lse = lse_full[GUARD:GUARD + Tq] if act == "softmax" else None
+    ja.jagged_attn_fwd(q, k, v, qo, ko, act=act, causal=causal, window=window, scale=w.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    if guard:
+        assert torch.isnan(out_full[:GUARD].float()).all() and torch.isnan(out_full[GUARD + Tq:].float()).all()
+        assert torch.isnan(lse_full[:GUARD]).all() and torch.isnan(lse_full[GUARD + Tq:]).all()
+    return out, lse
+
+
+def check_against_oracle(w, act, causal, window, pair_mask=None, what=""):
+    say(f"[fwd] {what} B={w.B} H={w.H} d={w.d} Tq={w.q.shape[0]} Tk={w.k.shape[0]} {w.dtype} act={act} "
+        f"causal={causal} window={window}")
+    out, lse = run_fwd(w, act, causal, window)
+    ref_out, ref_lse = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, act, causal, window, w.scale,
+                                  pair_mask=pair_mask)
+    sel = rows_of_pairs(w.q_offsets, w.H, pair_mask)
+    got = to_host64(out)
+    stats = compare(got, ref_out, w.dtype, f"out {what}", sel)
+    if act == "softmax":
+        gl = to_host64(lse)
+        fin = np.isfinite(ref_lse) & sel
+        assert np.array_equal(np.isneginf(gl) & sel, np.isneginf(ref_lse) & sel), "lse -inf rows differ"
+        if fin.any():
+            assert np.max(np.abs(gl[fin] - ref_lse[fin])) < 1e-3 * max(1.0, np.max(np.abs(ref_lse[fin])))
+    say(f"      ok {stats}")
+    return out, lse
+
+
+RAGGED = [1, 7, 64, 65, 127, 128, 129, 300, 0, 513]
+MASKS = [("softmax", False, 0), ("softmax", True, 0), ("softmax", True, 37), ("softmax", False, 50),
+         ("silu", False, 0), ("gelu", True, 0), ("silu", True, 100), ("gelu", False, 3)]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("act,causal,window", MASKS)
+def test_ragged_self_attention_bf16(d, act, causal, window):
+    w = W.make_case(RAGGED, H=2, d=d, dtype=W.BF16, seed=d + window)
+    check_against_oracle(w, act, causal, window, what="ragged-self")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("act,causal,window", [("softmax", False, 0), ("softmax", True, 5), ("silu", False, 0),
+                                               ("gelu", True, 20)])
+def test_ragged_cross_attention_bf16(d, act, causal, window):
+    lq = [200, 1, 0, 77, 130, 129]
+    lk = [64, 300, 5, 0, 1, 257]
+    w = W.make_case(lq, lk, H=3, d=d, dtype=W.BF16, seed=7 * d + window)
+    check_against_oracle(w, act, causal, window, what="ragged-cross")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("act,causal,window", [("softmax", False, 0), ("softmax", True, 9), ("silu", False, 0),
+                                               ("gelu", False, 0)])
+def test_ragged_fp32(d, act, causal, window):
+    w = W.make_case([5, 130, 64, 0, 200], H=2, d=d, dtype=W.F32, seed=11 * d)
+    check_against_oracle(w, act, causal, window, what="ragged-fp32")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("act,causal,window", [("softmax", False, 0), ("softmax", True, 0), ("gelu", False, 0),
+                                               ("silu", True, 40)])
+def test_short_queries_split_layout(d, act, causal, window):
+    rng = np.random.default_rng(d)
+    B = 23
+    lq = rng.integers(0, 41, size=B)
+    lk = rng.integers(0, 700, size=B)
+    lk[0], lk[1] = 0, 1
+    w = W.make_case(lq, lk, H=2, d=d, dtype=W.BF16, seed=d + 1)
+    bm, bn = ja.fwd_tile_shape(w.B, d, w.q.shape[0], act)
+    assert bm == 32, "short-query batch should take the split layout"
+    check_against_oracle(w, act, causal, window, what="split")
+
+
+def test_workload1_fp32_softmax_and_silu():
+    w = W.workload(1)
+    check_against_oracle(w, "softmax", False, 0, what="w1")
+    check_against_oracle(w, "silu", False, 0, what="w1-silu")
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_full_workloads_sampled(n):
+    say(f"[fwd] generating workload {n}")
+    w = W.workload(n)
+    mask = sample_pairs(w, 6, seed=n)
+    check_against_oracle(w, w.act, w.causal, w.window, pair_mask=mask, what=f"w{n}")
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu"])
+def test_zero_queries_give_exact_zero(act):
+    w = W.make_case([100, 3, 260], [70, 500, 1], H=2, d=128, dtype=W.BF16, seed=5)
+    w.q[:] = 0
+    out, _ = run_fwd(w, act, False, 0)
+    assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 40)])
+def test_identical_keys_give_mean_of_visible_values(causal, window):
+    lq = [150, 9, 300]
+    w = W.make_case(lq, H=2, d=64, dtype=W.BF16, seed=6)
+    w.k[:] = w.k[0, 0]
+    out, _ = run_fwd(w, "softmax", causal, window)
+    got = to_host64(out)
+    v = W.bf16_bits_to_f32(w.v).astype(np.float64)
+    for b, L in enumerate(lq):
+        qo = w.q_offsets[b]
+        for i in range(L):
+            lo = 0 if window == 0 else max(0, i - window + 1)
+            hi = i + 1 if causal else (L if window == 0 else min(L, i + window))
+            expect = v[qo + lo:qo + hi].mean(axis=0)
+            assert np.max(np.abs(got[qo + i] - expect)) < 2e-2
+
+
+@pytest.mark.parametrize("act,causal,window", [("softmax", True, 0), ("silu", False, 0), ("softmax", False, 70)])
+def test_sequence_permutation_is_bitwise_invariant(act, causal, window):
+    lq = np.array([300, 0, 129, 64, 17, 700])
+    w = W.make_case(lq, H=2, d=128, dtype=W.BF16, seed=8)
+    out, lse = run_fwd(w, act, causal, window)
+    perm = [3, 5, 0, 2, 1, 4]
+    rows = np.concatenate([np.arange(w.q_offsets[b], w.q_offsets[b + 1]) for b in perm]).astype(np.int64)
+    wp = W.Workload("perm", w.q[rows], w.k[rows], w.v[rows], W.offsets_from_lengths(lq[perm]),
+                    W.offsets_from_lengths(lq[perm]), w.H, w.d, w.dtype)
+    out2, lse2 = run_fwd(wp, act, causal, window)
+    idx = torch.from_numpy(rows).cuda()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16)[idx])
+    if lse is not None:
+        assert torch.equal(lse2, lse[idx])
+
+
+def test_runs_are_bitwise_deterministic():
+    w = W.workload(2)
+    out1, lse1 = run_fwd(w)
+    out2, lse2 = run_fwd(w)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1, lse2)
+
+
+def test_empty_keys_and_empty_rows():
+    # every sequence has zero keys: outputs 0, lse -inf
+    w = W.make_case([5, 40], [0, 0], H=2, d=64, dtype=W.BF16, seed=9)
+    out, lse = run_fwd(w, "softmax", False, 0)
+    assert torch.count_nonzero(out).item() == 0 and torch.isneginf(lse).all()
+    # more queries than keys under a causal window: late rows see nothing
+    w = W.make_case([300], [20], H=1, d=64, dtype=W.BF16, seed=10)
+    check_against_oracle(w, "softmax", True, 8, what="lq>lk")
+    out, lse = run_fwd(w, "softmax", True, 8)
+    assert torch.isneginf(lse[27:]).all() and torch.count_nonzero(out[27:]).item() == 0
+    # single-token batch
+    w = W.make_case([1], H=1, d=32, dtype=W.BF16, seed=12)
+    check_against_oracle(w, "softmax", True, 0, what="single")
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_schedule_matches_reference_work_list(n):
+    w = W.workload(n)
+    Tq, Tk = w.q.shape[0], w.k.shape[0]
+    items = ja.fwd_schedule(to_dev(w.q_offsets), to_dev(w.k_offsets), w.H, w.d, Tq, Tk, w.act, w.causal,
+                            w.window).cpu().numpy()
+    bm, bn = ja.fwd_tile_shape(w.B, w.d, Tq, w.act)
+    ref, _ = oracle.tile_list(w.q_offsets, w.k_offsets, bm, bn, w.causal, w.window, cap=511)
+    assert np.array_equal(items, ref)
+
+
+def test_schedule_small_cases_with_cap():
+    rng = np.random.default_rng(3)
+    for causal, window in [(False, 0), (True, 0), (True, 100), (False, 30)]:
+        lq = rng.integers(0, 2000, size=40)
+        lq[3] = 40000  # exceeds the 511 cost cap
+        w = W.make_case(lq, H=1, d=32, dtype=W.BF16, seed=1)
+        Tq = int(w.q_offsets[-1])
+        items = ja.fwd_schedule(to_dev(w.q_offsets), to_dev(w.k_offsets), 1, 32, Tq, Tq, "softmax", causal,
+                                window).cpu().numpy()
+        bm, bn = ja.fwd_tile_shape(w.B, 32, Tq, "softmax")
+        ref, _ = oracle.tile_list(w.q_offsets, w.k_offsets, bm, bn, causal, window, cap=511)
+        assert np.array_equal(items, ref)
+
+
+def test_validate_offsets():
+    good = torch.tensor([0, 3, 3, 10], dtype=torch.int32, device="cuda")
+    assert ja.validate_offsets(good, 10)
+    assert not ja.validate_offsets(good, 11)
+    bad = torch.tensor([0, 5, 3, 10], dtype=torch.int32, device="cuda")
+    assert not ja.validate_offsets(bad, 10)

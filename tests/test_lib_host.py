@@ -1,0 +1,109 @@
+"""Host-only checks of the C-ABI library (no GPU, no kernel launches).
+
+The library must load, export every function include/jagged_attn.h declares, and
+reject host-visible argument errors with the documented status codes before
+anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from jagged_attention_recsys_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jagged_attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ja_\w+|jagged_attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import jagged_attention_recsys_amd.build as b
+        b.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"jagged_attn_fwd", "jagged_attn_bwd", "ja_fwd_workspace_size", "ja_validate_offsets"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings_and_version(lib):
+    assert _lib.status_string(0) == "ok"
+    assert "workspace" in _lib.status_string(3)
+    assert lib.ja_version() >= 100
+
+
+FAKE = 1 << 20  # a non-null, aligned address that is never dereferenced on these paths
+
+
+def fwd(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, qo=FAKE, ko=FAKE, B=2, H=2, d=64, Tq=100, Tk=100, act=0, causal=0,
+                window=0, scale=0.125, dtype=1, out=FAKE, lse=None, ws=FAKE, ws_bytes=0, stream=None)
+    args.update(kw)
+    return lib.jagged_attn_fwd(args["q"], args["k"], args["v"], args["qo"], args["ko"], args["B"], args["H"],
+                               args["d"], args["Tq"], args["Tk"], args["act"], args["causal"], args["window"],
+                               args["scale"], args["dtype"], args["out"], args["lse"], args["ws"],
+                               args["ws_bytes"], args["stream"])
+
+
+def test_fwd_rejects_host_visible_errors(lib):
+    assert fwd(lib, q=None) == INVALID
+    assert fwd(lib, out=None) == INVALID
+    assert fwd(lib, ws=None) == INVALID
+    assert fwd(lib, window=-1) == INVALID
+    assert fwd(lib, scale=float("nan")) == INVALID
+    assert fwd(lib, scale=float("inf")) == INVALID
+    assert fwd(lib, H=0) == INVALID
+    assert fwd(lib, B=-1) == INVALID
+    assert fwd(lib, d=48) == UNSUPPORTED
+    assert fwd(lib, d=256) == UNSUPPORTED
+    assert fwd(lib, dtype=7) == UNSUPPORTED
+    assert fwd(lib, act=9) == UNSUPPORTED
+    assert fwd(lib, q=FAKE + 2) == INVALID  # misaligned
+    assert fwd(lib, ws_bytes=16) == WORKSPACE
+    assert fwd(lib, Tq=1 << 40) == UNSUPPORTED
+    # nothing to do: no launch, success
+    assert fwd(lib, B=0, Tq=0) == OK
+    assert fwd(lib, Tq=0) == OK
+
+
+def test_workspace_size_grows_with_tiles(lib):
+    small = lib.ja_fwd_workspace_size(4, 2, 128, 1000, 1000, 0, 1, 0, 1)
+    big = lib.ja_fwd_workspace_size(4, 2, 128, 100000, 1000, 0, 1, 0, 1)
+    assert 0 < small < big
+    assert small % 256 == 0
+    assert lib.ja_fwd_workspace_size(4, 2, 48, 1000, 1000, 0, 1, 0, 1) == 0
+
+
+def test_tile_shape_query(lib):
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.ja_fwd_tile_shape(64, 128, 70000, 0, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert (bm.value, bn.value) == (128, 64)
+    # short queries (mean <= 48 rows) use the split layout
+    assert lib.ja_fwd_tile_shape(256, 64, 256 * 32, 2, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert (bm.value, bn.value) == (32, 128)
+    assert lib.ja_fwd_tile_shape(4, 32, 233, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert (bm.value, bn.value) == (128, 64)
+    assert lib.ja_fwd_tile_shape(4, 40, 233, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == UNSUPPORTED
+
+
+def test_schedule_rejects_short_item_buffer(lib):
+    st = lib.ja_fwd_schedule(FAKE, FAKE, 2, 2, 64, 1000, 1000, 0, 0, 0, 1, FAKE, FAKE, 3, FAKE, 1 << 20, None)
+    assert st == INVALID
+
+
+def test_validate_offsets_rejects_null(lib):
+    assert lib.ja_validate_offsets(None, 3, 10, None) == INVALID
