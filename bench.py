@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Throughput of the jagged attention hot path on one MI355X; prints ONE JSON line.
+
+A step is one full ``jagged_attn_fwd`` call (device tile scheduler + fused attention
+kernel) over the whole synthetic batch, inputs already resident in HBM. The default
+workload is the jagged causal softmax self-attention batch (B=64, lengths
+log-uniform in [128, 4096], H=4, d=128, bf16). ``--workload 3|4|5`` measures the
+other named batches; ``--bwd`` adds the softmax backward (workload 5).
+
+Reported:
+  value        useful (unpadded) TFLOP/s of the whole step: 4 d H sum_b pairs_b per
+               forward (10 d H pairs for the backward), pairs_b = visible (query,
+               key) pairs of sequence b, over the measured step time;
+  roofline     the attention kernel alone, timed with HIP events recorded on its own
+               stream right before and after its launch (library profiling hook),
+               against the published dense bf16 MFMA peak; `traffic` is HBM bytes per
+               launch from committed rocprofv3 counter runs, or null when the kernel
+               source changed since they were taken;
+  cpu_baseline the fp64 oracle on a bounded sample of the same batch, on every host
+               core (a reported baseline, not a target); its outputs double as a
+               parity spot-check of the GPU result on the sampled pairs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "ja_fwd_kernel": ["ja_fwd.hip", "ja_common.h", "ja_tiles.h", "ja_internal.h"],
+    "ja_bwd_kernels": ["ja_bwd.hip", "ja_common.h", "ja_tiles.h", "ja_internal.h"],
+}
+METRIC = "useful (unpadded) bf16 TFLOP/s of jagged attn fwd; % of MI355X MFMA peak"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def visible_pairs(lq: np.ndarray, lk: np.ndarray, causal: bool, window: int) -> int:
+    """Exact number of visible (query, key) pairs of a jagged batch."""
+    total = 0
+    for Lq, Lk in zip(lq.tolist(), lk.tolist()):
+        if Lq <= 0 or Lk <= 0:
+            continue
+        if not causal and window == 0:
+            total += Lq * Lk
+            continue
+        i = np.arange(Lq, dtype=np.int64)
+        lo = np.zeros(Lq, dtype=np.int64) if window == 0 else np.maximum(0, i - window + 1)
+        if causal:
+            hi = np.minimum(i, Lk - 1)
+        else:
+            hi = np.full(Lq, Lk - 1, dtype=np.int64) if window == 0 else np.minimum(Lk - 1, i + window - 1)
+        total += int(np.maximum(0, hi - lo + 1).sum())
+    return total
+
+
+def kernel_sha(name: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        p = os.path.join(ROOT, "jagged_attention_recsys_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(name: str, workload: str):
+    """HBM bytes per launch from committed counter runs, if taken on the current kernel source."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(name, {}).get(workload)
+    if not rec or rec.get("source_sha256") != kernel_sha(name):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--bwd", action="store_true", help="time forward + backward (softmax workloads)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the attention path on a single MI355X and has "
+              "no multi-GPU path (each sequence and head is independent; sharding is by sequence, see the "
+              "design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import jagged_attention_recsys_amd as ja
+    from jagged_attention_recsys_amd import _lib
+    from jagged_attention_recsys_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    lib = _lib.load()  # raises if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] generating workload {args.workload}")
+    w = W.workload(args.workload)
+    if args.bwd and w.act != "softmax":
+        print("--bwd supports the softmax workloads (2 and 5)", file=sys.stderr)
+        return 2
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if a.dtype == np.uint16:
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    q, k, v = up(w.q), up(w.k), up(w.v)
+    qo, ko = up(w.q_offsets), up(w.k_offsets)
+    dout = up(w.dout) if (args.bwd and w.dout is not None) else (torch.randn_like(q) if args.bwd else None)
+    Tq, Tk = q.shape[0], k.shape[0]
+    out = torch.empty_like(q)
+    lse = torch.empty((Tq, w.H), dtype=torch.float32, device=dev) if w.act == "softmax" else None
+    ws = torch.empty(max(ja.fwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window), 256),
+                     dtype=torch.uint8, device=dev)
+    if args.bwd:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(max(ja.bwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window), 256),
+                          dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    pairs = visible_pairs(w.lq, w.lk, w.causal, w.window)
+    fwd_flop = 4.0 * w.d * w.H * pairs
+    bwd_flop = 10.0 * w.d * w.H * pairs if args.bwd else 0.0
+
+    def step(ev=None):
+        if ev is not None:
+            lib.ja_set_profile_events(ev[0].cuda_event, ev[1].cuda_event)
+        ja.jagged_attn_fwd(q, k, v, qo, ko, act=w.act, causal=w.causal, window=w.window, scale=w.scale,
+                           out=out, lse=lse, workspace=ws, stream=stream)
+        if args.bwd:
+            if ev is not None:
+                lib.ja_set_profile_events(ev[2].cuda_event, ev[3].cuda_event)
+            ja.jagged_attn_bwd(q, k, v, out, dout, lse, qo, ko, act=w.act, causal=w.causal, window=w.window,
+                               scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws, stream=stream)
+        if ev is not None:
+            lib.ja_set_profile_events(None, None)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nev = 4 if args.bwd else 2
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for evs in events:  # create the underlying HIP events before handing them to the library
+        for e in evs:
+            e.record(stream)
+    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    whole0.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    whole1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_events = whole0.elapsed_time(whole1) / args.steps
+    fwd_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    bwd_kernel_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if args.bwd else None
+    total_flop = fwd_flop + bwd_flop
+    value = total_flop / (ms_per_step * 1e-3) / 1e12
+
+    name = "ja_fwd_kernel"
+    achieved = fwd_flop / (fwd_kernel_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(name, f"w{args.workload}"),
+                "kernel": name, "kernel_ms": round(fwd_kernel_ms, 4),
+                "flop_per_launch": fwd_flop}
+    if args.workload in (3, 4):
+        # short key/value (3) and short query (4) batches are HBM-bound: their
+        # minimum traffic is reading Q, K, V once and writing O once.
+        esz = 2
+        min_bytes = esz * w.H * w.d * (2 * Tq + 2 * Tk)
+        roofline["min_hbm_bytes"] = min_bytes
+        roofline["hbm_gbs_at_min_bytes"] = round(min_bytes / (fwd_kernel_ms * 1e-3) / 1e9, 1)
+        roofline["hbm_frac"] = round(roofline["hbm_gbs_at_min_bytes"] / PEAK_HBM_GBS, 4)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_events": round(ms_events, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.extra.get("description", w.name), "B": w.B, "H": w.H, "d": w.d,
+                   "act": w.act, "causal": bool(w.causal), "window": int(w.window), "q_tokens": int(Tq),
+                   "kv_tokens": int(Tk), "visible_pairs": int(pairs), "fwd_flop": fwd_flop,
+                   "bwd_flop": bwd_flop, "phases": "fwd+bwd" if args.bwd else "fwd"},
+        "roofline": roofline,
+    }
+    if args.bwd:
+        result["bwd"] = {"kernel_ms": round(bwd_kernel_ms, 4),
+                         "tflops": round(bwd_flop / (bwd_kernel_ms * 1e-3) / 1e12, 2)}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, out, lse, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
+    """Time the fp64 oracle on a bounded sample of (sequence, head) pairs of the batch."""
+    import oracle  # test infrastructure: used here for the CPU baseline only
+
+    rng = np.random.default_rng(1234)
+    B, H = w.B, w.H
+    order = [(int(b), int(h)) for b in rng.permutation(B) for h in range(H)]
+    pair_flop = np.array([4.0 * w.d * visible_pairs(w.lq[b:b + 1], w.lk[b:b + 1], w.causal, w.window)
+                          for b, _ in order])
+    # Calibrate the oracle's rate on a growing prefix of the pair order (at least
+    # ~1 s of work), then fill the budget.
+    mask = np.zeros((B, H), dtype=bool)
+    rate, n_cal = None, 1
+    while rate is None:
+        mask[:] = False
+        for b, h in order[:n_cal]:
+            mask[b, h] = True
+        t = time.perf_counter()
+        oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale, pair_mask=mask)
+        dt = time.perf_counter() - t
+        if dt >= 1.0 or n_cal >= len(order):
+            rate = max(pair_flop[:n_cal].sum(), 1.0) / max(dt, 1e-4)
+        n_cal *= 2
+    budget_flop = rate * budget_s
+    mask[:] = False
+    acc = 0.0
+    for i, (b, h) in enumerate(order):
+        if acc > 0 and acc + pair_flop[i] > budget_flop:
+            continue
+        mask[b, h] = True
+        acc += pair_flop[i]
+    log(f"[bench] cpu baseline: {int(mask.sum())} pairs, {acc:.3g} flop")
+    t = time.perf_counter()
+    ref, ref_lse = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale,
+                              pair_mask=mask)
+    dt = time.perf_counter() - t
+    # parity spot-check of the GPU output on the same pairs
+    got = out_gpu.float().cpu().numpy().astype(np.float64)
+    sel = np.zeros(got.shape[:2], dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            if mask[b, h]:
+                sel[w.q_offsets[b]:w.q_offsets[b + 1], h] = True
+    err = np.abs(got[sel] - ref[sel])
+    return {"value": round(acc / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{int(mask.sum())} of {B * H} (sequence, head) pairs of the same batch, "
+                      f"{acc:.4g} useful flop, fp64 C oracle on all host cores",
+            "parity_on_sample": {"max_abs": float(err.max()) if err.size else 0.0,
+                                 "mean_abs": float(err.mean()) if err.size else 0.0,
+                                 "elements": int(err.size)}}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -144,6 +144,14 @@ ja_status_t ja_fwd_tile_shape(int32_t B, int32_t d, int64_t Tq, int32_t act, int
  * workspace. Returns JA_OK or JA_ERR_INVALID_OFFSETS. */
 ja_status_t ja_validate_offsets(const int32_t* offsets, int32_t B, int64_t T, void* stream);
 
+/* Profiling aid. While set (non-NULL), each jagged_attn_fwd / jagged_attn_bwd
+ * call made from this host thread records the caller's hipEvent_t `before` on its
+ * stream immediately before the first attention kernel (after the scheduler) and
+ * `after` immediately after the last one, so that the elapsed time between them is
+ * the attention kernels' own duration. Pass NULL, NULL to stop. The events are
+ * owned by the caller and must outlive the calls that record them. */
+void ja_set_profile_events(void* before, void* after);
+
 /* Static string for a status code. */
 const char* ja_status_string(ja_status_t status);
 

@@ -19,6 +19,10 @@ using namespace ja;
 namespace {
 
 constexpr size_t kWsAlign = 256;
+
+// Events recorded around the attention kernels (ja_set_profile_events).
+thread_local hipEvent_t g_prof_before = nullptr;
+thread_local hipEvent_t g_prof_after = nullptr;
 constexpr int kMaxDevices = 64;
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
@@ -155,7 +159,9 @@ ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v, const i
     int64_t grid = (int64_t)device_cus() * fwd_occupancy(dtype, d, act, p.split);
     if (grid > max_items) grid = max_items;
     if (grid < 1) grid = 1;
+    if (g_prof_before && hipEventRecord(g_prof_before, s) != hipSuccess) return JA_ERR_HIP;
     if (launch_fwd(fa, dtype, d, act, p.split, (int)grid, s) != hipSuccess) return JA_ERR_HIP;
+    if (g_prof_after && hipEventRecord(g_prof_after, s) != hipSuccess) return JA_ERR_HIP;
     return JA_OK;
 }
 
@@ -216,6 +222,11 @@ ja_status_t ja_validate_offsets(const int32_t* offsets, int32_t B, int64_t T, vo
     for (int32_t b = 0; b < B; ++b)
         if (h[b + 1] < h[b]) return JA_ERR_INVALID_OFFSETS;
     return JA_OK;
+}
+
+void ja_set_profile_events(void* before, void* after) {
+    g_prof_before = static_cast<hipEvent_t>(before);
+    g_prof_after = static_cast<hipEvent_t>(after);
 }
 
 const char* ja_status_string(ja_status_t status) {

@@ -3,7 +3,13 @@ its C ABI binding, compare against the fp64 oracle with the stated tolerances.
 
 Tolerances:
   * fp32 inputs: max|x - y| / max|y| <= 1e-5 over all compared elements;
-  * bf16 in / fp32 accumulate: max|x - y| <= 2e-2 and mean|x - y| <= 2e-3.
+  * bf16 in / fp32 accumulate: max|x - y| <= 2e-2 and mean|x - y| <= 2e-3 (strict:
+    used for the named workloads).
+  * non-strict bf16 (edge cases whose outputs can be large, e.g. one or two keys per
+    sequence under SiLU/GELU): |x - y| <= 2e-2 + 2^-8 |y| elementwise and the same mean
+    bound. The relative term is the arithmetic's own floor: P is rounded to bf16 before
+    the second product and the output is rounded to bf16, each within 2^-9 relative, so
+    an output of magnitude 6 already carries up to 0.023 of rounding.
 """
 from __future__ import annotations
 
@@ -15,6 +21,7 @@ import torch
 F32_REL = 1e-5
 BF16_MAX = 2e-2
 BF16_MEAN = 2e-3
+BF16_REL = 2.0 ** -8
 
 
 def say(msg: str) -> None:
@@ -45,7 +52,8 @@ def rows_of_pairs(offsets: np.ndarray, H: int, pair_mask: np.ndarray | None):
     return sel
 
 
-def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.ndarray | None = None) -> dict:
+def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.ndarray | None = None,
+            strict: bool = True) -> dict:
     """Assert the tolerance for `dtype` ("f32" or "bf16"); returns the error statistics."""
     if sel is not None:
         got, ref = got[sel], ref[sel]
@@ -61,8 +69,13 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.nda
         rel = stats["max_abs"] / max(stats["max_ref"], 1e-30)
         stats["rel"] = rel
         assert rel <= F32_REL, f"{what}: relative error {rel:.3e} > {F32_REL} ({stats})"
-    else:
+    elif strict:
         assert stats["max_abs"] <= BF16_MAX, f"{what}: max abs error {stats['max_abs']:.4e} > {BF16_MAX} ({stats})"
+        assert stats["mean_abs"] <= BF16_MEAN, f"{what}: mean abs error {stats['mean_abs']:.4e} > {BF16_MEAN}"
+    else:
+        excess = float(np.max(err - BF16_REL * np.abs(ref)))
+        stats["excess"] = excess
+        assert excess <= BF16_MAX, f"{what}: |err| - 2^-8|ref| reaches {excess:.4e} > {BF16_MAX} ({stats})"
         assert stats["mean_abs"] <= BF16_MEAN, f"{what}: mean abs error {stats['mean_abs']:.4e} > {BF16_MEAN}"
     return stats
 
