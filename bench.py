@@ -97,7 +97,12 @@ def main() -> int:
     ap.add_argument("--bwd", action="store_true", help="time forward + backward (softmax workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy (y = x * 1) of MIB MiB, 5 times: the reference "
+                         "for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -236,6 +241,21 @@ def main() -> int:
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def copy_calibration(mib: int) -> int:
+    """A plain streaming kernel of known traffic: reads and writes mib MiB per launch."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": 5}), flush=True)
     return 0
 
 

@@ -5,33 +5,38 @@
 // Dot-Product Attention (GDPA)" sections of the GEM training post): act is an
 // online softmax (running max, running sum, rescaled accumulator) or a pointwise
 // SiLU / tanh-GELU normalised by 1/Lk with no max, no rescale and no correction
-// stage. Sliding-window and causal tiles that no query can see are never loaded
-// ("BlockAttention" section: off-window tiles are skipped).
+// stage. Key tiles that no query of a work item can see (causal diagonal, window
+// edges: "BlockAttention" section) are never loaded.
 //
 // Work decomposition. A persistent grid pops (sequence, query-tile, head) items,
-// longest first, from the list ja_sched.hip built on the device. Each workgroup
-// has four waves.
-//   * Standard layout: the item is a 128-row query tile; wave w owns rows
-//     [32w, 32w+32) and all four waves share each 64-key stage in LDS.
+// longest first, from the list ja_sched.hip built on the device.
+//   * Standard layout: 8 waves, a 256-row query tile; wave w owns rows
+//     [32w, 32w+32) and all waves share each 64-key stage in LDS.
 //   * Split layout (short queries, e.g. pooled attention with 32 seeds): the item
-//     is a 32-row query tile; the waves split each 128-key stage four ways and
-//     merge their partial results through LDS at the end.
+//     is a 32-row query tile; the waves split each stage's keys and merge their
+//     partial results through LDS at the end.
 //
 // Per wave and 32-key block the scores are computed transposed, S^T = K Q^T, on
-// the 32x32 matrix cores: A = K rows from LDS, B = the wave's queries held in
-// registers for the whole item. In the C layout each lane then owns one query
-// column, so the softmax statistics are per-lane scalars and a row reduction is a
-// 16-register loop plus one exchange between the two half-waves. The probabilities
-// P^T are already in the B-operand layout of the second product O^T += V^T P^T, so
-// they feed it without any data movement; V is stored transposed in LDS (and keys
-// are permuted inside the block, see key_of_arow) so that each lane's A operand is
-// one contiguous vector read.
+// the 32x32x16 bf16 matrix cores: A = K rows from LDS, B = the wave's queries
+// held in registers for the whole item. In the C layout each lane then owns one
+// query column, so the softmax statistics are per-lane scalars and a row
+// reduction is a 16-register loop plus one permlane32 swap between the half-waves.
+// P^T is already in the B-operand layout of the second product O^T += V^T P^T.
+// The V^T operand is read from V's natural [key][d] layout with the LDS transpose
+// read (ds_read_tr16_b64: each 16-lane group gathers 4 keys x 16 dims), and keys
+// are permuted inside each 32-key block (key_of_arow) so that one lane's 8 keys
+// are 2 x 4 consecutive rows.
 //
-// K/V stages are double-buffered: the next stage is fetched from HBM into
-// registers (coalesced 16-byte loads, zero-filled past the sequence end) while the
-// current one is consumed, then written to the other LDS buffer; one barrier per
-// stage. Masks are evaluated only on stages that cross the sequence end, the
-// causal diagonal or a window edge; fully invisible blocks are skipped per wave.
+// Memory path. K and V stages stream from HBM straight into LDS with buffer loads
+// (no staging registers). The buffer descriptor of a stage ends at the sequence's
+// last key, so keys past the end read as zero (softmax masks them; for SiLU/GELU
+// act(0) = 0 and V = 0, so they contribute nothing). 16-byte chunks are
+// XOR-swizzled per row so that both the matrix-operand reads of K and the
+// transpose reads of V hit distinct LDS banks. Stages are double-buffered: the
+// next stage's loads are issued before the current stage is consumed.
+//
+// Masks are evaluated only on blocks that cross the sequence end, the causal
+// diagonal or a window edge; fully invisible blocks are skipped per wave.
 // Softmax rescaling is lazy: the running max is only raised when a block exceeds
 // it by more than 2^8, which leaves the result unchanged in exact arithmetic.
 #include <math.h>
@@ -45,32 +50,40 @@ namespace {
 
 template <typename T, int D, bool SPLIT>
 struct FwdCfg {
-    static constexpr int NW = 4;                    // waves per workgroup
-    static constexpr int WQ = SPLIT ? 1 : 4;        // query slices
-    static constexpr int WK = NW / WQ;              // key slices
-    static constexpr int NB = SPLIT ? 1 : 2;        // 32-key blocks per wave per stage
-    static constexpr int BM = 32 * WQ;              // query rows per item
-    static constexpr int KT = 32 * NB * WK;         // keys per stage
+    static constexpr int NW = SPLIT ? (D == 128 ? 4 : 8) : 8;  // waves per workgroup
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int WQ = SPLIT ? 1 : NW;                 // query slices
+    static constexpr int WK = NW / WQ;                        // key slices
+    static constexpr int NB = SPLIT ? 1 : 2;                  // 32-key blocks per wave per stage
+    static constexpr int BM = 32 * WQ;                        // query rows per item
+    static constexpr int KT = 32 * NB * WK;                   // keys per stage
     static constexpr int KP = Mma<T>::KPACK;
-    static constexpr int NS = D / (2 * KP);         // k-steps of S^T over d
-    static constexpr int NT = 32 / (2 * KP);        // k-steps of P V over one 32-key block
-    static constexpr int ND = D / 32;               // 32-row blocks of O^T
+    static constexpr int NS = D / (2 * KP);                   // k-steps of S^T over d
+    static constexpr int NT = 32 / (2 * KP);                  // k-steps of P V per 32-key block
+    static constexpr int ND = D / 32;                         // 32-row blocks of O^T
     static constexpr int ESZ = (int)sizeof(T);
-    static constexpr int PAD = 16 / ESZ;            // 16 bytes of padding per LDS row
-    static constexpr int KPITCH = D + PAD;          // K stored [key][d]
-    static constexpr int VPITCH = KT + PAD;         // V stored transposed [d][key]
-    static constexpr int K_ELEMS = KT * KPITCH;
-    static constexpr int V_ELEMS = D * VPITCH;
-    static constexpr int STAGE_BYTES = (K_ELEMS + V_ELEMS) * ESZ;
-    static constexpr int VEC = 16 / ESZ;            // elements per 16-byte access
-    static constexpr int KLOADS = KT * D / VEC / 256;
-    static constexpr int VUNITS = (KT / 4) * (D / VEC);  // (4 keys x VEC dims) V units
-    static constexpr int VLOADS = (VUNITS + 255) / 256;
-    static constexpr int COMBINE_BYTES = SPLIT ? WK * 64 * (D / 2 + 2) * 4 : 0;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES > COMBINE_BYTES ? 2 * STAGE_BYTES : COMBINE_BYTES;
-    static_assert(KT * D % (VEC * 256) == 0, "K stage must split evenly over 256 threads");
+    static constexpr int ROWB = D * ESZ;                      // bytes per K/V row in LDS
+    static constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
+    static constexpr int TILE_BYTES = KT * ROWB;              // K or V of one stage
+    static constexpr int INSTR = TILE_BYTES / 1024;           // 64-lane x 16-byte loads per tile
+    static constexpr int SLICE = 64 * (D / 2 + 2);            // floats one wave hands over when merging
+    static_assert(TILE_BYTES % 1024 == 0, "tile must be whole 64-lane loads");
+    // Merge slots alternate between two free stage arrays.
+    static_assert(!SPLIT || ((WK / 2 + 1) / 2) * SLICE * 4 <= TILE_BYTES, "merge slots must fit");
     static_assert(D % (2 * KP) == 0 && D % 32 == 0, "unsupported head dim");
 };
+
+// XOR swizzle of the 16-byte chunks of an LDS row (bf16 rows of 4, 8 or 16
+// chunks). Within any 16 consecutive rows it maps a fixed chunk to 16 distinct
+// bank groups (matrix-operand reads of K), and for 4 consecutive rows two
+// adjacent chunks to 8 distinct groups (transpose reads of V).
+template <int CPR, int ESZ>
+__device__ __forceinline__ int swz(int row) {
+    if (ESZ != 2) return 0;
+    if (CPR == 16) return ((row & 7) << 1) | ((row >> 3) & 1);
+    if (CPR == 8) return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+    return (row >> 2) & 3;
+}
 
 template <typename T> struct Frag;
 template <> struct Frag<bf16> {
@@ -82,44 +95,13 @@ template <> struct Frag<float> {
     static __device__ __forceinline__ type zero() { return 0.0f; }
 };
 
-// Pack four keys' VEC-element rows into VEC transposed groups of four keys.
-template <typename T> struct VTrans;
-template <> struct VTrans<bf16> {
-    // r[i] holds 8 bf16 of key i; writes 8 x (4 keys) = 8 x 8 bytes.
-    static __device__ __forceinline__ void store(bf16* dst, int pitch, const u32x4 r[4]) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            u32x2 p;
-            p[0] = __builtin_amdgcn_perm(r[1][e >> 1], r[0][e >> 1], sel);
-            p[1] = __builtin_amdgcn_perm(r[3][e >> 1], r[2][e >> 1], sel);
-            *(u32x2*)(dst + e * pitch) = p;
-        }
-    }
-};
-template <> struct VTrans<float> {
-    static __device__ __forceinline__ void store(float* dst, int pitch, const u32x4 r[4]) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            u32x4 p;
-            p[0] = r[0][e];
-            p[1] = r[1][e];
-            p[2] = r[2][e];
-            p[3] = r[3][e];
-            *(u32x4*)(dst + e * pitch) = p;
-        }
-    }
-};
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bool visible(int row, int key, int Lk, int causal, int window) {
-    if (key >= Lk) return false;
-    if (causal && key > row) return false;
-    if (window > 0) {
-        int diff = row - key;
-        if (!causal && diff < 0) diff = -diff;
-        if (diff >= window) return false;
-    }
-    return true;
+    const int diff = row - key;
+    const int adiff = causal ? diff : (diff < 0 ? -diff : diff);
+    return (key < Lk) & (!causal | (key <= row)) & ((window == 0) | (adiff < window));
 }
 
 template <typename T> __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
@@ -140,26 +122,48 @@ template <> __device__ __forceinline__ void store4<float>(float* dst, float a, f
     *(floatx4*)dst = v;
 }
 
-template <typename T, int D, int ACT, bool SPLIT>
-__global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
+// Max of x over lanes l and l^32 (the two halves of a C-tile column).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+template <typename T, int D, int ACT, bool SPLIT, int NTHREADS = FwdCfg<T, D, SPLIT>::THREADS>
+__global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
+    // The body uses gfx950-only types and builtins; the host pass only needs the
+    // kernel's signature for its launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
     using C = FwdCfg<T, D, SPLIT>;
     using M = Mma<T>;
     typedef typename Frag<T>::type frag;
     constexpr int KP = C::KP;
 
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+    // Two K/V stage buffers as four distinct arrays: the loads of one stage and the
+    // reads of the other then have provably disjoint targets, so the compiler does
+    // not wait for the prefetch before reading the current stage.
+    __shared__ __attribute__((aligned(1024))) char lds_k0[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_v0[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_k1[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_v1[C::TILE_BYTES];
     __shared__ int s_item;
+    __shared__ float s_max[SPLIT ? C::WK * 64 : 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
     const int wq = SPLIT ? 0 : wave;
     const int wk = SPLIT ? wave : 0;
     const int col = lane & 31, grp = lane >> 5;
     const int total = a.counters[kCtrTotal];
     const T* __restrict__ Qg = (const T*)a.q;
-    const T* __restrict__ Kg = (const T*)a.k;
-    const T* __restrict__ Vg = (const T*)a.v;
+    const char* __restrict__ Kg = (const char*)a.k;
+    const char* __restrict__ Vg = (const char*)a.v;
     T* __restrict__ Og = (T*)a.out;
-    const int64_t rs = (int64_t)a.H * D;  // token row stride, elements
+    const int64_t rs = (int64_t)a.H * D;          // token row stride, elements
+    const uint32_t rsb = (uint32_t)(rs * C::ESZ);  // ... bytes
     const int causal = a.causal, window = a.window;
 
     // Softmax works in the exp2 domain. With scale > 0 the row max is taken on raw
@@ -167,13 +171,52 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
     const bool prescale = !(a.scale > 0.0f);
     const float c_exp = prescale ? 1.0f : a.scale * kLog2e;
 
-    const int k_arow = key_of_arow<KP>(col);  // this lane's K row inside a 32-key block
+    // ---- per-lane constant LDS offsets -------------------------------------
+    // K (A operand of S^T): this lane's K row inside a 32-key block and its chunks.
+    const int k_row = key_of_arow<KP>(col);
+    int koff[C::NS];
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+        if constexpr (KP == 8) {
+            const int c = 2 * s + grp;
+            koff[s] = k_row * C::ROWB + ((c ^ swz<C::CPR, C::ESZ>(k_row)) << 4);
+        } else {
+            koff[s] = k_row * C::ROWB + (2 * s + grp) * 4;
+        }
+    }
+    // V (A operand of O^T += V^T P^T). bf16: transpose reads; lane i of each
+    // 16-lane group addresses 4 dims of key row (i/4) of a 4-key quad.
+    int voff[C::ND][2];
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+            if constexpr (KP == 8) {
+                const int i = lane & 15, cb = (lane >> 4) & 1;
+                const int row = 8 * grp + 4 * hq + (i >> 2);
+                const int d = 32 * db + 16 * cb + 4 * (i & 3);
+                const int c = d >> 3;
+                voff[db][hq] = row * C::ROWB + ((c ^ swz<C::CPR, C::ESZ>(row)) << 4) + 8 * ((d >> 2) & 1);
+            } else {
+                voff[db][hq] = grp * C::ROWB + (32 * db + col) * 4;
+            }
+        }
+    // Loads: this lane's row and swizzled chunk for each 64-lane load it issues.
+    constexpr int LPW = (C::INSTR + C::NW - 1) / C::NW;  // loads per wave per tile (upper bound)
+    uint32_t ld_voff[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int inst = wave + j * C::NW;
+        const int slot = inst * 64 + lane;
+        const int row = slot / C::CPR, p = slot % C::CPR;
+        ld_voff[j] = (uint32_t)row * rsb + (uint32_t)((p ^ swz<C::CPR, C::ESZ>(row)) << 4);
+    }
 
     for (;;) {
         __syncthreads();
         if (tid == 0) s_item = atomicAdd(&a.counters[kCtrPop], 1);
         __syncthreads();
-        const int idx = s_item;
+        const int idx = __builtin_amdgcn_readfirstlane(s_item);  // same for every lane
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
         const int b = a.items[2 * pair], qt = a.items[2 * pair + 1];
@@ -189,9 +232,6 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
         const int qw0 = q0 + 32 * wq;  // first query row of this wave
         const int my_row = qw0 + col;
 
-        const T* Kseq = Kg + ko * rs + (int64_t)h * D;
-        const T* Vseq = Vg + ko * rs + (int64_t)h * D;
-
         // Queries as the B operand of S^T = K Q^T, kept in registers.
         frag qf[C::NS];
         {
@@ -206,64 +246,35 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
         for (int i = 0; i < C::ND; ++i) oacc[i] = floatx16{};
         float m_run = -INFINITY, l_run = 0.0f;
 
-        u32x4 kr[C::KLOADS];
-        u32x4 vr[C::VLOADS][4];
+        const char* Kseq = Kg + (ko * rs + (int64_t)h * D) * C::ESZ;
+        const char* Vseq = Vg + (ko * rs + (int64_t)h * D) * C::ESZ;
 
-        auto issue = [&](int kt) {
+        // Stage kt -> (kdst, vdst): K and V rows [kt*KT, kt*KT + KT) of this
+        // sequence and head; rows at or past Lk read as zero.
+        auto issue = [&](int kt, char* kdst_g, char* vdst_g) {
             const int kbase = kt * C::KT;
-            const int nvalid = Lk - kbase;
+            const uint32_t nrec =
+                __builtin_amdgcn_readfirstlane((uint32_t)min(max(Lk - kbase, 0), C::KT) * rsb);
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(Kseq + (int64_t)kbase * rsb), (short)0, (int)nrec, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(Vseq + (int64_t)kbase * rsb), (short)0, (int)nrec, 0x00020000);
+            lds_char* kdst = (lds_char*)kdst_g;
+            lds_char* vdst = (lds_char*)vdst_g;
 #pragma unroll
-            for (int i = 0; i < C::KLOADS; ++i) {
-                const int chunk = i * 256 + tid;
-                const int key = chunk / (D / C::VEC), c = chunk % (D / C::VEC);
-                kr[i] = key < nvalid ? *(const u32x4*)(Kseq + (int64_t)(kbase + key) * rs + c * C::VEC)
-                                     : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int j = 0; j < C::VLOADS; ++j) {
-                const int u = j * 256 + tid;
-                const int kg = u % (C::KT / 4), dc = u / (C::KT / 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = 4 * kg + i;
-                    vr[j][i] = (u < C::VUNITS && key < nvalid)
-                                   ? *(const u32x4*)(Vseq + (int64_t)(kbase + key) * rs + dc * C::VEC)
-                                   : u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-        };
-        auto store = [&](int buf) {
-            T* kl = (T*)(smem + buf * C::STAGE_BYTES);
-            T* vl = kl + C::K_ELEMS;
-#pragma unroll
-            for (int i = 0; i < C::KLOADS; ++i) {
-                const int chunk = i * 256 + tid;
-                const int key = chunk / (D / C::VEC), c = chunk % (D / C::VEC);
-                *(u32x4*)(kl + key * C::KPITCH + c * C::VEC) = kr[i];
-            }
-#pragma unroll
-            for (int j = 0; j < C::VLOADS; ++j) {
-                const int u = j * 256 + tid;
-                if (u < C::VUNITS) {
-                    const int kg = u % (C::KT / 4), dc = u / (C::KT / 4);
-                    VTrans<T>::store(vl + (dc * C::VEC) * C::VPITCH + 4 * kg, C::VPITCH, vr[j]);
+            for (int j = 0; j < LPW; ++j) {
+                const int inst = wave + j * C::NW;
+                if (C::INSTR % C::NW == 0 || inst < C::INSTR) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst + inst * 1024, 16, ld_voff[j], 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst + inst * 1024, 16, ld_voff[j], 0, 0, 0);
                 }
             }
         };
 
-        if (kt_hi > kt_lo) {
-            issue(kt_lo);
-            store(0);
-            __syncthreads();
-        }
-
-        for (int kt = kt_lo; kt < kt_hi; ++kt) {
-            const int buf = (kt - kt_lo) & 1;
-            const bool more = kt + 1 < kt_hi;
-            if (more) issue(kt + 1);
-
-            const T* kl = (const T*)(smem + buf * C::STAGE_BYTES);
-            const T* vl = kl + C::K_ELEMS;
+        // Consume the stage in (kl, vl) while the next one (if any) streams into
+        // (kn, vn).
+        auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
+            if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
             const int kw0 = kt * C::KT + wk * 32 * C::NB;  // first key of this wave's blocks
             const bool skip = qw0 >= Lq || block_all_masked(qw0, 32, kw0, 32 * C::NB, Lk, causal, window);
             if (!skip) {
@@ -271,25 +282,13 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < C::NB; ++nb) {
                     sacc[nb] = floatx16{};
-                    const T* krow = kl + (wk * 32 * C::NB + nb * 32 + k_arow) * C::KPITCH + KP * grp;
+                    const char* kblk = kl + (wk * C::NB + nb) * 32 * C::ROWB;
 #pragma unroll
                     for (int s = 0; s < C::NS; ++s)
-                        sacc[nb] = M::run(*(const frag*)(krow + 2 * KP * s), qf[s], sacc[nb]);
+                        sacc[nb] = M::run(*(const frag*)(kblk + koff[s]), qf[s], sacc[nb]);
                 }
 
                 const bool need_mask = block_needs_mask(qw0, 32, kw0, 32 * C::NB, Lk, causal, window);
-                uint32_t vis = 0xffffffffu;  // bit nb*16+r: element visible
-                if (need_mask) {
-                    vis = 0;
-#pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
-                            if (visible(my_row, key, Lk, causal, window)) vis |= 1u << (nb * 16 + r);
-                        }
-                }
-
                 if (ACT == ACT_SOFTMAX) {
                     if (prescale) {
 #pragma unroll
@@ -301,15 +300,17 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
 #pragma unroll
                         for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r)
-                                if (!(vis >> (nb * 16 + r) & 1u)) sacc[nb][r] = -INFINITY;
+                            for (int r = 0; r < 16; ++r) {
+                                const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
+                                sacc[nb][r] = visible(my_row, key, Lk, causal, window) ? sacc[nb][r] : -INFINITY;
+                            }
                     }
                     float mx = -INFINITY;
 #pragma unroll
                     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-                    mx = xhalf_max(mx) * c_exp;
+                    mx = halves_max(mx) * c_exp;
                     if (__any(mx > m_run + 8.0f)) {
                         const float m_new = fmaxf(m_run, mx);
                         const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run - m_new);
@@ -319,21 +320,26 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
                         m_run = m_new;
                     }
                     const float msub = m_run == -INFINITY ? 0.0f : m_run;
+                    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const float p = fast_exp2(fmaf(sacc[nb][r], c_exp, -msub));
-                            l_run += p;
+                            lsum[r & 3] += p;
                             sacc[nb][r] = p;
                         }
+                    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
                 } else {
 #pragma unroll
                     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             float p = pointwise<ACT>(sacc[nb][r] * a.scale);
-                            if (need_mask && !(vis >> (nb * 16 + r) & 1u)) p = 0.0f;
+                            if (need_mask) {
+                                const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
+                                p = visible(my_row, key, Lk, causal, window) ? p : 0.0f;
+                            }
                             sacc[nb][r] = p;
                         }
                 }
@@ -352,55 +358,79 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
                         }
                     }
 #pragma unroll
-                for (int db = 0; db < C::ND; ++db) {
-                    const T* vrow = vl + (32 * db + col) * C::VPITCH + wk * 32 * C::NB + KP * grp;
+                for (int nb = 0; nb < C::NB; ++nb) {
+                    const char* vblk = vl + (wk * C::NB + nb) * 32 * C::ROWB;
 #pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb)
+                    for (int t = 0; t < C::NT; ++t) {
 #pragma unroll
-                        for (int t = 0; t < C::NT; ++t)
-                            oacc[db] = M::run(*(const frag*)(vrow + nb * 32 + 2 * KP * t), pf[nb][t], oacc[db]);
+                        for (int db = 0; db < C::ND; ++db) {
+                            frag af;
+                            if constexpr (KP == 8) {
+                                const char* base = vblk + 16 * t * C::ROWB;
+                                const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (__attribute__((address_space(3))) shortx4*)(base + voff[db][0]));
+                                const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (__attribute__((address_space(3))) shortx4*)(base + voff[db][1]));
+                                af = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
+                                                             0, 1, 2, 3, 4, 5, 6, 7);
+                            } else {
+                                af = *(const float*)(vblk + 2 * t * C::ROWB + voff[db][0]);
+                            }
+                            oacc[db] = M::run(af, pf[nb][t], oacc[db]);
+                        }
+                    }
                 }
             }
+            __syncthreads();
+        };
 
-            if (more) store(buf ^ 1);
+        if (kt_hi > kt_lo) {
+            issue(kt_lo, lds_k0, lds_v0);
             __syncthreads();
         }
+        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+            stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+            if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+        }
 
-        // Split layout: merge the four key slices through LDS (stage buffers are
-        // free: the loop ended on a barrier, or no stage was loaded at all).
+        // Split layout: merge the key slices (the loop ended on a barrier, or no
+        // stage was loaded, so the stage buffers are free). Softmax first agrees on
+        // the row max, then partial sums and accumulators are added pairwise.
         if constexpr (SPLIT) {
-            float* red_o = (float*)smem;                  // [wave][D/2][64]
-            float* red_m = red_o + C::WK * (D / 2) * 64;  // [wave][64]
-            float* red_l = red_m + C::WK * 64;            // [wave][64]
             if (ACT == ACT_SOFTMAX) {
-                red_m[wave * 64 + lane] = m_run;
+                s_max[wave * 64 + lane] = m_run;
                 __syncthreads();
                 float mg = -INFINITY;
 #pragma unroll
-                for (int w = 0; w < C::WK; ++w) mg = fmaxf(mg, red_m[w * 64 + lane]);
+                for (int w = 0; w < C::WK; ++w) mg = fmaxf(mg, s_max[w * 64 + lane]);
                 const float sc = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mg);
                 l_run *= sc;
 #pragma unroll
                 for (int i = 0; i < C::ND; ++i) oacc[i] *= sc;
                 m_run = mg;
             }
-            if (wave > 0) {
-                red_l[wave * 64 + lane] = l_run;
+            // slot j: [D/2 + 2][64] floats at (j/2) * SLICE of lds_k0 (j even) or lds_v0 (j odd)
+            auto slot = [&](int j) { return (float*)((j & 1) ? lds_v0 : lds_k0) + (j >> 1) * C::SLICE; };
 #pragma unroll
-                for (int i = 0; i < C::ND; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) red_o[((wave * C::ND + i) * 16 + r) * 64 + lane] = oacc[i][r];
-            }
-            __syncthreads();
-            if (wave == 0) {
-#pragma unroll
-                for (int w = 1; w < C::WK; ++w) {
-                    l_run += red_l[w * 64 + lane];
+            for (int half = C::WK / 2; half >= 1; half /= 2) {
+                if (wave >= half && wave < 2 * half) {
+                    float* dst = slot(wave - half);
 #pragma unroll
                     for (int i = 0; i < C::ND; ++i)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[i][r] += red_o[((w * C::ND + i) * 16 + r) * 64 + lane];
+                        for (int r = 0; r < 16; ++r) dst[(i * 16 + r) * 64 + lane] = oacc[i][r];
+                    dst[(D / 2) * 64 + lane] = l_run;
                 }
+                __syncthreads();
+                if (wave < half) {
+                    const float* src = slot(wave);
+#pragma unroll
+                    for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[i][r] += src[(i * 16 + r) * 64 + lane];
+                    l_run += src[(D / 2) * 64 + lane];
+                }
+                __syncthreads();
             }
         }
 
@@ -408,7 +438,7 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
             float inv;
             float lse_val = 0.0f;
             if (ACT == ACT_SOFTMAX) {
-                const float l_tot = xhalf_sum(l_run);
+                const float l_tot = halves_sum(l_run);
                 inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
                 lse_val = l_tot > 0.0f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
             } else {
@@ -427,23 +457,23 @@ __global__ __launch_bounds__(256) void ja_fwd_kernel(FwdArgs a) {
             }
         }
     }
+#else
+    (void)a;
+#endif
 }
 
 template <typename T, int D, int ACT, bool SPLIT>
-struct FwdKernel {
-    static void* fn() { return (void*)ja_fwd_kernel<T, D, ACT, SPLIT>; }
-};
-
-template <typename T, int D, int ACT, bool SPLIT>
 hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((ja_fwd_kernel<T, D, ACT, SPLIT>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((ja_fwd_kernel<T, D, ACT, SPLIT>), dim3(grid), dim3(FwdCfg<T, D, SPLIT>::THREADS), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int D, int ACT, bool SPLIT>
 int occupancy_one() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ja_fwd_kernel<T, D, ACT, SPLIT>, 256, 0) != hipSuccess)
+    const void* fn = reinterpret_cast<const void*>(&ja_fwd_kernel<T, D, ACT, SPLIT>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, FwdCfg<T, D, SPLIT>::THREADS, 0) != hipSuccess)
         return 1;
     return n > 0 ? n : 1;
 }
@@ -451,19 +481,19 @@ int occupancy_one() {
 // Dispatch over (dtype, d, act, split) to a callable template F<T, D, ACT, SPLIT>.
 template <template <typename, int, int, bool> class F, typename R, typename... Args>
 R dispatch(int dtype, int d, int act, bool split, R fail, Args... args) {
-#define JA_ACTS(T, D, S)                                              \
-    switch (act) {                                                    \
+#define JA_ACTS(T, D, S)                                                 \
+    switch (act) {                                                       \
         case ACT_SOFTMAX: return F<T, D, ACT_SOFTMAX, S>::call(args...); \
         case ACT_SILU: return F<T, D, ACT_SILU, S>::call(args...);       \
         case ACT_GELU: return F<T, D, ACT_GELU, S>::call(args...);       \
-        default: return fail;                                         \
+        default: return fail;                                            \
     }
-#define JA_DIMS(T, S)                      \
-    switch (d) {                           \
-        case 32: JA_ACTS(T, 32, S)         \
-        case 64: JA_ACTS(T, 64, S)         \
-        case 128: JA_ACTS(T, 128, S)       \
-        default: return fail;              \
+#define JA_DIMS(T, S)              \
+    switch (d) {                   \
+        case 32: JA_ACTS(T, 32, S)   \
+        case 64: JA_ACTS(T, 64, S)   \
+        case 128: JA_ACTS(T, 128, S) \
+        default: return fail;      \
     }
     if (dtype == 1) {
         if (split) { JA_DIMS(bf16, true) }
