@@ -63,6 +63,31 @@ ja_status_t plan_fwd(int32_t B, int32_t H, int32_t d, int64_t Tq, int32_t act, i
     return JA_OK;
 }
 
+struct BwdPlan {
+    int rows, cols;                     // rows per item, columns per stage
+    int64_t max_q_pairs, max_k_pairs;
+    size_t off_qctr, off_kctr, off_qtbase, off_ktbase, off_qitems, off_kitems, off_di, bytes;
+};
+
+ja_status_t plan_bwd(int32_t B, int32_t H, int64_t Tq, int64_t Tk, BwdPlan* p) {
+    p->rows = bwd_rows_per_item();
+    p->cols = bwd_cols_per_stage();
+    p->max_q_pairs = (Tq + p->rows - 1) / p->rows + B;
+    p->max_k_pairs = (Tk + p->rows - 1) / p->rows + B;
+    if (p->max_q_pairs * (int64_t)H >= INT32_MAX || p->max_k_pairs * (int64_t)H >= INT32_MAX)
+        return JA_ERR_UNSUPPORTED;
+    size_t o = 0;
+    p->off_qctr = o; o = align_up(o + sizeof(int32_t) * kCtrCount);
+    p->off_kctr = o; o = align_up(o + sizeof(int32_t) * kCtrCount);
+    p->off_qtbase = o; o = align_up(o + sizeof(int32_t) * ((size_t)B + 1));
+    p->off_ktbase = o; o = align_up(o + sizeof(int32_t) * ((size_t)B + 1));
+    p->off_qitems = o; o = align_up(o + sizeof(int32_t) * 2 * (size_t)p->max_q_pairs);
+    p->off_kitems = o; o = align_up(o + sizeof(int32_t) * 2 * (size_t)p->max_k_pairs);
+    p->off_di = o; o = align_up(o + sizeof(float) * (size_t)Tq * (size_t)H);
+    p->bytes = o;
+    return JA_OK;
+}
+
 int device_cus() {
     static std::atomic<int> cache[kMaxDevices];
     int dev = 0;
@@ -167,8 +192,12 @@ ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v, const i
 
 size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
                              int32_t causal, int32_t window, int32_t dtype) {
-    (void)B; (void)H; (void)d; (void)Tq; (void)Tk; (void)act; (void)causal; (void)window; (void)dtype;
-    return 0;
+    (void)causal;
+    if (check_common(B, H, d, Tq, Tk, act, window, 1.0f, dtype) != JA_OK) return 0;
+    if (!bwd_supported(dtype, d, act)) return 0;
+    BwdPlan p;
+    if (plan_bwd(B, H, Tq, Tk, &p) != JA_OK) return 0;
+    return p.bytes;
 }
 
 ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -176,10 +205,80 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const v
                             int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t causal,
                             int32_t window, float scale, int32_t dtype, void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes, void* stream) {
-    (void)q; (void)k; (void)v; (void)out; (void)dout; (void)lse; (void)q_offsets; (void)k_offsets;
-    (void)B; (void)H; (void)d; (void)Tq; (void)Tk; (void)act; (void)causal; (void)window; (void)scale;
-    (void)dtype; (void)dq; (void)dk; (void)dv; (void)workspace; (void)workspace_bytes; (void)stream;
-    return JA_ERR_UNSUPPORTED;
+    ja_status_t st = check_common(B, H, d, Tq, Tk, act, window, scale, dtype);
+    if (st != JA_OK) return st;
+    if (!bwd_supported(dtype, d, act)) return JA_ERR_UNSUPPORTED;
+    if (B == 0 || (Tq == 0 && Tk == 0)) return JA_OK;
+    if (!q_offsets || !k_offsets || !workspace) return JA_ERR_INVALID_ARG;
+    if (Tq > 0 && (!q || !out || !dout || !lse || !dq)) return JA_ERR_INVALID_ARG;
+    if (Tk > 0 && (!k || !v || !dk || !dv)) return JA_ERR_INVALID_ARG;
+    const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv, workspace};
+    for (const void* p16 : ptrs16)
+        if (!aligned(p16, 16)) return JA_ERR_INVALID_ARG;
+    if (!aligned(lse, 4) || !aligned(q_offsets, 4) || !aligned(k_offsets, 4)) return JA_ERR_INVALID_ARG;
+    BwdPlan p;
+    st = plan_bwd(B, H, Tq, Tk, &p);
+    if (st != JA_OK) return st;
+    if (workspace_bytes < p.bytes) return JA_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    SchedArgs sq;
+    sq.row_off = q_offsets;
+    sq.col_off = k_offsets;
+    sq.B = B;
+    sq.H = H;
+    sq.bm = p.rows;
+    sq.bn = p.cols;
+    sq.causal = causal ? 1 : 0;
+    sq.window = window;
+    sq.transposed = 0;
+    sq.max_pairs = p.max_q_pairs;
+    sq.tbase = reinterpret_cast<int32_t*>(ws + p.off_qtbase);
+    sq.items = reinterpret_cast<int32_t*>(ws + p.off_qitems);
+    sq.counters = reinterpret_cast<int32_t*>(ws + p.off_qctr);
+    SchedArgs sk = sq;
+    sk.row_off = k_offsets;
+    sk.col_off = q_offsets;
+    sk.transposed = 1;
+    sk.max_pairs = p.max_k_pairs;
+    sk.tbase = reinterpret_cast<int32_t*>(ws + p.off_ktbase);
+    sk.items = reinterpret_cast<int32_t*>(ws + p.off_kitems);
+    sk.counters = reinterpret_cast<int32_t*>(ws + p.off_kctr);
+    if (launch_sched(sq, s) != hipSuccess) return JA_ERR_HIP;
+    if (launch_sched(sk, s) != hipSuccess) return JA_ERR_HIP;
+
+    BwdArgs ba;
+    ba.q = q;
+    ba.k = k;
+    ba.v = v;
+    ba.out = out;
+    ba.dout = dout;
+    ba.lse = lse;
+    ba.dq = dq;
+    ba.dk = dk;
+    ba.dv = dv;
+    ba.di = reinterpret_cast<float*>(ws + p.off_di);
+    ba.q_off = q_offsets;
+    ba.k_off = k_offsets;
+    ba.q_items = sq.items;
+    ba.k_items = sk.items;
+    ba.q_counters = sq.counters;
+    ba.k_counters = sk.counters;
+    ba.H = H;
+    ba.Tq = (int32_t)Tq;
+    ba.Tk = (int32_t)Tk;
+    ba.causal = causal ? 1 : 0;
+    ba.window = window;
+    ba.scale = scale;
+    const int64_t cap = (int64_t)device_cus() * bwd_blocks_per_cu(d);
+    int64_t gq = p.max_q_pairs * H, gk = p.max_k_pairs * H;
+    gq = gq < cap ? gq : cap;
+    gk = gk < cap ? gk : cap;
+    if (gq < 1) gq = 1;
+    if (gk < 1) gk = 1;
+    if (launch_bwd(ba, d, (int)gq, (int)gk, s, g_prof_before, g_prof_after) != hipSuccess) return JA_ERR_HIP;
+    return JA_OK;
 }
 
 ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets, int32_t B, int32_t H, int32_t d,

@@ -1,0 +1,452 @@
+// ja_bwd.hip -- softmax jagged attention backward for gfx950, split into a
+// query-stationary dQ pass and a key-stationary dK/dV pass ("Jagged Sequence
+// Flash Attention" section of the GEM training post: dQ in its own pass, no
+// atomic accumulation of any gradient, no recomputation shared across passes).
+//
+// With P = exp(scale Q K^T - lse) (the forward's log-sum-exp per row):
+//   Di  = sum_c dO_ic O_ic                       (dQ pass prologue, to workspace)
+//   dP  = dO V^T,  dS = P o (dP - Di)
+//   dQ  = scale dS K                             (dQ pass, written once)
+//   dV  = P^T dO,  dK = scale dS^T Q             (dK/dV pass, written once)
+//
+// dQ pass: 4 waves, a 128-row query tile, wave w owns 32 rows. For each 64-key
+// stage (K and V streamed into LDS as in the forward): S^T = K Q^T and
+// dP^T = V dO^T on the matrix cores (queries and dO held as B operands in
+// registers, so every lane owns one query column), then dQ^T += K^T dS^T with K^T
+// read through LDS transpose reads.
+//
+// dK/dV pass: 4 waves, a 128-key tile, wave w owns 32 keys (K and V held as B
+// operands). For each 64-query stage (Q, dO, lse and Di streamed into LDS):
+// S = Q K^T and dP = dO V^T give lane-per-key C tiles; dV^T += dO^T P and
+// dK^T += Q^T dS use transpose reads of dO and Q. Query tiles no key of the item
+// can see (causal diagonal, window) are never loaded.
+#include <math.h>
+
+#include "ja_common.h"
+#include "ja_internal.h"
+#include "ja_lds.h"
+#include "ja_tiles.h"
+
+namespace ja {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;  // rows (queries or keys) per work item
+constexpr int kBwdStage = 64;             // columns (keys or queries) per stage
+
+template <typename T, int D>
+struct BwdCfg {
+    using STile = Tile<T, D, kBwdStage>;  // one stage of K, V, Q or dO
+    using Loader = TileLoader<STile, kBwdWaves>;
+    static constexpr int KP = STile::KP;
+    static constexpr int NS = STile::NS;
+    static constexpr int ND = STile::ND;
+    static constexpr int NB = kBwdStage / 32;  // 32-column blocks per stage
+    static constexpr int NT = 32 / (2 * KP);   // k-steps per 32-column block
+    static constexpr int ROWB = STile::ROWB;
+};
+
+// dQ pass ---------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdThreads) void ja_bwd_dq_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = BwdCfg<T, D>;
+    using M = Mma<T>;
+    typedef typename Frag<T>::type frag;
+    constexpr int KP = C::KP;
+
+    __shared__ __attribute__((aligned(1024))) char lds_k0[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_v0[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_k1[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_v1[C::STile::BYTES];
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, grp = lane >> 5;
+    const int total = a.q_counters[kCtrTotal];
+    const int64_t rs = (int64_t)a.H * D;
+    const uint32_t rsb = (uint32_t)(rs * (int)sizeof(T));
+    const int causal = a.causal, window = a.window;
+    const float c_exp = a.scale * kLog2e;
+
+    int koff[C::NS];
+    int toff[C::ND][2];
+    C::STile::row_offsets(col, grp, koff);
+    C::STile::tr_offsets(lane, toff);
+    typename C::Loader ld;
+    ld.init(wave, lane, rsb);
+
+    for (;;) {
+        __syncthreads();
+        if (tid == 0) s_item = atomicAdd(&a.q_counters[kCtrPop], 1);
+        __syncthreads();
+        const int idx = __builtin_amdgcn_readfirstlane(s_item);
+        if (idx >= total) break;
+        const int pair = idx / a.H, h = idx - pair * a.H;
+        const int b = a.q_items[2 * pair], qt = a.q_items[2 * pair + 1];
+        const int64_t qo = a.q_off[b], ko = a.k_off[b];
+        const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
+        const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
+        const int q0 = qt * kBwdRows;
+        const ColRange cr = visible_cols(Lq, Lk, q0, kBwdRows, causal, window, 0);
+        const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
+        const int kt_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
+        const int qw0 = q0 + 32 * wave;
+        const int my_row = qw0 + col;
+        const bool row_ok = my_row < Lq;
+        const int64_t qrow = (qo + my_row) * rs + (int64_t)h * D + KP * grp;
+
+        // Q^T and dO^T as B operands; Di from O and dO in the same layout.
+        frag qf[C::NS], dof[C::NS];
+        float di = 0.0f;
+        {
+            const T* qs = (const T*)a.q + qrow;
+            const T* ds = (const T*)a.dout + qrow;
+            const T* os = (const T*)a.out + qrow;
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) {
+                qf[s] = row_ok ? *(const frag*)(qs + 2 * KP * s) : Frag<T>::zero();
+                dof[s] = row_ok ? *(const frag*)(ds + 2 * KP * s) : Frag<T>::zero();
+                const frag of = row_ok ? *(const frag*)(os + 2 * KP * s) : Frag<T>::zero();
+                if constexpr (KP == 8) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) di = fmaf((float)dof[s][e], (float)of[e], di);
+                } else {
+                    di = fmaf(dof[s], of, di);
+                }
+            }
+        }
+        di = halves_sum(di);
+        const float nlse2 = row_ok ? -a.lse[(qo + my_row) * a.H + h] * kLog2e : 0.0f;
+        if (row_ok && grp == 0) a.di[(qo + my_row) * a.H + h] = di;
+
+        floatx16 dqacc[C::ND];
+#pragma unroll
+        for (int i = 0; i < C::ND; ++i) dqacc[i] = floatx16{};
+
+        const char* Kseq = (const char*)a.k + (ko * rs + (int64_t)h * D) * (int)sizeof(T);
+        const char* Vseq = (const char*)a.v + (ko * rs + (int64_t)h * D) * (int)sizeof(T);
+        auto issue = [&](int kt, char* kdst, char* vdst) {
+            const int kbase = kt * kBwdStage;
+            const uint32_t nrec =
+                __builtin_amdgcn_readfirstlane((uint32_t)min(max(Lk - kbase, 0), kBwdStage) * rsb);
+            ld.issue(Kseq + (int64_t)kbase * rsb, nrec, kdst, wave);
+            ld.issue(Vseq + (int64_t)kbase * rsb, nrec, vdst, wave);
+        };
+
+        auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
+            if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
+            const int kw0 = kt * kBwdStage;
+            const bool skip = qw0 >= Lq || block_all_masked(qw0, 32, kw0, kBwdStage, Lk, causal, window);
+            if (!skip) {
+                const bool need_mask = block_needs_mask(qw0, 32, kw0, kBwdStage, Lk, causal, window);
+                frag dsf[C::NB][C::NT];
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb) {
+                    floatx16 sacc = floatx16{}, dpacc = floatx16{};
+                    const char* kblk = kl + nb * 32 * C::ROWB;
+                    const char* vblk = vl + nb * 32 * C::ROWB;
+#pragma unroll
+                    for (int s = 0; s < C::NS; ++s) {
+                        sacc = M::run(C::STile::read_rows(kblk, koff[s]), qf[s], sacc);
+                        dpacc = M::run(C::STile::read_rows(vblk, koff[s]), dof[s], dpacc);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p = fast_exp2(fmaf(sacc[r], c_exp, nlse2));
+                        if (need_mask) {
+                            const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
+                            p = visible(my_row, key, Lk, causal, window) ? p : 0.0f;
+                        }
+                        sacc[r] = p * (dpacc[r] - di);
+                    }
+#pragma unroll
+                    for (int t = 0; t < C::NT; ++t) dsf[nb][t] = to_frag<T>(sacc, KP * t);
+                }
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb) {
+                    const char* kblk = kl + nb * 32 * C::ROWB;
+#pragma unroll
+                    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+                        for (int db = 0; db < C::ND; ++db)
+                            dqacc[db] = M::run(C::STile::read_tr(kblk, t, toff, db), dsf[nb][t], dqacc[db]);
+                }
+            }
+            __syncthreads();
+        };
+
+        if (kt_hi > kt_lo) {
+            issue(kt_lo, lds_k0, lds_v0);
+            __syncthreads();
+        }
+        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+            stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+            if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+        }
+
+        if (row_ok) {
+            T* dst = (T*)a.dq + (qo + my_row) * rs + (int64_t)h * D + 4 * grp;
+            const float sc = a.scale;
+#pragma unroll
+            for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    store4<T>(dst + 32 * i + 8 * j, dqacc[i][4 * j] * sc, dqacc[i][4 * j + 1] * sc,
+                              dqacc[i][4 * j + 2] * sc, dqacc[i][4 * j + 3] * sc);
+        }
+    }
+#else
+    (void)a;
+#endif
+}
+
+// dK/dV pass -------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = BwdCfg<T, D>;
+    using M = Mma<T>;
+    typedef typename Frag<T>::type frag;
+    constexpr int KP = C::KP;
+
+    __shared__ __attribute__((aligned(1024))) char lds_q0[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_o0[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_q1[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_o1[C::STile::BYTES];
+    __shared__ __attribute__((aligned(256))) float lds_l0[kBwdStage];
+    __shared__ __attribute__((aligned(256))) float lds_d0[kBwdStage];
+    __shared__ __attribute__((aligned(256))) float lds_l1[kBwdStage];
+    __shared__ __attribute__((aligned(256))) float lds_d1[kBwdStage];
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, grp = lane >> 5;
+    const int total = a.k_counters[kCtrTotal];
+    const int64_t rs = (int64_t)a.H * D;
+    const uint32_t rsb = (uint32_t)(rs * (int)sizeof(T));
+    const uint32_t hsb = (uint32_t)(a.H * 4);  // stride of one row of lse / Di, bytes
+    const int causal = a.causal, window = a.window;
+    const float c_exp = a.scale * kLog2e;
+
+    int roff[C::NS];
+    int toff[C::ND][2];
+    C::STile::row_offsets(col, grp, roff);
+    C::STile::tr_offsets(lane, toff);
+    typename C::Loader ld;
+    ld.init(wave, lane, rsb);
+
+    for (;;) {
+        __syncthreads();
+        if (tid == 0) s_item = atomicAdd(&a.k_counters[kCtrPop], 1);
+        __syncthreads();
+        const int idx = __builtin_amdgcn_readfirstlane(s_item);
+        if (idx >= total) break;
+        const int pair = idx / a.H, h = idx - pair * a.H;
+        const int b = a.k_items[2 * pair], kt = a.k_items[2 * pair + 1];
+        const int64_t qo = a.q_off[b], ko = a.k_off[b];
+        const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
+        const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
+        const int k0 = kt * kBwdRows;
+        const ColRange cr = visible_cols(Lk, Lq, k0, kBwdRows, causal, window, 1);
+        const int qs_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
+        const int qs_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
+        const int kw0 = k0 + 32 * wave;
+        const int my_key = kw0 + col;
+        const bool key_ok = my_key < Lk;
+        const int64_t krow = (ko + my_key) * rs + (int64_t)h * D + KP * grp;
+
+        frag kf[C::NS], vf[C::NS];
+        {
+            const T* ks = (const T*)a.k + krow;
+            const T* vs = (const T*)a.v + krow;
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) {
+                kf[s] = key_ok ? *(const frag*)(ks + 2 * KP * s) : Frag<T>::zero();
+                vf[s] = key_ok ? *(const frag*)(vs + 2 * KP * s) : Frag<T>::zero();
+            }
+        }
+        floatx16 dkacc[C::ND], dvacc[C::ND];
+#pragma unroll
+        for (int i = 0; i < C::ND; ++i) {
+            dkacc[i] = floatx16{};
+            dvacc[i] = floatx16{};
+        }
+
+        const char* Qseq = (const char*)a.q + (qo * rs + (int64_t)h * D) * (int)sizeof(T);
+        const char* Oseq = (const char*)a.dout + (qo * rs + (int64_t)h * D) * (int)sizeof(T);
+        const char* Lseq = (const char*)(a.lse + qo * a.H + h);
+        const char* Dseq = (const char*)(a.di + qo * a.H + h);
+        auto issue = [&](int qs, char* qdst, char* odst, float* ldst, float* ddst) {
+            const int qbase = qs * kBwdStage;
+            const int nvalid = min(max(Lq - qbase, 0), kBwdStage);
+            const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * rsb);
+            ld.issue(Qseq + (int64_t)qbase * rsb, nrec, qdst, wave);
+            ld.issue(Oseq + (int64_t)qbase * rsb, nrec, odst, wave);
+            // lse and Di of the stage's queries: one 64-lane dword load each.
+            if (wave < 2) {
+                const uint32_t nrec_s = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * hsb);
+                const char* src = (wave == 0 ? Lseq : Dseq) + (int64_t)qbase * hsb;
+                const __amdgpu_buffer_rsrc_t r =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, (int)nrec_s, 0x00020000);
+                lds_char* dst = (lds_char*)(wave == 0 ? ldst : ddst);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, (uint32_t)lane * hsb, 0, 0, 0);
+            }
+        };
+
+        auto stage = [&](int qs, const char* ql, const char* ol, const float* ll, const float* dl, char* qn,
+                         char* on, float* ln, float* dn) {
+            if (qs + 1 < qs_hi) issue(qs + 1, qn, on, ln, dn);
+            const int qbase = qs * kBwdStage;
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                const int qb0 = qbase + nb * 32;  // first query of this block
+                // Wave-uniform: lanes past the sequence end still feed the shared
+                // matrix operands (their K/V rows are zero and masked below).
+                const bool skip = qb0 >= Lq || block_all_masked(qb0, 32, kw0, 32, Lk, causal, window);
+                if (skip) continue;
+                const bool need_mask =
+                    qb0 + 32 > Lq || block_needs_mask(qb0, 32, kw0, 32, Lk, causal, window);
+                const char* qblk = ql + nb * 32 * C::ROWB;
+                const char* oblk = ol + nb * 32 * C::ROWB;
+                floatx16 sacc = floatx16{}, dpacc = floatx16{};
+#pragma unroll
+                for (int s = 0; s < C::NS; ++s) {
+                    sacc = M::run(C::STile::read_rows(qblk, roff[s]), kf[s], sacc);
+                    dpacc = M::run(C::STile::read_rows(oblk, roff[s]), vf[s], dpacc);
+                }
+                // Register r holds query qb0 + key_of_reg(grp, r): for bf16 two runs
+                // of 8 consecutive queries, read as float4s from lse / Di.
+                float lse_r[16], di_r[16];
+#pragma unroll
+                for (int r = 0; r < 16; r += 4) {
+                    const int ql_ = nb * 32 + key_of_reg<KP>(grp, r);
+                    if constexpr (KP == 8) {
+                        const floatx4 l4 = *(const floatx4*)(ll + ql_);
+                        const floatx4 d4 = *(const floatx4*)(dl + ql_);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            lse_r[r + e] = l4[e];
+                            di_r[r + e] = d4[e];
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int qe = nb * 32 + key_of_reg<KP>(grp, r + e);
+                            lse_r[r + e] = ll[qe];
+                            di_r[r + e] = dl[qe];
+                        }
+                    }
+                }
+                floatx16 dsacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(sacc[r], c_exp, -lse_r[r] * kLog2e));
+                    if (need_mask) {
+                        const int q = qb0 + key_of_reg<KP>(grp, r);
+                        p = (q < Lq && visible(q, my_key, Lk, causal, window)) ? p : 0.0f;
+                    }
+                    sacc[r] = p;
+                    dsacc[r] = p * (dpacc[r] - di_r[r]);
+                }
+#pragma unroll
+                for (int t = 0; t < C::NT; ++t) {
+                    const frag pf = to_frag<T>(sacc, KP * t);
+                    const frag dsf = to_frag<T>(dsacc, KP * t);
+#pragma unroll
+                    for (int db = 0; db < C::ND; ++db) {
+                        dvacc[db] = M::run(C::STile::read_tr(oblk, t, toff, db), pf, dvacc[db]);
+                        dkacc[db] = M::run(C::STile::read_tr(qblk, t, toff, db), dsf, dkacc[db]);
+                    }
+                }
+            }
+            __syncthreads();
+        };
+
+        if (qs_hi > qs_lo) {
+            issue(qs_lo, lds_q0, lds_o0, lds_l0, lds_d0);
+            __syncthreads();
+        }
+        for (int qs = qs_lo; qs < qs_hi; qs += 2) {
+            stage(qs, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
+            if (qs + 1 < qs_hi) stage(qs + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
+        }
+
+        if (key_ok) {
+            const int64_t base = (ko + my_key) * rs + (int64_t)h * D + 4 * grp;
+            T* dk = (T*)a.dk + base;
+            T* dv = (T*)a.dv + base;
+            const float sc = a.scale;
+#pragma unroll
+            for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    store4<T>(dk + 32 * i + 8 * j, dkacc[i][4 * j] * sc, dkacc[i][4 * j + 1] * sc,
+                              dkacc[i][4 * j + 2] * sc, dkacc[i][4 * j + 3] * sc);
+                    store4<T>(dv + 32 * i + 8 * j, dvacc[i][4 * j], dvacc[i][4 * j + 1], dvacc[i][4 * j + 2],
+                              dvacc[i][4 * j + 3]);
+                }
+        }
+    }
+#else
+    (void)a;
+#endif
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hipEvent_t before, hipEvent_t after) {
+    if (before && hipEventRecord(before, s) != hipSuccess) return hipErrorUnknown;
+    hipLaunchKernelGGL((ja_bwd_dq_kernel<bf16, D>), dim3(grid_q), dim3(kBwdThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ja_bwd_dkdv_kernel<bf16, D>), dim3(grid_k), dim3(kBwdThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (after && hipEventRecord(after, s) != hipSuccess) return hipErrorUnknown;
+    return hipSuccess;
+}
+
+template <int D>
+int occupancy_d() {
+    int n1 = 0, n2 = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n1, reinterpret_cast<const void*>(&ja_bwd_dq_kernel<bf16, D>), kBwdThreads, 0) != hipSuccess)
+        n1 = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n2, reinterpret_cast<const void*>(&ja_bwd_dkdv_kernel<bf16, D>), kBwdThreads, 0) != hipSuccess)
+        n2 = 1;
+    return (n1 < n2 ? n1 : n2) > 0 ? (n1 < n2 ? n1 : n2) : 1;
+}
+
+}  // namespace
+
+bool bwd_supported(int dtype, int d, int act) {
+    return dtype == 1 && (d == 32 || d == 64 || d == 128) && act == ACT_SOFTMAX;
+}
+
+int bwd_rows_per_item() { return kBwdRows; }
+int bwd_cols_per_stage() { return kBwdStage; }
+
+hipError_t launch_bwd(const BwdArgs& a, int d, int grid_q, int grid_k, hipStream_t stream, hipEvent_t before,
+                      hipEvent_t after) {
+    switch (d) {
+        case 32: return launch_d<32>(a, grid_q, grid_k, stream, before, after);
+        case 64: return launch_d<64>(a, grid_q, grid_k, stream, before, after);
+        case 128: return launch_d<128>(a, grid_q, grid_k, stream, before, after);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int bwd_blocks_per_cu(int d) {
+    switch (d) {
+        case 32: return occupancy_d<32>();
+        case 64: return occupancy_d<64>();
+        case 128: return occupancy_d<128>();
+        default: return 1;
+    }
+}
+
+}  // namespace ja

@@ -43,6 +43,7 @@
 
 #include "ja_common.h"
 #include "ja_internal.h"
+#include "ja_lds.h"
 #include "ja_tiles.h"
 
 namespace ja {
@@ -66,71 +67,14 @@ struct FwdCfg {
     static constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
     static constexpr int TILE_BYTES = KT * ROWB;              // K or V of one stage
     static constexpr int INSTR = TILE_BYTES / 1024;           // 64-lane x 16-byte loads per tile
+    using KVTile = Tile<T, D, KT>;
+    using Loader = TileLoader<KVTile, NW>;
     static constexpr int SLICE = 64 * (D / 2 + 2);            // floats one wave hands over when merging
     static_assert(TILE_BYTES % 1024 == 0, "tile must be whole 64-lane loads");
     // Merge slots alternate between two free stage arrays.
     static_assert(!SPLIT || ((WK / 2 + 1) / 2) * SLICE * 4 <= TILE_BYTES, "merge slots must fit");
     static_assert(D % (2 * KP) == 0 && D % 32 == 0, "unsupported head dim");
 };
-
-// XOR swizzle of the 16-byte chunks of an LDS row (bf16 rows of 4, 8 or 16
-// chunks). Within any 16 consecutive rows it maps a fixed chunk to 16 distinct
-// bank groups (matrix-operand reads of K), and for 4 consecutive rows two
-// adjacent chunks to 8 distinct groups (transpose reads of V).
-template <int CPR, int ESZ>
-__device__ __forceinline__ int swz(int row) {
-    if (ESZ != 2) return 0;
-    if (CPR == 16) return ((row & 7) << 1) | ((row >> 3) & 1);
-    if (CPR == 8) return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
-    return (row >> 2) & 3;
-}
-
-template <typename T> struct Frag;
-template <> struct Frag<bf16> {
-    typedef bf16x8 type;
-    static __device__ __forceinline__ type zero() { return type{}; }
-};
-template <> struct Frag<float> {
-    typedef float type;
-    static __device__ __forceinline__ type zero() { return 0.0f; }
-};
-
-typedef __attribute__((address_space(3))) char lds_char;
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bool visible(int row, int key, int Lk, int causal, int window) {
-    const int diff = row - key;
-    const int adiff = causal ? diff : (diff < 0 ? -diff : diff);
-    return (key < Lk) & (!causal | (key <= row)) & ((window == 0) | (adiff < window));
-}
-
-template <typename T> __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
-template <> __device__ __forceinline__ void store4<bf16>(bf16* dst, float a, float b, float c, float d) {
-    bf16x4 v;
-    v[0] = (bf16)a;
-    v[1] = (bf16)b;
-    v[2] = (bf16)c;
-    v[3] = (bf16)d;
-    *(bf16x4*)dst = v;
-}
-template <> __device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
-    floatx4 v;
-    v[0] = a;
-    v[1] = b;
-    v[2] = c;
-    v[3] = d;
-    *(floatx4*)dst = v;
-}
-
-// Max of x over lanes l and l^32 (the two halves of a C-tile column).
-__device__ __forceinline__ float halves_max(float x) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
 
 template <typename T, int D, int ACT, bool SPLIT, int NTHREADS = FwdCfg<T, D, SPLIT>::THREADS>
 __global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
@@ -171,46 +115,14 @@ __global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
     const bool prescale = !(a.scale > 0.0f);
     const float c_exp = prescale ? 1.0f : a.scale * kLog2e;
 
-    // ---- per-lane constant LDS offsets -------------------------------------
-    // K (A operand of S^T): this lane's K row inside a 32-key block and its chunks.
-    const int k_row = key_of_arow<KP>(col);
+    // Per-lane constant LDS offsets: K as the row operand of S^T, V through
+    // transpose reads, and the chunks this lane loads.
     int koff[C::NS];
-#pragma unroll
-    for (int s = 0; s < C::NS; ++s) {
-        if constexpr (KP == 8) {
-            const int c = 2 * s + grp;
-            koff[s] = k_row * C::ROWB + ((c ^ swz<C::CPR, C::ESZ>(k_row)) << 4);
-        } else {
-            koff[s] = k_row * C::ROWB + (2 * s + grp) * 4;
-        }
-    }
-    // V (A operand of O^T += V^T P^T). bf16: transpose reads; lane i of each
-    // 16-lane group addresses 4 dims of key row (i/4) of a 4-key quad.
     int voff[C::ND][2];
-#pragma unroll
-    for (int db = 0; db < C::ND; ++db)
-#pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
-            if constexpr (KP == 8) {
-                const int i = lane & 15, cb = (lane >> 4) & 1;
-                const int row = 8 * grp + 4 * hq + (i >> 2);
-                const int d = 32 * db + 16 * cb + 4 * (i & 3);
-                const int c = d >> 3;
-                voff[db][hq] = row * C::ROWB + ((c ^ swz<C::CPR, C::ESZ>(row)) << 4) + 8 * ((d >> 2) & 1);
-            } else {
-                voff[db][hq] = grp * C::ROWB + (32 * db + col) * 4;
-            }
-        }
-    // Loads: this lane's row and swizzled chunk for each 64-lane load it issues.
-    constexpr int LPW = (C::INSTR + C::NW - 1) / C::NW;  // loads per wave per tile (upper bound)
-    uint32_t ld_voff[LPW];
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int inst = wave + j * C::NW;
-        const int slot = inst * 64 + lane;
-        const int row = slot / C::CPR, p = slot % C::CPR;
-        ld_voff[j] = (uint32_t)row * rsb + (uint32_t)((p ^ swz<C::CPR, C::ESZ>(row)) << 4);
-    }
+    C::KVTile::row_offsets(col, grp, koff);
+    C::KVTile::tr_offsets(lane, voff);
+    typename C::Loader ld;
+    ld.init(wave, lane, rsb);
 
     for (;;) {
         __syncthreads();
@@ -251,24 +163,12 @@ __global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
 
         // Stage kt -> (kdst, vdst): K and V rows [kt*KT, kt*KT + KT) of this
         // sequence and head; rows at or past Lk read as zero.
-        auto issue = [&](int kt, char* kdst_g, char* vdst_g) {
+        auto issue = [&](int kt, char* kdst, char* vdst) {
             const int kbase = kt * C::KT;
             const uint32_t nrec =
                 __builtin_amdgcn_readfirstlane((uint32_t)min(max(Lk - kbase, 0), C::KT) * rsb);
-            const __amdgpu_buffer_rsrc_t rk =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(Kseq + (int64_t)kbase * rsb), (short)0, (int)nrec, 0x00020000);
-            const __amdgpu_buffer_rsrc_t rv =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(Vseq + (int64_t)kbase * rsb), (short)0, (int)nrec, 0x00020000);
-            lds_char* kdst = (lds_char*)kdst_g;
-            lds_char* vdst = (lds_char*)vdst_g;
-#pragma unroll
-            for (int j = 0; j < LPW; ++j) {
-                const int inst = wave + j * C::NW;
-                if (C::INSTR % C::NW == 0 || inst < C::INSTR) {
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst + inst * 1024, 16, ld_voff[j], 0, 0, 0);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst + inst * 1024, 16, ld_voff[j], 0, 0, 0);
-                }
-            }
+            ld.issue(Kseq + (int64_t)kbase * rsb, nrec, kdst, wave);
+            ld.issue(Vseq + (int64_t)kbase * rsb, nrec, vdst, wave);
         };
 
         // Consume the stage in (kl, vl) while the next one (if any) streams into
@@ -285,7 +185,7 @@ __global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
                     const char* kblk = kl + (wk * C::NB + nb) * 32 * C::ROWB;
 #pragma unroll
                     for (int s = 0; s < C::NS; ++s)
-                        sacc[nb] = M::run(*(const frag*)(kblk + koff[s]), qf[s], sacc[nb]);
+                        sacc[nb] = M::run(C::KVTile::read_rows(kblk, koff[s]), qf[s], sacc[nb]);
                 }
 
                 const bool need_mask = block_needs_mask(qw0, 32, kw0, 32 * C::NB, Lk, causal, window);
@@ -349,36 +249,15 @@ __global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-                    for (int t = 0; t < C::NT; ++t) {
-                        if constexpr (KP == 8) {
-#pragma unroll
-                            for (int s = 0; s < 8; ++s) pf[nb][t][s] = (bf16)sacc[nb][8 * t + s];
-                        } else {
-                            pf[nb][t] = sacc[nb][t];
-                        }
-                    }
+                    for (int t = 0; t < C::NT; ++t) pf[nb][t] = to_frag<T>(sacc[nb], KP * t);
 #pragma unroll
                 for (int nb = 0; nb < C::NB; ++nb) {
                     const char* vblk = vl + (wk * C::NB + nb) * 32 * C::ROWB;
 #pragma unroll
-                    for (int t = 0; t < C::NT; ++t) {
+                    for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-                        for (int db = 0; db < C::ND; ++db) {
-                            frag af;
-                            if constexpr (KP == 8) {
-                                const char* base = vblk + 16 * t * C::ROWB;
-                                const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                    (__attribute__((address_space(3))) shortx4*)(base + voff[db][0]));
-                                const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                    (__attribute__((address_space(3))) shortx4*)(base + voff[db][1]));
-                                af = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
-                                                             0, 1, 2, 3, 4, 5, 6, 7);
-                            } else {
-                                af = *(const float*)(vblk + 2 * t * C::ROWB + voff[db][0]);
-                            }
-                            oacc[db] = M::run(af, pf[nb][t], oacc[db]);
-                        }
-                    }
+                        for (int db = 0; db < C::ND; ++db)
+                            oacc[db] = M::run(C::KVTile::read_tr(vblk, t, voff, db), pf[nb][t], oacc[db]);
                 }
             }
             __syncthreads();

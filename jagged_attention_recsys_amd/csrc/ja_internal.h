@@ -59,4 +59,34 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, int act, bool split, i
 // Workgroups per CU the forward kernel reaches (from the occupancy query).
 int fwd_blocks_per_cu(int dtype, int d, int act, bool split);
 
+// Softmax backward: dQ pass (query tiles) then dK/dV pass (key tiles).
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;          // forward log-sum-exp, natural log, [Tq, H]
+    void* dq;
+    void* dk;
+    void* dv;
+    float* di;                 // workspace [Tq, H]: rowsum(dO * O), written by the dQ pass
+    const int32_t* q_off;
+    const int32_t* k_off;
+    const int32_t* q_items;    // (sequence, query tile) pairs
+    const int32_t* k_items;    // (sequence, key tile) pairs
+    int32_t* q_counters;
+    int32_t* k_counters;
+    int32_t H;
+    int32_t Tq, Tk;
+    int32_t causal, window;
+    float scale;
+};
+bool bwd_supported(int dtype, int d, int act);
+int bwd_rows_per_item();   // query rows (dQ pass) and key rows (dK/dV pass) per work item
+int bwd_cols_per_stage();  // keys (dQ pass) and queries (dK/dV pass) per stage: scheduler cost unit
+hipError_t launch_bwd(const BwdArgs& a, int d, int grid_q, int grid_k, hipStream_t stream, hipEvent_t before,
+                      hipEvent_t after);
+int bwd_blocks_per_cu(int d);
+
 }  // namespace ja

@@ -1,0 +1,193 @@
+// ja_lds.h -- LDS tiles of token rows and the matrix-operand reads on them.
+//
+// A tile holds ROWS consecutive token rows of one head (K, V, Q or dO), d
+// contiguous, streamed from HBM by buffer loads straight into LDS. Each row's
+// 16-byte chunks are XOR-swizzled (swz) so that the two read patterns the
+// kernels use are free of bank conflicts:
+//   * row-operand reads (A operand "rows x d" of a 32x32x16 product): lane l
+//     reads 8 bf16 of row kappa(l%32) at d-chunk 2s + l/32;
+//   * transpose reads (A operand "d x rows"): ds_read_tr16_b64, each 16-lane
+//     group gathering 4 rows x 16 dims, twice for 8 rows.
+// Rows past the end of the sequence read as zero: the buffer descriptor of a
+// tile ends at the sequence's last row.
+#pragma once
+
+#include "ja_common.h"
+
+namespace ja {
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+    typedef bf16x8 type;
+    static __device__ __forceinline__ type zero() { return type{}; }
+};
+template <> struct Frag<float> {
+    typedef float type;
+    static __device__ __forceinline__ type zero() { return 0.0f; }
+};
+
+// XOR swizzle of the 16-byte chunks of an LDS row (bf16 rows of 4, 8 or 16
+// chunks; fp32 tiles are not swizzled). Within any 16 consecutive rows it maps a
+// fixed chunk to 16 distinct bank groups (row-operand reads), and for 4
+// consecutive rows two adjacent chunks to 8 distinct groups (transpose reads).
+template <int CPR, int ESZ>
+__device__ __forceinline__ int swz(int row) {
+    if (ESZ != 2) return 0;
+    if (CPR == 16) return ((row & 7) << 1) | ((row >> 3) & 1);
+    if (CPR == 8) return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+    return (row >> 2) & 3;
+}
+
+template <typename T, int D, int ROWS>
+struct Tile {
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int KP = Mma<T>::KPACK;
+    static constexpr int ROWB = D * ESZ;           // bytes per row
+    static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+    static constexpr int BYTES = ROWS * ROWB;
+    static constexpr int INSTR = BYTES / 1024;     // 64-lane x 16-byte loads per tile
+    static constexpr int NS = D / (2 * KP);        // k-steps over d
+    static constexpr int ND = D / 32;              // 32-row blocks over d
+    static_assert(BYTES % 1024 == 0, "tile must be whole 64-lane loads");
+
+    // Row-operand offsets of lane (col, grp) inside a 32-row block, per k-step.
+    static __device__ __forceinline__ void row_offsets(int col, int grp, int (&off)[NS]) {
+        const int r = key_of_arow<KP>(col);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if constexpr (KP == 8) {
+                const int c = 2 * s + grp;
+                off[s] = r * ROWB + ((c ^ swz<CPR, ESZ>(r)) << 4);
+            } else {
+                off[s] = r * ROWB + (2 * s + grp) * 4;
+            }
+        }
+    }
+
+    // Transpose-read offsets (bf16) of lane l inside a 16-row step, per 32-dim
+    // block and row quad; fp32 tiles read single elements instead.
+    static __device__ __forceinline__ void tr_offsets(int lane, int (&off)[ND][2]) {
+        const int grp = lane >> 5, col = lane & 31;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int hq = 0; hq < 2; ++hq) {
+                if constexpr (KP == 8) {
+                    const int i = lane & 15, cb = (lane >> 4) & 1;
+                    const int row = 8 * grp + 4 * hq + (i >> 2);
+                    const int d = 32 * db + 16 * cb + 4 * (i & 3);
+                    off[db][hq] = row * ROWB + (((d >> 3) ^ swz<CPR, ESZ>(row)) << 4) + 8 * ((d >> 2) & 1);
+                } else {
+                    off[db][hq] = grp * ROWB + (32 * db + col) * 4;
+                }
+            }
+    }
+
+    // A operand "rows x d" of k-step s for the 32-row block starting at blk.
+    static __device__ __forceinline__ typename Frag<T>::type read_rows(const char* blk, int off) {
+        return *(const typename Frag<T>::type*)(blk + off);
+    }
+
+    // A operand "d x rows" for k-step t over the 32-row block at blk (rows
+    // 16t + 8grp + 0..7 in the key_of_reg order), 32-dim block db.
+    static __device__ __forceinline__ typename Frag<T>::type read_tr(const char* blk, int t, const int (&off)[ND][2],
+                                                                    int db) {
+        if constexpr (KP == 8) {
+            const char* base = blk + 16 * t * ROWB;
+            const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) shortx4*)(base + off[db][0]));
+            const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) shortx4*)(base + off[db][1]));
+            return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1,
+                                           2, 3, 4, 5, 6, 7);
+        } else {
+            return *(const float*)(blk + 2 * t * ROWB + off[db][0]);
+        }
+    }
+};
+
+// Per-lane global byte offsets of the chunks this lane loads for a tile, for
+// each of its (at most LPW) 64-lane loads; load j of wave w is tile load
+// w + j*NW.
+template <typename TileT, int NW>
+struct TileLoader {
+    static constexpr int LPW = (TileT::INSTR + NW - 1) / NW;
+    uint32_t voff[LPW];
+
+    __device__ __forceinline__ void init(int wave, int lane, uint32_t row_stride_bytes) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int slot = (wave + j * NW) * 64 + lane;
+            const int row = slot / TileT::CPR, p = slot % TileT::CPR;
+            voff[j] = (uint32_t)row * row_stride_bytes +
+                      (uint32_t)((p ^ swz<TileT::CPR, TileT::ESZ>(row)) << 4);
+        }
+    }
+
+    // Rows [0, nvalid) of the tile start at `src` (row stride fixed at init);
+    // rows at or past nvalid read as zero.
+    __device__ __forceinline__ void issue(const char* src, uint32_t nrec_bytes, char* dst, int wave) const {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, (int)nrec_bytes, 0x00020000);
+        lds_char* d = (lds_char*)dst;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int inst = wave + j * NW;
+            if (TileT::INSTR % NW == 0 || inst < TileT::INSTR)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d + inst * 1024, 16, voff[j], 0, 0, 0);
+        }
+    }
+};
+
+__device__ __forceinline__ bool visible(int row, int key, int Lk, int causal, int window) {
+    const int diff = row - key;
+    const int adiff = causal ? diff : (diff < 0 ? -diff : diff);
+    return (key < Lk) & (!causal | (key <= row)) & ((window == 0) | (adiff < window));
+}
+
+// Reductions over lanes l and l^32 (the two halves of a C-tile column).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+template <typename T> __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<bf16>(bf16* dst, float a, float b, float c, float d) {
+    bf16x4 v;
+    v[0] = (bf16)a;
+    v[1] = (bf16)b;
+    v[2] = (bf16)c;
+    v[3] = (bf16)d;
+    *(bf16x4*)dst = v;
+}
+template <> __device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
+    floatx4 v;
+    v[0] = a;
+    v[1] = b;
+    v[2] = c;
+    v[3] = d;
+    *(floatx4*)dst = v;
+}
+
+// Convert 8 consecutive fp32 C-registers (r0..r0+7) to a bf16 B-operand fragment
+// (fp32: the single register r0).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type to_frag(const floatx16& c, int r0) {
+    if constexpr (Mma<T>::KPACK == 8) {
+        typename Frag<T>::type f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) f[s] = (bf16)c[r0 + s];
+        return f;
+    } else {
+        return c[r0];
+    }
+}
+
+}  // namespace ja
