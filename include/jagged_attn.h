@@ -91,7 +91,7 @@ size_t ja_fwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_
  *   out [Tq,H,d]: written for every row of every sequence.
  *   lse [Tq,H] fp32: softmax log-sum-exp per row, natural log; may be NULL;
  *   ignored for SiLU/GELU.
- *   workspace: at least ja_fwd_workspace_size() bytes, 256-byte aligned; its
+ *   workspace: at least ja_fwd_workspace_size() bytes, 16-byte aligned; its
  *   contents on entry do not matter and are clobbered. */
 ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v,
                             const int32_t* q_offsets, const int32_t* k_offsets,
