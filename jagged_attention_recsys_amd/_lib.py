@@ -8,7 +8,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjagged_attn.so")
+# The in-tree build; JAGGED_ATTN_LIB may name another build of the same library.
+LIB_PATH = os.environ.get("JAGGED_ATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                             "libjagged_attn.so")
 
 # Symbols declared in include/jagged_attn.h, with their ctypes signatures.
 _i32, _i64, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p

@@ -30,15 +30,19 @@ template <> struct Frag<float> {
 };
 
 // XOR swizzle of the 16-byte chunks of an LDS row (bf16 rows of 4, 8 or 16
-// chunks; fp32 tiles are not swizzled). Within any 16 consecutive rows it maps a
-// fixed chunk to 16 distinct bank groups (row-operand reads), and for 4
-// consecutive rows two adjacent chunks to 8 distinct groups (transpose reads).
+// chunks; fp32 tiles are not swizzled). The LDS serves 64 banks of 4 bytes per
+// cycle: 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read. The swizzle
+// keeps both read patterns free of bank conflicts:
+//   * row-operand reads (16 lanes): 16 rows at one fixed chunk land on 16
+//     distinct 16-byte bank groups;
+//   * transpose reads (32 lanes): 4 consecutive rows (4-aligned) x 4 consecutive
+//     chunks (4-aligned) land on 16 distinct groups.
 template <int CPR, int ESZ>
 __device__ __forceinline__ int swz(int row) {
     if (ESZ != 2) return 0;
-    if (CPR == 16) return ((row & 7) << 1) | ((row >> 3) & 1);
-    if (CPR == 8) return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
-    return (row >> 2) & 3;
+    if (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);        // 256-B rows
+    if (CPR == 8) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);  // 128-B rows, 2 per bank cycle
+    return (row >> 2) & 3;                                            // 64-B rows, 4 per bank cycle
 }
 
 template <typename T, int D, int ROWS>
