@@ -5,7 +5,8 @@ A step is one full ``jagged_attn_fwd`` call (device tile scheduler + fused atten
 kernel) over the whole synthetic batch, inputs already resident in HBM. The default
 workload is the jagged causal softmax self-attention batch (B=64, lengths
 log-uniform in [128, 4096], H=4, d=128, bf16). ``--workload 3|4|5`` measures the
-other named batches; ``--bwd`` adds the softmax backward (workload 5).
+other named batches; ``--bwd`` adds the backward (softmax for 2 and 5, the
+pointwise SiLU / GELU backward for 3 and 4).
 
 Reported:
   value        useful (unpadded) TFLOP/s of the whole step: 4 d H sum_b pairs_b per
@@ -94,7 +95,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
-    ap.add_argument("--bwd", action="store_true", help="time forward + backward (softmax workloads)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time forward + backward (softmax for 2 and 5, SiLU / GELU for 3 and 4)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -126,9 +128,8 @@ def main() -> int:
 
     log(f"[bench] generating workload {args.workload}")
     w = W.workload(args.workload)
-    if args.bwd and w.act != "softmax":
-        print("--bwd supports the softmax workloads (2 and 5)", file=sys.stderr)
-        return 2
+    if args.bwd and w.dout is None:
+        W.with_upstream_gradient(w, 1000 + args.workload)  # seeded dO for the batches that draw none
 
     def up(a):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -138,7 +139,7 @@ def main() -> int:
 
     q, k, v = up(w.q), up(w.k), up(w.v)
     qo, ko = up(w.q_offsets), up(w.k_offsets)
-    dout = up(w.dout) if (args.bwd and w.dout is not None) else (torch.randn_like(q) if args.bwd else None)
+    dout = up(w.dout) if args.bwd else None
     Tq, Tk = q.shape[0], k.shape[0]
     out = torch.empty_like(q)
     lse = torch.empty((Tq, w.H), dtype=torch.float32, device=dev) if w.act == "softmax" else None
@@ -235,6 +236,11 @@ def main() -> int:
     if args.bwd:
         result["bwd"] = {"kernel_ms": round(bwd_kernel_ms, 4),
                          "tflops": round(bwd_flop / (bwd_kernel_ms * 1e-3) / 1e12, 2)}
+        if args.workload in (3, 4):
+            # reading Q, K, V, dO once and writing dQ, dK, dV once
+            min_b = 2 * w.H * w.d * (3 * Tq + 4 * Tk)
+            result["bwd"]["min_hbm_bytes"] = min_b
+            result["bwd"]["hbm_gbs_at_min_bytes"] = round(min_b / (bwd_kernel_ms * 1e-3) / 1e9, 1)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, out, lse, args.cpu_seconds)

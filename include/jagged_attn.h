@@ -104,10 +104,16 @@ ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v,
 size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
                              int32_t act, int32_t causal, int32_t window, int32_t dtype);
 
-/* Backward of the softmax forward (act must be JA_ACT_SOFTMAX, dtype JA_BF16).
- * Needs the forward's out and lse. Computes Di = rowsum(dO * O) inside the dQ
- * pass, writes dq once per row from that pass, then dk and dv once per row from
- * a key-stationary pass; no atomics on any gradient.
+/* Backward of jagged_attn_fwd for dtype JA_BF16 and every act ("Jagged Sequence
+ * Flash Attention" section of the GEM training post: dQ in its own pass, no
+ * atomics; "Generalized Dot-Product Attention (GDPA)" section for SiLU / GELU).
+ * Writes dq once per row from a query-stationary pass, then dk and dv once per
+ * row from a key-stationary pass; no atomics on any gradient.
+ *   act == JA_ACT_SOFTMAX: needs the forward's out and lse (same scale); Di =
+ *     rowsum(dO * O) is computed inside the dQ pass into the workspace.
+ *   act == JA_ACT_SILU / JA_ACT_GELU_TANH: with Z = scale Q K^T, P = act(Z)/Lk
+ *     and dS = act'(Z) * (dO V^T) / Lk; out and lse are not read and may be
+ *     NULL.
  *   dout [Tq,H,d]: upstream gradient; dq [Tq,H,d], dk/dv [Tk,H,d]: outputs,
  *   every row written (rows no query sees get zeros). */
 ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v,

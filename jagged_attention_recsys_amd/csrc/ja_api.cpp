@@ -210,12 +210,14 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const v
     if (!bwd_supported(dtype, d, act)) return JA_ERR_UNSUPPORTED;
     if (B == 0 || (Tq == 0 && Tk == 0)) return JA_OK;
     if (!q_offsets || !k_offsets || !workspace) return JA_ERR_INVALID_ARG;
-    if (Tq > 0 && (!q || !out || !dout || !lse || !dq)) return JA_ERR_INVALID_ARG;
+    const bool softmax = act == JA_ACT_SOFTMAX;  // only softmax reads the forward's out and lse
+    if (Tq > 0 && (!q || !dout || !dq || (softmax && (!out || !lse)))) return JA_ERR_INVALID_ARG;
     if (Tk > 0 && (!k || !v || !dk || !dv)) return JA_ERR_INVALID_ARG;
-    const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv, workspace};
+    const void* ptrs16[] = {q, k, v, softmax ? out : nullptr, dout, dq, dk, dv, workspace};
     for (const void* p16 : ptrs16)
         if (!aligned(p16, 16)) return JA_ERR_INVALID_ARG;
-    if (!aligned(lse, 4) || !aligned(q_offsets, 4) || !aligned(k_offsets, 4)) return JA_ERR_INVALID_ARG;
+    if ((softmax && !aligned(lse, 4)) || !aligned(q_offsets, 4) || !aligned(k_offsets, 4))
+        return JA_ERR_INVALID_ARG;
     BwdPlan p;
     st = plan_bwd(B, H, Tq, Tk, &p);
     if (st != JA_OK) return st;
@@ -252,9 +254,9 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const v
     ba.q = q;
     ba.k = k;
     ba.v = v;
-    ba.out = out;
+    ba.out = softmax ? out : nullptr;
     ba.dout = dout;
-    ba.lse = lse;
+    ba.lse = softmax ? lse : nullptr;
     ba.dq = dq;
     ba.dk = dk;
     ba.dv = dv;
@@ -271,13 +273,13 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const v
     ba.causal = causal ? 1 : 0;
     ba.window = window;
     ba.scale = scale;
-    const int64_t cap = (int64_t)device_cus() * bwd_blocks_per_cu(d);
+    const int64_t cap = (int64_t)device_cus() * bwd_blocks_per_cu(d, act);
     int64_t gq = p.max_q_pairs * H, gk = p.max_k_pairs * H;
     gq = gq < cap ? gq : cap;
     gk = gk < cap ? gk : cap;
     if (gq < 1) gq = 1;
     if (gk < 1) gk = 1;
-    if (launch_bwd(ba, d, (int)gq, (int)gk, s, g_prof_before, g_prof_after) != hipSuccess) return JA_ERR_HIP;
+    if (launch_bwd(ba, d, act, (int)gq, (int)gk, s, g_prof_before, g_prof_after) != hipSuccess) return JA_ERR_HIP;
     return JA_OK;
 }
 

@@ -1,13 +1,18 @@
-// ja_bwd.hip -- softmax jagged attention backward for gfx950, split into a
+// ja_bwd.hip -- jagged attention backward for gfx950, split into a
 // query-stationary dQ pass and a key-stationary dK/dV pass ("Jagged Sequence
 // Flash Attention" section of the GEM training post: dQ in its own pass, no
 // atomic accumulation of any gradient, no recomputation shared across passes).
 //
-// With P = exp(scale Q K^T - lse) (the forward's log-sum-exp per row):
+// Softmax, with P = exp(scale Q K^T - lse) (the forward's log-sum-exp per row):
 //   Di  = sum_c dO_ic O_ic                       (dQ pass prologue, to workspace)
 //   dP  = dO V^T,  dS = P o (dP - Di)
 //   dQ  = scale dS K                             (dQ pass, written once)
 //   dV  = P^T dO,  dK = scale dS^T Q             (dK/dV pass, written once)
+//
+// Pointwise SiLU / tanh-GELU ("Generalized Dot-Product Attention (GDPA)"
+// section: the activation replaces softmax, output normalised by 1/Lk), with
+// Z = scale Q K^T: P = act(Z) / Lk and dS = act'(Z) o dP / Lk, then the same
+// three products. There is no lse, no Di and no forward output to read.
 //
 // dQ pass: 4 waves, a 128-row query tile, wave w owns 32 rows. For each 64-key
 // stage (K and V streamed into LDS as in the forward): S^T = K Q^T and
@@ -48,7 +53,7 @@ struct BwdCfg {
 };
 
 // dQ pass ---------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int ACT>
 __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = BwdCfg<T, D>;
@@ -98,7 +103,8 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dq_kernel(BwdArgs a) {
         const bool row_ok = my_row < Lq;
         const int64_t qrow = (qo + my_row) * rs + (int64_t)h * D + KP * grp;
 
-        // Q^T and dO^T as B operands; Di from O and dO in the same layout.
+        // Q^T and dO^T as B operands; for softmax Di from O and dO in the same
+        // layout.
         frag qf[C::NS], dof[C::NS];
         float di = 0.0f;
         {
@@ -109,18 +115,24 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dq_kernel(BwdArgs a) {
             for (int s = 0; s < C::NS; ++s) {
                 qf[s] = row_ok ? *(const frag*)(qs + 2 * KP * s) : Frag<T>::zero();
                 dof[s] = row_ok ? *(const frag*)(ds + 2 * KP * s) : Frag<T>::zero();
-                const frag of = row_ok ? *(const frag*)(os + 2 * KP * s) : Frag<T>::zero();
-                if constexpr (KP == 8) {
+                if constexpr (ACT == ACT_SOFTMAX) {
+                    const frag of = row_ok ? *(const frag*)(os + 2 * KP * s) : Frag<T>::zero();
+                    if constexpr (KP == 8) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) di = fmaf((float)dof[s][e], (float)of[e], di);
-                } else {
-                    di = fmaf(dof[s], of, di);
+                        for (int e = 0; e < 8; ++e) di = fmaf((float)dof[s][e], (float)of[e], di);
+                    } else {
+                        di = fmaf(dof[s], of, di);
+                    }
                 }
             }
         }
-        di = halves_sum(di);
-        const float nlse2 = row_ok ? -a.lse[(qo + my_row) * a.H + h] * kLog2e : 0.0f;
-        if (row_ok && grp == 0) a.di[(qo + my_row) * a.H + h] = di;
+        float nlse2 = 0.0f;
+        if constexpr (ACT == ACT_SOFTMAX) {
+            di = halves_sum(di);
+            nlse2 = row_ok ? -a.lse[(qo + my_row) * a.H + h] * kLog2e : 0.0f;
+            if (row_ok && grp == 0) a.di[(qo + my_row) * a.H + h] = di;
+        }
+        const float inv_lk = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
 
         floatx16 dqacc[C::ND];
 #pragma unroll
@@ -155,12 +167,19 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dq_kernel(BwdArgs a) {
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float p = fast_exp2(fmaf(sacc[r], c_exp, nlse2));
+                        float g;
+                        if constexpr (ACT == ACT_SOFTMAX) {
+                            g = fast_exp2(fmaf(sacc[r], c_exp, nlse2)) * (dpacc[r] - di);
+                        } else {
+                            float act, dact;
+                            pointwise_grad<ACT>(sacc[r] * a.scale, act, dact);
+                            g = dact * dpacc[r] * inv_lk;
+                        }
                         if (need_mask) {
                             const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
-                            p = visible(my_row, key, Lk, causal, window) ? p : 0.0f;
+                            g = visible(my_row, key, Lk, causal, window) ? g : 0.0f;
                         }
-                        sacc[r] = p * (dpacc[r] - di);
+                        sacc[r] = g;
                     }
 #pragma unroll
                     for (int t = 0; t < C::NT; ++t) dsf[nb][t] = to_frag<T>(sacc, KP * t);
@@ -204,7 +223,7 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dq_kernel(BwdArgs a) {
 }
 
 // dK/dV pass -------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int ACT>
 __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = BwdCfg<T, D>;
@@ -259,6 +278,7 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
         const bool key_ok = my_key < Lk;
         const int64_t krow = (ko + my_key) * rs + (int64_t)h * D + KP * grp;
 
+        const float inv_lk = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
         frag kf[C::NS], vf[C::NS];
         {
             const T* ks = (const T*)a.k + krow;
@@ -287,7 +307,7 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
             ld.issue(Qseq + (int64_t)qbase * rsb, nrec, qdst, wave);
             ld.issue(Oseq + (int64_t)qbase * rsb, nrec, odst, wave);
             // lse and Di of the stage's queries: one 64-lane dword load each.
-            if (wave < 2) {
+            if (ACT == ACT_SOFTMAX && wave < 2) {
                 const uint32_t nrec_s = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * hsb);
                 const char* src = (wave == 0 ? Lseq : Dseq) + (int64_t)qbase * hsb;
                 const __amdgpu_buffer_rsrc_t r =
@@ -322,7 +342,7 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
                 // of 8 consecutive queries, read as float4s from lse / Di.
                 float lse_r[16], di_r[16];
 #pragma unroll
-                for (int r = 0; r < 16; r += 4) {
+                for (int r = 0; r < 16 && ACT == ACT_SOFTMAX; r += 4) {
                     const int ql_ = nb * 32 + key_of_reg<KP>(grp, r);
                     if constexpr (KP == 8) {
                         const floatx4 l4 = *(const floatx4*)(ll + ql_);
@@ -344,13 +364,24 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
                 floatx16 dsacc;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(sacc[r], c_exp, -lse_r[r] * kLog2e));
+                    float p, g;
+                    if constexpr (ACT == ACT_SOFTMAX) {
+                        p = fast_exp2(fmaf(sacc[r], c_exp, -lse_r[r] * kLog2e));
+                        g = p * (dpacc[r] - di_r[r]);
+                    } else {
+                        float act, dact;
+                        pointwise_grad<ACT>(sacc[r] * a.scale, act, dact);
+                        p = act * inv_lk;
+                        g = dact * dpacc[r] * inv_lk;
+                    }
                     if (need_mask) {
                         const int q = qb0 + key_of_reg<KP>(grp, r);
-                        p = (q < Lq && visible(q, my_key, Lk, causal, window)) ? p : 0.0f;
+                        const bool ok = q < Lq && visible(q, my_key, Lk, causal, window);
+                        p = ok ? p : 0.0f;
+                        g = ok ? g : 0.0f;
                     }
                     sacc[r] = p;
-                    dsacc[r] = p * (dpacc[r] - di_r[r]);
+                    dsacc[r] = g;
                 }
 #pragma unroll
                 for (int t = 0; t < C::NT; ++t) {
@@ -396,27 +427,27 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
 #endif
 }
 
-template <int D>
+template <int D, int ACT>
 hipError_t launch_d(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hipEvent_t before, hipEvent_t after) {
     if (before && hipEventRecord(before, s) != hipSuccess) return hipErrorUnknown;
-    hipLaunchKernelGGL((ja_bwd_dq_kernel<bf16, D>), dim3(grid_q), dim3(kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((ja_bwd_dq_kernel<bf16, D, ACT>), dim3(grid_q), dim3(kBwdThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ja_bwd_dkdv_kernel<bf16, D>), dim3(grid_k), dim3(kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((ja_bwd_dkdv_kernel<bf16, D, ACT>), dim3(grid_k), dim3(kBwdThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (after && hipEventRecord(after, s) != hipSuccess) return hipErrorUnknown;
     return hipSuccess;
 }
 
-template <int D>
+template <int D, int ACT>
 int occupancy_d() {
     int n1 = 0, n2 = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n1, reinterpret_cast<const void*>(&ja_bwd_dq_kernel<bf16, D>), kBwdThreads, 0) != hipSuccess)
+            &n1, reinterpret_cast<const void*>(&ja_bwd_dq_kernel<bf16, D, ACT>), kBwdThreads, 0) != hipSuccess)
         n1 = 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n2, reinterpret_cast<const void*>(&ja_bwd_dkdv_kernel<bf16, D>), kBwdThreads, 0) != hipSuccess)
+            &n2, reinterpret_cast<const void*>(&ja_bwd_dkdv_kernel<bf16, D, ACT>), kBwdThreads, 0) != hipSuccess)
         n2 = 1;
     return (n1 < n2 ? n1 : n2) > 0 ? (n1 < n2 ? n1 : n2) : 1;
 }
@@ -424,27 +455,48 @@ int occupancy_d() {
 }  // namespace
 
 bool bwd_supported(int dtype, int d, int act) {
-    return dtype == 1 && (d == 32 || d == 64 || d == 128) && act == ACT_SOFTMAX;
+    return dtype == 1 && (d == 32 || d == 64 || d == 128) && act >= ACT_SOFTMAX && act <= ACT_GELU;
 }
 
 int bwd_rows_per_item() { return kBwdRows; }
 int bwd_cols_per_stage() { return kBwdStage; }
 
-hipError_t launch_bwd(const BwdArgs& a, int d, int grid_q, int grid_k, hipStream_t stream, hipEvent_t before,
-                      hipEvent_t after) {
+template <int ACT>
+hipError_t launch_a(const BwdArgs& a, int d, int grid_q, int grid_k, hipStream_t stream, hipEvent_t before,
+                    hipEvent_t after) {
     switch (d) {
-        case 32: return launch_d<32>(a, grid_q, grid_k, stream, before, after);
-        case 64: return launch_d<64>(a, grid_q, grid_k, stream, before, after);
-        case 128: return launch_d<128>(a, grid_q, grid_k, stream, before, after);
+        case 32: return launch_d<32, ACT>(a, grid_q, grid_k, stream, before, after);
+        case 64: return launch_d<64, ACT>(a, grid_q, grid_k, stream, before, after);
+        case 128: return launch_d<128, ACT>(a, grid_q, grid_k, stream, before, after);
         default: return hipErrorInvalidValue;
     }
 }
 
-int bwd_blocks_per_cu(int d) {
+template <int ACT>
+int occupancy_a(int d) {
     switch (d) {
-        case 32: return occupancy_d<32>();
-        case 64: return occupancy_d<64>();
-        case 128: return occupancy_d<128>();
+        case 32: return occupancy_d<32, ACT>();
+        case 64: return occupancy_d<64, ACT>();
+        case 128: return occupancy_d<128, ACT>();
+        default: return 1;
+    }
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, hipStream_t stream,
+                      hipEvent_t before, hipEvent_t after) {
+    switch (act) {
+        case ACT_SOFTMAX: return launch_a<ACT_SOFTMAX>(a, d, grid_q, grid_k, stream, before, after);
+        case ACT_SILU: return launch_a<ACT_SILU>(a, d, grid_q, grid_k, stream, before, after);
+        case ACT_GELU: return launch_a<ACT_GELU>(a, d, grid_q, grid_k, stream, before, after);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int bwd_blocks_per_cu(int d, int act) {
+    switch (act) {
+        case ACT_SOFTMAX: return occupancy_a<ACT_SOFTMAX>(d);
+        case ACT_SILU: return occupancy_a<ACT_SILU>(d);
+        case ACT_GELU: return occupancy_a<ACT_GELU>(d);
         default: return 1;
     }
 }

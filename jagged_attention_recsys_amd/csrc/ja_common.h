@@ -87,6 +87,28 @@ __device__ __forceinline__ float pointwise(float x) {
     return x * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
 }
 
+// Activation and its derivative for the backward. Both activations have the form
+// act(x) = x s(w(x)) with s the logistic function: w = x for SiLU, and for the
+// tanh GELU w = 2 sqrt(2/pi) (x + 0.044715 x^3), because (1 + tanh(u)) / 2 =
+// s(2u). Then act'(x) = s (1 + x (1 - s) w'(x)). For large |x| s saturates to
+// exactly 0 or 1 and both results stay finite.
+template <int ACT>
+__device__ __forceinline__ void pointwise_grad(float x, float& a, float& da) {
+    float w, dw;
+    if (ACT == ACT_SILU) {
+        w = x;
+        dw = 1.0f;
+    } else {
+        const float c2 = 1.5957691216057308f;  // 2 * sqrt(2/pi)
+        const float x2 = x * x;
+        w = c2 * fmaf(0.044715f * x, x2, x);
+        dw = c2 * fmaf(3.0f * 0.044715f, x2, 1.0f);
+    }
+    const float sg = fast_rcp(1.0f + fast_exp2(-w * kLog2e));
+    a = x * sg;
+    da = sg * fmaf(x * (1.0f - sg), dw, 1.0f);
+}
+
 // Block-uniform scalar broadcast helpers.
 __device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

@@ -99,13 +99,20 @@ def bwd_workspace_size(B, H, d, Tq, Tk, act="softmax", causal=False, window=0, d
 
 def jagged_attn_bwd(q, k, v, out, dout, lse, q_offsets, k_offsets, act="softmax", causal=False, window=0,
                     scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward of the softmax forward. Returns (dq, dk, dv)."""
+    """Backward of jagged_attn_fwd. Returns (dq, dk, dv).
+
+    Softmax needs the forward's ``out`` and ``lse``; SiLU / GELU read neither
+    (pass None)."""
     lib = _lib.load()
     _check_tensor("q", q, dim=3)
     dtype = q.dtype
-    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
         _check_tensor(name, t, dtype, 3)
-    _check_tensor("lse", lse, torch.float32, 2)
+    # None passes through as a null pointer: the library rejects it for softmax.
+    if out is not None:
+        _check_tensor("out", out, dtype, 3)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, 2)
     Tq, H, d = q.shape
     Tk = k.shape[0]
     B = q_offsets.numel() - 1

@@ -126,6 +126,13 @@ def make_case(lq, lk=None, H=1, d=32, dtype=BF16, seed=0, act="softmax", causal=
     return _build(rng, name, lq_arr, lk_arr, H, d, dtype, act, causal, window, with_dout, shared_q_rows)
 
 
+def with_upstream_gradient(w: Workload, seed: int) -> Workload:
+    """Give ``w`` a seeded upstream gradient dO of the queries' shape (the named
+    workloads other than 5 draw none)."""
+    w.dout = _normal(np.random.default_rng(seed), int(w.q.shape[0]), w.H, w.d, w.dtype)
+    return w
+
+
 def _build(rng, name, lq, lk, H, d, dtype, act, causal, window, with_dout, shared_q_rows):
     qo, ko = offsets_from_lengths(lq), offsets_from_lengths(lk)
     Tq, Tk = int(qo[-1]), int(ko[-1])

@@ -10,6 +10,9 @@ Tolerances:
     bound. The relative term is the arithmetic's own floor: P is rounded to bf16 before
     the second product and the output is rounded to bf16, each within 2^-9 relative, so
     an output of magnitude 6 already carries up to 0.023 of rounding.
+  * bounded bf16 (the pointwise backward, whose gradients are unnormalised sums
+    over up to Lq terms): |x - y| <= 2^-8 (sum |term| + |y|) + 2e-3 elementwise, the
+    rounding bound of compare_bounded, and the same mean bound.
 """
 from __future__ import annotations
 
@@ -77,6 +80,32 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.nda
         stats["excess"] = excess
         assert excess <= BF16_MAX, f"{what}: |err| - 2^-8|ref| reaches {excess:.4e} > {BF16_MAX} ({stats})"
         assert stats["mean_abs"] <= BF16_MEAN, f"{what}: mean abs error {stats['mean_abs']:.4e} > {BF16_MEAN}"
+    return stats
+
+
+def compare_bounded(got: np.ndarray, ref: np.ndarray, terms: np.ndarray, what: str,
+                    sel: np.ndarray | None = None) -> dict:
+    """bf16 check against a per-element rounding bound.
+
+    For an output that is a sum of products whose one factor was rounded to bf16
+    (within 2^-9 relative) and which is itself rounded to bf16, the error is at
+    most 2^-9 (sum |term| + |result|) plus fp32 accumulation noise. `terms` holds
+    sum |term| per element (fp64); the assertion allows twice the bound plus
+    2e-3, and the usual mean bound.
+    """
+    if sel is not None:
+        got, ref, terms = got[sel], ref[sel], terms[sel]
+    got, ref, terms = got.reshape(-1), ref.reshape(-1), terms.reshape(-1)
+    if got.size == 0:
+        return {"n": 0}
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values in the HIP output"
+    err = np.abs(got - ref)
+    allowed = BF16_REL * (terms + np.abs(ref)) + 2e-3
+    ratio = float(np.max(err / allowed))
+    stats = {"n": int(got.size), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+             "max_ref": float(np.abs(ref).max()), "max_err_over_bound": ratio}
+    assert ratio <= 1.0, f"{what}: error exceeds the rounding bound ({stats})"
+    assert stats["mean_abs"] <= BF16_MEAN, f"{what}: mean abs error {stats['mean_abs']:.4e} > {BF16_MEAN}"
     return stats
 
 
