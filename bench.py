@@ -39,8 +39,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "ja_fwd_kernel": ["ja_fwd.hip", "ja_common.h", "ja_tiles.h", "ja_internal.h"],
-    "ja_bwd_kernels": ["ja_bwd.hip", "ja_common.h", "ja_tiles.h", "ja_internal.h"],
+    "ja_fwd_kernel": ["ja_fwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
+    "ja_bwd_kernels": ["ja_bwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
 }
 METRIC = "useful (unpadded) bf16 TFLOP/s of jagged attn fwd; % of MI355X MFMA peak"
 
@@ -102,9 +102,14 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy (y = x * 1) of MIB MiB, 5 times: the reference "
                          "for scaling HBM byte counters")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --workload (and of "
+                         "--copy-calibration 1024) into HBM bytes per forward launch in profiles/traffic.json")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
+    if args.record_traffic:
+        return record_traffic(args.workload, *args.record_traffic)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -247,6 +252,59 @@ def main() -> int:
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def _counter_per_dispatch(run_dir: str, counter: str, kernel_part: str) -> list[float]:
+    """Counter values (summed over the rows of each dispatch) of the dispatches whose
+    kernel name contains kernel_part, from a rocprofv3 --output-format csv run."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel_part in r["Kernel_Name"]:
+                key = (f, r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def record_traffic(workload: int, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> int:
+    """HBM bytes per forward launch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled so that the copy kernel of known size reads and writes exactly its bytes."""
+    copy_bytes = 1024 * (1 << 20)
+    cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "elementwise")
+    cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "elementwise")
+    kf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "ja_fwd_kernel")
+    kw = _counter_per_dispatch(write_dir, "WRITE_SIZE", "ja_fwd_kernel")
+    if not (cf and cw and kf and kw):
+        raise SystemExit("missing dispatches in the counter runs")
+    f_scale = copy_bytes / (float(np.median(cf)) * 1024.0)
+    w_scale = copy_bytes / (float(np.median(cw)) * 1024.0)
+    fetch = float(np.median(kf)) * 1024.0 * f_scale
+    write = float(np.median(kw)) * 1024.0 * w_scale
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        data = {}
+    name = "ja_fwd_kernel"
+    data.setdefault(name, {})[f"w{workload}"] = {
+        "hbm_bytes_per_launch": round(fetch + write),
+        "fetch_bytes": round(fetch), "write_bytes": round(write),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "source_sha256": kernel_sha(name),
+        "method": "rocprofv3 --pmc FETCH_SIZE then --pmc WRITE_SIZE on bench.py --workload "
+                  f"{workload} --steps 2 --warmup 1 --no-cpu-baseline; KiB per dispatch (median) x 1024 x "
+                  "scale, scale = 1 GiB / the same counter on bench.py --copy-calibration 1024",
+    }
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(data[name][f"w{workload}"]))
     return 0
 
 
