@@ -31,8 +31,12 @@ def _hipcc() -> str:
 
 
 def common_flags() -> list[str]:
+    # The atomic optimizer would wrap the forward's single-lane work-queue pop in
+    # wave-wide bookkeeping that waits for the atomic's return on the spot; the pop
+    # is issued before an item's epilogue and its result is read after it.
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-I", INCLUDE, "-I", CSRC]
 
 

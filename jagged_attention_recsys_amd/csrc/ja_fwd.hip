@@ -124,11 +124,19 @@ __global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
     typename C::Loader ld;
     ld.init(wave, lane, rsb);
 
+    // The next item is popped before the current item's output stores, and the
+    // barriers between items only publish LDS: the atomic's return does not queue
+    // behind the stores, and the stores drain while the next item starts.
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    int next = 0;
+    if (tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
     for (;;) {
-        __syncthreads();
-        if (tid == 0) s_item = atomicAdd(&a.counters[kCtrPop], 1);
-        __syncthreads();
+        if (tid == 0) s_item = next;
+        lds_barrier();
         const int idx = __builtin_amdgcn_readfirstlane(s_item);  // same for every lane
+        lds_barrier();  // s_item is read by every wave before it is rewritten
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
         const int b = a.items[2 * pair], qt = a.items[2 * pair + 1];
@@ -271,6 +279,8 @@ __global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
             stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
             if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
         }
+
+        if (tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
 
         // Split layout: merge the key slices (the loop ended on a barrier, or no
         // stage was loaded, so the stage buffers are free). Softmax first agrees on
