@@ -21,6 +21,10 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+// Batches of up to kLdsSeqs sequences keep the per-sequence tile prefix and the
+// offsets in LDS, so the per-tile binary search and length lookups do not wait
+// on global memory; larger batches read them from the workspace and the inputs.
+constexpr int kLdsSeqs = 2048;
 
 // Inclusive scan of one int per thread over the whole workgroup. `tmp` holds
 // kWaves+1 ints of LDS. Returns the inclusive prefix; *total gets the sum.
@@ -64,7 +68,11 @@ __device__ int find_seq(const int32_t* tbase, int B, int f) {
 __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
     __shared__ int cnt[kWaves * kSchedBins];  // [wave][bin] counts, then offsets
     __shared__ int tmp[kWaves + 1];
+    __shared__ int32_t s_tbase[kLdsSeqs + 1];
+    __shared__ int32_t s_row[kLdsSeqs + 1];
+    __shared__ int32_t s_col[kLdsSeqs + 1];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool in_lds = a.B <= kLdsSeqs;
 
     // Phase 0: row tiles per sequence and their exclusive prefix (tbase[0..B]).
     int carry = 0;
@@ -77,9 +85,19 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
         }
         int total;
         int incl = block_scan(n, tmp, &total);
-        if (b <= a.B) a.tbase[b] = carry + incl - n;
+        if (b <= a.B) {
+            a.tbase[b] = carry + incl - n;
+            if (in_lds) {
+                s_tbase[b] = carry + incl - n;
+                s_row[b] = a.row_off[b];
+                s_col[b] = a.col_off[b];
+            }
+        }
         carry += total;
     }
+    const int32_t* tb = in_lds ? s_tbase : a.tbase;
+    const int32_t* ro = in_lds ? s_row : a.row_off;
+    const int32_t* co = in_lds ? s_col : a.col_off;
     // An enumeration larger than the item buffer (offsets inconsistent with the
     // sizes the host was given) schedules nothing rather than writing past it.
     const int F = (int64_t)carry <= a.max_pairs ? carry : 0;
@@ -92,10 +110,10 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
     const int f_hi = (int)(((int64_t)F * (w + 1)) / kWaves);
 
     auto bin_of = [&](int f, int* pb, int* pt) {
-        const int b = find_seq(a.tbase, a.B, f);
-        const int t = f - a.tbase[b];
-        const int64_t Lr = (int64_t)a.row_off[b + 1] - a.row_off[b];
-        const int64_t Lc = (int64_t)a.col_off[b + 1] - a.col_off[b];
+        const int b = find_seq(tb, a.B, f);
+        const int t = f - tb[b];
+        const int64_t Lr = (int64_t)ro[b + 1] - ro[b];
+        const int64_t Lc = (int64_t)co[b + 1] - co[b];
         const ColRange cr = visible_cols(Lr, Lc, (int64_t)t * a.bm, a.bm, a.causal, a.window, a.transposed);
         const int cost = tile_cost(cr, a.bn);
         *pb = b;

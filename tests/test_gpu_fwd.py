@@ -212,6 +212,22 @@ def test_schedule_small_cases_with_cap():
         assert np.array_equal(items, ref)
 
 
+@pytest.mark.parametrize("B", [2048, 2049, 5000])
+def test_schedule_many_sequences(B):
+    # Up to 2048 sequences the scheduler keeps its per-sequence tables in LDS;
+    # beyond that it reads them from global memory. Both orders must match.
+    rng = np.random.default_rng(B)
+    lq = rng.integers(0, 700, size=B)
+    lk = rng.integers(0, 700, size=B)
+    qo, ko = W.offsets_from_lengths(lq), W.offsets_from_lengths(lk)
+    Tq, Tk = int(qo[-1]), int(ko[-1])
+    for causal, window in [(True, 0), (False, 90)]:
+        items = ja.fwd_schedule(to_dev(qo), to_dev(ko), 2, 64, Tq, Tk, "softmax", causal, window).cpu().numpy()
+        bm, bn = ja.fwd_tile_shape(B, 64, Tq, "softmax")
+        ref, _ = oracle.tile_list(qo, ko, bm, bn, causal, window, cap=511)
+        assert np.array_equal(items, ref)
+
+
 def test_validate_offsets():
     good = torch.tensor([0, 3, 3, 10], dtype=torch.int32, device="cuda")
     assert ja.validate_offsets(good, 10)
