@@ -10,8 +10,9 @@
 //
 // Work decomposition. A persistent grid pops (sequence, query-tile, head) items,
 // longest first, from the list ja_sched.hip built on the device.
-//   * Standard layout: 8 waves, a 256-row query tile; wave w owns rows
-//     [32w, 32w+32) and all waves share each 64-key stage in LDS.
+//   * Standard layout: 4 waves, a 128-row query tile; wave w owns rows
+//     [32w, 32w+32) and all waves share each 64-key stage in LDS. Two such
+//     workgroups run on each CU, independently.
 //   * Split layout (short queries, e.g. pooled attention with 32 seeds): the item
 //     is a 32-row query tile; the waves split each stage's keys and merge their
 //     partial results through LDS at the end.
@@ -51,8 +52,12 @@ namespace {
 
 template <typename T, int D, bool SPLIT>
 struct FwdCfg {
-    static constexpr int NW = SPLIT ? (D == 128 ? 4 : 8) : 8;  // waves per workgroup
+    static constexpr int NW = SPLIT ? (D == 128 ? 4 : 8) : 4;  // waves per workgroup
     static constexpr int THREADS = 64 * NW;
+    // Standard layout: two independent workgroups share each CU (64 KB of LDS and
+    // at most 256 VGPRs each), so one's barriers and idle waves do not hold the
+    // other's matrix work.
+    static constexpr int MIN_BLOCKS = SPLIT ? 1 : 2;
     static constexpr int WQ = SPLIT ? 1 : NW;                 // query slices
     static constexpr int WK = NW / WQ;                        // key slices
     static constexpr int NB = SPLIT ? 1 : 2;                  // 32-key blocks per wave per stage
@@ -76,8 +81,9 @@ struct FwdCfg {
     static_assert(D % (2 * KP) == 0 && D % 32 == 0, "unsupported head dim");
 };
 
-template <typename T, int D, int ACT, bool SPLIT, int NTHREADS = FwdCfg<T, D, SPLIT>::THREADS>
-__global__ __launch_bounds__(NTHREADS) void ja_fwd_kernel(FwdArgs a) {
+template <typename T, int D, int ACT, bool SPLIT, int NTHREADS = FwdCfg<T, D, SPLIT>::THREADS,
+          int MINB = FwdCfg<T, D, SPLIT>::MIN_BLOCKS>
+__global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
     // The body uses gfx950-only types and builtins; the host pass only needs the
     // kernel's signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)

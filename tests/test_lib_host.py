@@ -90,9 +90,9 @@ def test_workspace_size_grows_with_tiles(lib):
 
 def test_tile_shape_query(lib):
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
-    # standard layout: 8 waves x 32 query rows, 64-key stages
+    # standard layout: 4 waves x 32 query rows, 64-key stages
     assert lib.ja_fwd_tile_shape(64, 128, 70000, 0, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
-    assert (bm.value, bn.value) == (256, 64)
+    assert (bm.value, bn.value) == (128, 64)
     # short queries (mean <= 48 rows) use the split layout: one 32-row tile, the
     # waves splitting each key stage (8 x 32 keys for d <= 64, 4 x 32 for d = 128)
     assert lib.ja_fwd_tile_shape(256, 64, 256 * 32, 2, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
@@ -101,7 +101,7 @@ def test_tile_shape_query(lib):
     assert (bm.value, bn.value) == (32, 128)
     # fp32 never splits
     assert lib.ja_fwd_tile_shape(4, 32, 233, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == OK
-    assert (bm.value, bn.value) == (256, 64)
+    assert (bm.value, bn.value) == (128, 64)
     assert lib.ja_fwd_tile_shape(4, 40, 233, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == UNSUPPORTED
 
 
