@@ -273,10 +273,11 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const v
     ba.causal = causal ? 1 : 0;
     ba.window = window;
     ba.scale = scale;
-    const int64_t cap = (int64_t)device_cus() * bwd_blocks_per_cu(d, act);
+    const int64_t cap_q = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, false);
+    const int64_t cap_k = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, true);
     int64_t gq = p.max_q_pairs * H, gk = p.max_k_pairs * H;
-    gq = gq < cap ? gq : cap;
-    gk = gk < cap ? gk : cap;
+    gq = gq < cap_q ? gq : cap_q;
+    gk = gk < cap_k ? gk : cap_k;
     if (gq < 1) gq = 1;
     if (gk < 1) gk = 1;
     if (launch_bwd(ba, d, act, (int)gq, (int)gk, s, g_prof_before, g_prof_after) != hipSuccess) return JA_ERR_HIP;

@@ -53,8 +53,10 @@ struct BwdCfg {
 };
 
 // dQ pass ---------------------------------------------------------------------
+// The dQ pass fits in 256 VGPRs, so two of its workgroups share a CU; the dK/dV
+// pass holds two accumulators per row and runs one workgroup per CU.
 template <typename T, int D, int ACT>
-__global__ __launch_bounds__(kBwdThreads) void ja_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = BwdCfg<T, D>;
     using M = Mma<T>;
@@ -441,15 +443,12 @@ hipError_t launch_d(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hip
 }
 
 template <int D, int ACT>
-int occupancy_d() {
-    int n1 = 0, n2 = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n1, reinterpret_cast<const void*>(&ja_bwd_dq_kernel<bf16, D, ACT>), kBwdThreads, 0) != hipSuccess)
-        n1 = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n2, reinterpret_cast<const void*>(&ja_bwd_dkdv_kernel<bf16, D, ACT>), kBwdThreads, 0) != hipSuccess)
-        n2 = 1;
-    return (n1 < n2 ? n1 : n2) > 0 ? (n1 < n2 ? n1 : n2) : 1;
+int occupancy_d(bool dkdv) {
+    int n = 0;
+    const void* fn = dkdv ? reinterpret_cast<const void*>(&ja_bwd_dkdv_kernel<bf16, D, ACT>)
+                          : reinterpret_cast<const void*>(&ja_bwd_dq_kernel<bf16, D, ACT>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBwdThreads, 0) != hipSuccess) n = 1;
+    return n > 0 ? n : 1;
 }
 
 }  // namespace
@@ -473,11 +472,11 @@ hipError_t launch_a(const BwdArgs& a, int d, int grid_q, int grid_k, hipStream_t
 }
 
 template <int ACT>
-int occupancy_a(int d) {
+int occupancy_a(int d, bool dkdv) {
     switch (d) {
-        case 32: return occupancy_d<32, ACT>();
-        case 64: return occupancy_d<64, ACT>();
-        case 128: return occupancy_d<128, ACT>();
+        case 32: return occupancy_d<32, ACT>(dkdv);
+        case 64: return occupancy_d<64, ACT>(dkdv);
+        case 128: return occupancy_d<128, ACT>(dkdv);
         default: return 1;
     }
 }
@@ -492,11 +491,11 @@ hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, 
     }
 }
 
-int bwd_blocks_per_cu(int d, int act) {
+int bwd_blocks_per_cu(int d, int act, bool dkdv) {
     switch (act) {
-        case ACT_SOFTMAX: return occupancy_a<ACT_SOFTMAX>(d);
-        case ACT_SILU: return occupancy_a<ACT_SILU>(d);
-        case ACT_GELU: return occupancy_a<ACT_GELU>(d);
+        case ACT_SOFTMAX: return occupancy_a<ACT_SOFTMAX>(d, dkdv);
+        case ACT_SILU: return occupancy_a<ACT_SILU>(d, dkdv);
+        case ACT_GELU: return occupancy_a<ACT_GELU>(d, dkdv);
         default: return 1;
     }
 }

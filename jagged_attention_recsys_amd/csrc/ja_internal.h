@@ -87,6 +87,6 @@ int bwd_rows_per_item();   // query rows (dQ pass) and key rows (dK/dV pass) per
 int bwd_cols_per_stage();  // keys (dQ pass) and queries (dK/dV pass) per stage: scheduler cost unit
 hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, hipStream_t stream,
                       hipEvent_t before, hipEvent_t after);
-int bwd_blocks_per_cu(int d, int act);
+int bwd_blocks_per_cu(int d, int act, bool dkdv);  // workgroups per CU of the dQ (false) or dK/dV pass
 
 }  // namespace ja
