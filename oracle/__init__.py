@@ -52,16 +52,16 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         vp, i32p, u8p, f64p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
         i32, f64, i64 = ctypes.c_int32, ctypes.c_double, ctypes.c_int64
-        lib.ora_fwd.argtypes = [vp, vp, vp, ctypes.c_int, i32p, i32p, i32, i32, i32,
-                                ctypes.c_int, ctypes.c_int, i32, f64, u8p, f64p, f64p, ctypes.c_int]
-        lib.ora_fwd.restype = ctypes.c_int
-        lib.ora_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i32p, i32p, i32, i32, i32,
-                                ctypes.c_int, ctypes.c_int, i32, f64, u8p, f64p, f64p,
-                                f64p, f64p, f64p, ctypes.c_int]
-        lib.ora_bwd.restype = ctypes.c_int
-        lib.ora_tile_list.argtypes = [i32p, i32p, i32, i32, i32, ctypes.c_int, i32,
-                                      ctypes.c_int, i32, i32p, i32p, i64]
-        lib.ora_tile_list.restype = ctypes.c_int64
+        lib.ora_fwd_block.argtypes = [vp, vp, vp, ctypes.c_int, i32p, i32p, i32, i32, i32,
+                                      ctypes.c_int, ctypes.c_int, i32, i32, f64, u8p, f64p, f64p, ctypes.c_int]
+        lib.ora_fwd_block.restype = ctypes.c_int
+        lib.ora_bwd_block.argtypes = [vp, vp, vp, vp, ctypes.c_int, i32p, i32p, i32, i32, i32,
+                                      ctypes.c_int, ctypes.c_int, i32, i32, f64, u8p, f64p, f64p,
+                                      f64p, f64p, f64p, ctypes.c_int]
+        lib.ora_bwd_block.restype = ctypes.c_int
+        lib.ora_tile_list_block.argtypes = [i32p, i32p, i32, i32, i32, ctypes.c_int, i32, i32,
+                                            ctypes.c_int, i32, i32p, i32p, i64]
+        lib.ora_tile_list_block.restype = ctypes.c_int64
         lib.ora_num_threads.argtypes = []
         lib.ora_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -93,11 +93,13 @@ def _offsets(off) -> np.ndarray:
 
 
 def fwd(q, k, v, q_offsets, k_offsets, act="softmax", causal=False, window=0, scale=None,
-        pair_mask=None, nthreads=0):
+        pair_mask=None, nthreads=0, block=0):
     """Forward oracle. q: [Tq,H,d]; k, v: [Tk,H,d] (float32, float64 or bf16 bits as uint16).
 
-    Returns (out [Tq,H,d] float64, lse [Tq,H] float64). Rows of pairs not selected by
-    ``pair_mask`` ([B,H] bool) are NaN.
+    ``block`` > 0 adds the block-diagonal mask (query i sees key j only if both lie
+    in the same ``block``-token block of their sequence). Returns (out [Tq,H,d]
+    float64, lse [Tq,H] float64). Rows of pairs not selected by ``pair_mask``
+    ([B,H] bool) are NaN.
     """
     lib = _load()
     q, dt = _as_input(q)
@@ -113,16 +115,16 @@ def fwd(q, k, v, q_offsets, k_offsets, act="softmax", causal=False, window=0, sc
     out = np.full((Tq, H, d), np.nan, dtype=np.float64)
     lse = np.full((Tq, H), np.nan, dtype=np.float64)
     pm = None if pair_mask is None else np.ascontiguousarray(np.asarray(pair_mask, dtype=np.uint8).reshape(-1))
-    rc = lib.ora_fwd(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(qo), _ptr(ko), B, H, d,
-                     ACTS[act] if isinstance(act, str) else int(act), int(bool(causal)), int(window),
-                     float(scale), _ptr(pm), _ptr(out), _ptr(lse), int(nthreads))
+    rc = lib.ora_fwd_block(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(qo), _ptr(ko), B, H, d,
+                           ACTS[act] if isinstance(act, str) else int(act), int(bool(causal)), int(window),
+                           int(block), float(scale), _ptr(pm), _ptr(out), _ptr(lse), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out, lse
 
 
 def bwd(q, k, v, dout, q_offsets, k_offsets, act="softmax", causal=False, window=0, scale=None,
-        pair_mask=None, nthreads=0):
+        pair_mask=None, nthreads=0, block=0):
     """Backward oracle. Returns (out, lse, dq, dk, dv) as float64 arrays (NaN outside pair_mask)."""
     lib = _load()
     q, dt = _as_input(q)
@@ -143,16 +145,17 @@ def bwd(q, k, v, dout, q_offsets, k_offsets, act="softmax", causal=False, window
     dk = np.full((Tk, H, d), np.nan)
     dv = np.full((Tk, H, d), np.nan)
     pm = None if pair_mask is None else np.ascontiguousarray(np.asarray(pair_mask, dtype=np.uint8).reshape(-1))
-    rc = lib.ora_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), dt, _ptr(qo), _ptr(ko), B, H, d,
-                     ACTS[act] if isinstance(act, str) else int(act), int(bool(causal)), int(window),
-                     float(scale), _ptr(pm), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                     int(nthreads))
+    rc = lib.ora_bwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), dt, _ptr(qo), _ptr(ko), B, H, d,
+                           ACTS[act] if isinstance(act, str) else int(act), int(bool(causal)), int(window),
+                           int(block), float(scale), _ptr(pm), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk),
+                           _ptr(dv), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out, lse, dq, dk, dv
 
 
-def tile_list(row_offsets, col_offsets, BM, BN, causal=False, window=0, transposed=False, cap=1 << 30):
+def tile_list(row_offsets, col_offsets, BM, BN, causal=False, window=0, transposed=False, cap=1 << 30,
+              block=0):
     """Reference work list: (items [n,2] int32 of (b, tile), costs [n] int32), sorted by
     min(cost, cap) descending, then b, then tile ascending."""
     lib = _load()
@@ -162,8 +165,8 @@ def tile_list(row_offsets, col_offsets, BM, BN, causal=False, window=0, transpos
     nmax = int(np.sum((L + BM - 1) // BM)) if B > 0 else 0
     items = np.zeros((max(nmax, 1), 2), dtype=np.int32)
     costs = np.zeros(max(nmax, 1), dtype=np.int32)
-    n = lib.ora_tile_list(_ptr(ro), _ptr(co), B, int(BM), int(BN), int(bool(causal)), int(window),
-                          int(bool(transposed)), int(cap), _ptr(items), _ptr(costs), nmax)
+    n = lib.ora_tile_list_block(_ptr(ro), _ptr(co), B, int(BM), int(BN), int(bool(causal)), int(window),
+                                int(block), int(bool(transposed)), int(cap), _ptr(items), _ptr(costs), nmax)
     if n < 0:
         raise ValueError("oracle rejected the arguments")
     return items[:n].copy(), costs[:n].copy()

@@ -62,10 +62,14 @@ static double act_deriv(int act, double x) {
 
 /* ---- visibility ----------------------------------------------------------
  * Query i sees key j (both local to their sequence) iff j < Lk, and
- * causal => j <= i, and window W > 0 => (causal ? i - j < W : |i - j| < W). */
-static int visible(int64_t i, int64_t j, int64_t Lk, int causal, int32_t window) {
+ * causal => j <= i, and window W > 0 => (causal ? i - j < W : |i - j| < W),
+ * and block size G > 0 => i and j lie in the same G-token block of the
+ * sequence (floor(i / G) == floor(j / G)): "BlockAttention" section, each
+ * query block attends only to its own key/value block. */
+static int visible(int64_t i, int64_t j, int64_t Lk, int causal, int32_t window, int32_t block) {
     if (j < 0 || j >= Lk) return 0;
     if (causal && j > i) return 0;
+    if (block > 0 && i / block != j / block) return 0;
     if (window > 0) {
         int64_t diff = i - j;
         if (!causal && diff < 0) diff = -diff;
@@ -83,6 +87,7 @@ typedef struct {
     int32_t B, H, d;
     int act, causal;
     int32_t window;
+    int32_t block;
     double scale;
     const uint8_t* pair_mask;
     double *out, *lse, *dq, *dk, *dv;
@@ -116,7 +121,7 @@ static void fwd_rows(job_t* J, int32_t b, int32_t h, int64_t i0, int64_t i1) {
             double m = -INFINITY;
             int64_t n = 0;
             for (int64_t j = 0; j < Lk; ++j) {
-                if (!visible(i, j, Lk, J->causal, J->window)) continue;
+                if (!visible(i, j, Lk, J->causal, J->window, J->block)) continue;
                 s[j] = score(J, qo + i, ko + j, (int32_t)h);
                 if (s[j] > m) m = s[j];
                 ++n;
@@ -126,9 +131,9 @@ static void fwd_rows(job_t* J, int32_t b, int32_t h, int64_t i0, int64_t i1) {
             } else {
                 double l = 0.0;
                 for (int64_t j = 0; j < Lk; ++j)
-                    if (visible(i, j, Lk, J->causal, J->window)) l += exp(s[j] - m);
+                    if (visible(i, j, Lk, J->causal, J->window, J->block)) l += exp(s[j] - m);
                 for (int64_t j = 0; j < Lk; ++j) {
-                    if (!visible(i, j, Lk, J->causal, J->window)) continue;
+                    if (!visible(i, j, Lk, J->causal, J->window, J->block)) continue;
                     double p = exp(s[j] - m);
                     for (int64_t c = 0; c < d; ++c)
                         o[c] += p * elem(J->v, J->dtype, ((ko + j) * H + h) * d + c);
@@ -138,7 +143,7 @@ static void fwd_rows(job_t* J, int32_t b, int32_t h, int64_t i0, int64_t i1) {
             }
         } else {
             for (int64_t j = 0; j < Lk; ++j) {
-                if (!visible(i, j, Lk, J->causal, J->window)) continue;
+                if (!visible(i, j, Lk, J->causal, J->window, J->block)) continue;
                 double a = act_apply(J->act, score(J, qo + i, ko + j, (int32_t)h));
                 for (int64_t c = 0; c < d; ++c)
                     o[c] += a * elem(J->v, J->dtype, ((ko + j) * H + h) * d + c);
@@ -175,13 +180,13 @@ static void bwd_pair(job_t* J, int32_t b, int32_t h) {
         if (J->lse) { lse_local[i] = J->lse[(qo + i) * H + h]; continue; }
         double m = -INFINITY;
         for (int64_t j = 0; j < Lk; ++j)
-            if (visible(i, j, Lk, J->causal, J->window)) {
+            if (visible(i, j, Lk, J->causal, J->window, J->block)) {
                 double sj = score(J, qo + i, ko + j, (int32_t)h);
                 if (sj > m) m = sj;
             }
         double l = 0.0;
         for (int64_t j = 0; j < Lk; ++j)
-            if (visible(i, j, Lk, J->causal, J->window))
+            if (visible(i, j, Lk, J->causal, J->window, J->block))
                 l += exp(score(J, qo + i, ko + j, (int32_t)h) - m);
         lse_local[i] = (m == -INFINITY) ? -INFINITY : m + log(l);
     }
@@ -198,7 +203,7 @@ static void bwd_pair(job_t* J, int32_t b, int32_t h) {
         if (J->act == ORA_SOFTMAX)
             for (int64_t c = 0; c < d; ++c) Di += elem(J->dout, J->dtype, qi + c) * J->out[qi + c];
         for (int64_t j = 0; j < Lk; ++j) {
-            if (!visible(i, j, Lk, J->causal, J->window)) continue;
+            if (!visible(i, j, Lk, J->causal, J->window, J->block)) continue;
             const int64_t kj = ((ko + j) * H + h) * d;
             double sij = score(J, qo + i, ko + j, (int32_t)h);
             double p, dsfac;
@@ -305,19 +310,47 @@ static int check_common(const int32_t* q_off, const int32_t* k_off, int32_t B, i
     return 0;
 }
 
-int ora_fwd(const void* q, const void* k, const void* v, int dtype,
-            const int32_t* q_off, const int32_t* k_off,
-            int32_t B, int32_t H, int32_t d,
-            int act, int causal, int32_t window, double scale,
-            const uint8_t* pair_mask, double* out, double* lse, int nthreads) {
-    if (check_common(q_off, k_off, B, H, d, act, window) || !out) return -1;
+int ora_fwd_block(const void* q, const void* k, const void* v, int dtype,
+                  const int32_t* q_off, const int32_t* k_off,
+                  int32_t B, int32_t H, int32_t d,
+                  int act, int causal, int32_t window, int32_t block, double scale,
+                  const uint8_t* pair_mask, double* out, double* lse, int nthreads) {
+    if (check_common(q_off, k_off, B, H, d, act, window) || !out || block < 0) return -1;
     if (dtype != ORA_F32 && dtype != ORA_BF16 && dtype != ORA_F64) return -1;
     job_t J;
     memset(&J, 0, sizeof J);
     J.q = q; J.k = k; J.v = v; J.dtype = dtype;
     J.q_off = q_off; J.k_off = k_off; J.B = B; J.H = H; J.d = d;
-    J.act = act; J.causal = causal != 0; J.window = window; J.scale = scale;
+    J.act = act; J.causal = causal != 0; J.window = window; J.block = block; J.scale = scale;
     J.pair_mask = pair_mask; J.out = out; J.lse = lse;
+    return run(&J, nthreads);
+}
+
+int ora_fwd(const void* q, const void* k, const void* v, int dtype,
+            const int32_t* q_off, const int32_t* k_off,
+            int32_t B, int32_t H, int32_t d,
+            int act, int causal, int32_t window, double scale,
+            const uint8_t* pair_mask, double* out, double* lse, int nthreads) {
+    return ora_fwd_block(q, k, v, dtype, q_off, k_off, B, H, d, act, causal, window, 0, scale,
+                         pair_mask, out, lse, nthreads);
+}
+
+int ora_bwd_block(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                  const int32_t* q_off, const int32_t* k_off,
+                  int32_t B, int32_t H, int32_t d,
+                  int act, int causal, int32_t window, int32_t block, double scale,
+                  const uint8_t* pair_mask, double* out, double* lse,
+                  double* dq, double* dk, double* dv, int nthreads) {
+    if (check_common(q_off, k_off, B, H, d, act, window) || block < 0) return -1;
+    if (!out || !dq || !dk || !dv || !dout) return -1;
+    if (dtype != ORA_F32 && dtype != ORA_BF16 && dtype != ORA_F64) return -1;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dout = dout; J.dtype = dtype;
+    J.q_off = q_off; J.k_off = k_off; J.B = B; J.H = H; J.d = d;
+    J.act = act; J.causal = causal != 0; J.window = window; J.block = block; J.scale = scale;
+    J.pair_mask = pair_mask; J.out = out; J.lse = lse;
+    J.dq = dq; J.dk = dk; J.dv = dv;
     return run(&J, nthreads);
 }
 
@@ -327,17 +360,8 @@ int ora_bwd(const void* q, const void* k, const void* v, const void* dout, int d
             int act, int causal, int32_t window, double scale,
             const uint8_t* pair_mask, double* out, double* lse,
             double* dq, double* dk, double* dv, int nthreads) {
-    if (check_common(q_off, k_off, B, H, d, act, window)) return -1;
-    if (!out || !dq || !dk || !dv || !dout) return -1;
-    if (dtype != ORA_F32 && dtype != ORA_BF16 && dtype != ORA_F64) return -1;
-    job_t J;
-    memset(&J, 0, sizeof J);
-    J.q = q; J.k = k; J.v = v; J.dout = dout; J.dtype = dtype;
-    J.q_off = q_off; J.k_off = k_off; J.B = B; J.H = H; J.d = d;
-    J.act = act; J.causal = causal != 0; J.window = window; J.scale = scale;
-    J.pair_mask = pair_mask; J.out = out; J.lse = lse;
-    J.dq = dq; J.dk = dk; J.dv = dv;
-    return run(&J, nthreads);
+    return ora_bwd_block(q, k, v, dout, dtype, q_off, k_off, B, H, d, act, causal, window, 0, scale,
+                         pair_mask, out, lse, dq, dk, dv, nthreads);
 }
 
 /* ---- reference work list ---------------------------------------------- */
@@ -353,11 +377,11 @@ static int item_cmp(const void* pa, const void* pb) {
     return 0;
 }
 
-int64_t ora_tile_list(const int32_t* row_off, const int32_t* col_off, int32_t B,
-                      int32_t BM, int32_t BN, int causal, int32_t window,
-                      int transposed, int32_t cap,
-                      int32_t* items, int32_t* costs, int64_t max_items) {
-    if (!row_off || !col_off || B < 0 || BM < 1 || BN < 1 || window < 0 || cap < 1) return -1;
+int64_t ora_tile_list_block(const int32_t* row_off, const int32_t* col_off, int32_t B,
+                            int32_t BM, int32_t BN, int causal, int32_t window, int32_t block,
+                            int transposed, int32_t cap,
+                            int32_t* items, int32_t* costs, int64_t max_items) {
+    if (!row_off || !col_off || B < 0 || BM < 1 || BN < 1 || window < 0 || block < 0 || cap < 1) return -1;
     int64_t n = 0;
     for (int32_t b = 0; b < B; ++b) {
         int64_t L = row_off[b + 1] - row_off[b];
@@ -379,8 +403,8 @@ int64_t ora_tile_list(const int32_t* row_off, const int32_t* col_off, int32_t B,
                 for (int64_t r = r0; r < r1 && !any; ++r) {
                     /* not transposed: rows are queries i, columns keys j;
                      * transposed: rows are keys j, columns queries i. */
-                    any = transposed ? visible(c, r, Lr, causal, window)
-                                     : visible(r, c, Lc, causal, window);
+                    any = transposed ? visible(c, r, Lr, causal, window, block)
+                                     : visible(r, c, Lc, causal, window, block);
                 }
                 if (any) {
                     if (lo < 0) lo = c;
@@ -404,4 +428,12 @@ int64_t ora_tile_list(const int32_t* row_off, const int32_t* col_off, int32_t B,
     }
     free(it);
     return m;
+}
+
+int64_t ora_tile_list(const int32_t* row_off, const int32_t* col_off, int32_t B,
+                      int32_t BM, int32_t BN, int causal, int32_t window,
+                      int transposed, int32_t cap,
+                      int32_t* items, int32_t* costs, int64_t max_items) {
+    return ora_tile_list_block(row_off, col_off, B, BM, BN, causal, window, 0, transposed, cap,
+                               items, costs, max_items);
 }

@@ -87,6 +87,26 @@ int64_t ora_tile_list(const int32_t* row_off, const int32_t* col_off, int32_t B,
 /* Number of online cores the oracle uses when nthreads <= 0. */
 int ora_num_threads(void);
 
+/* The same three functions with a block-diagonal mask ("BlockAttention"
+ * section: fixed token blocks, each query block attending only to its own
+ * key/value block): block G > 0 additionally requires floor(i/G) == floor(j/G)
+ * for query i to see key j (local indices); G == 0 is the functions above. */
+int ora_fwd_block(const void* q, const void* k, const void* v, int dtype,
+                  const int32_t* q_off, const int32_t* k_off,
+                  int32_t B, int32_t H, int32_t d,
+                  int act, int causal, int32_t window, int32_t block, double scale,
+                  const uint8_t* pair_mask, double* out, double* lse, int nthreads);
+int ora_bwd_block(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                  const int32_t* q_off, const int32_t* k_off,
+                  int32_t B, int32_t H, int32_t d,
+                  int act, int causal, int32_t window, int32_t block, double scale,
+                  const uint8_t* pair_mask, double* out, double* lse,
+                  double* dq, double* dk, double* dv, int nthreads);
+int64_t ora_tile_list_block(const int32_t* row_off, const int32_t* col_off, int32_t B,
+                            int32_t BM, int32_t BN, int causal, int32_t window, int32_t block,
+                            int transposed, int32_t cap,
+                            int32_t* items, int32_t* costs, int64_t max_items);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,9 +28,10 @@ from jagged_attention_recsys_amd import workloads as W
 # independent dense references (torch float64, padded)
 # --------------------------------------------------------------------------
 
-def _visible_mask(Lq, Lk, causal, window):
+def _visible_mask(Lq, Lk, causal, window, block=0):
     """Boolean [Lq, Lk] visibility, written from the reading: causal means j <= i
-    (top-left aligned); a window W keeps W keys including the query's own position."""
+    (top-left aligned); a window W keeps W keys including the query's own position;
+    a block size G keeps keys of the query's own G-token block."""
     i = torch.arange(Lq).view(-1, 1)
     j = torch.arange(Lk).view(1, -1)
     m = torch.ones(Lq, Lk, dtype=torch.bool)
@@ -39,6 +40,8 @@ def _visible_mask(Lq, Lk, causal, window):
     if window > 0:
         diff = (i - j) if causal else (i - j).abs()
         m &= diff < window
+    if block > 0:
+        m &= torch.div(i, block, rounding_mode="floor") == torch.div(j, block, rounding_mode="floor")
     return m
 
 
@@ -48,7 +51,7 @@ def _to_f64(x):
     return torch.from_numpy(np.asarray(x, dtype=np.float64))
 
 
-def dense_reference(w: W.Workload, act="softmax", causal=False, window=0, need_grad=False, dout=None):
+def dense_reference(w: W.Workload, act="softmax", causal=False, window=0, need_grad=False, dout=None, block=0):
     """Per-sequence padded dense attention with torch library calls. Returns out, lse
     and (optionally) gradients of sum(dout * out) w.r.t. q, k, v."""
     q, k, v = _to_f64(w.q), _to_f64(w.k), _to_f64(w.v)
@@ -64,7 +67,7 @@ def dense_reference(w: W.Workload, act="softmax", causal=False, window=0, need_g
         qb = q[qo:q1].permute(1, 0, 2)  # [H, Lq, d]
         kb = k[ko:k1].permute(1, 0, 2)
         vb = v[ko:k1].permute(1, 0, 2)
-        mask = _visible_mask(Lq, Lk, causal, window)  # [Lq, Lk]
+        mask = _visible_mask(Lq, Lk, causal, window, block)  # [Lq, Lk]
         has = mask.any(dim=1) if Lk > 0 else torch.zeros(Lq, dtype=torch.bool)
         if Lq == 0:
             ob = qb * 0.0
@@ -379,16 +382,16 @@ def test_backward_identical_keys_closed_form():
 # work list
 # --------------------------------------------------------------------------
 
-def _brute_items(row_off, col_off, BM, BN, causal, window, transposed):
+def _brute_items(row_off, col_off, BM, BN, causal, window, transposed, block=0):
     items = []
     for b in range(len(row_off) - 1):
         Lr, Lc = row_off[b + 1] - row_off[b], col_off[b + 1] - col_off[b]
         for t in range((Lr + BM - 1) // BM):
             rows = np.arange(t * BM, min(Lr, t * BM + BM))
             if transposed:  # rows are keys, columns are queries
-                m = _visible_mask(Lc, Lr, causal, window).numpy()[:, rows].T
+                m = _visible_mask(Lc, Lr, causal, window, block).numpy()[:, rows].T
             else:
-                m = _visible_mask(len(rows) + rows[0], Lc, causal, window).numpy()[rows]
+                m = _visible_mask(len(rows) + rows[0], Lc, causal, window, block).numpy()[rows]
             cols = np.nonzero(m.any(axis=0))[0] if m.size else np.array([], dtype=np.int64)
             tiles = set((cols // BN).tolist())
             items.append((b, t, len(tiles)))
@@ -409,6 +412,17 @@ def test_tile_list_matches_brute_force(causal, window, transposed):
     assert sorted((int(b), int(t), int(c)) for (b, t), c in zip(items, costs)) == sorted(brute)
     keys = [(-c, b, t) for (b, t), c in zip(items.tolist(), costs.tolist())]
     assert keys == sorted(keys)
+
+
+@pytest.mark.parametrize("causal,transposed", [(False, False), (True, False), (True, True), (False, True)])
+def test_tile_list_block_matches_brute_force(causal, transposed):
+    rng = np.random.default_rng(41 + causal + 2 * transposed)
+    lr = rng.integers(0, 70, size=9)
+    ro = W.offsets_from_lengths(lr)
+    BM, BN, G = 8, 4, 12
+    items, costs = oracle.tile_list(ro, ro, BM, BN, causal, 0, transposed, block=G)
+    brute = _brute_items(ro, ro, BM, BN, causal, 0, transposed, block=G)
+    assert sorted((int(b), int(t), int(c)) for (b, t), c in zip(items, costs)) == sorted(brute)
 
 
 def test_tile_list_cap_orders_by_capped_cost():
@@ -442,3 +456,54 @@ def test_workload_shapes():
     assert w3.B == 128 and np.all(w3.lk == 64) and w3.lq.min() >= 512 and w3.lq.max() <= 8192
     w5 = W.workload(5)
     assert w5.B == 32 and w5.lq.max() <= 32768 and w5.dout is not None and w5.window == 1024
+
+
+# --------------------------------------------------------------------------
+# block-diagonal attention ("BlockAttention" section)
+# --------------------------------------------------------------------------
+
+def _resplit(lengths, G):
+    """Lengths of the same rows cut into consecutive G-token pieces per sequence."""
+    out = []
+    for L in lengths:
+        L = int(L)
+        out += [G] * (L // G) + ([L % G] if L % G else [])
+    return np.array(out, dtype=np.int64)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("G", [8, 64])
+def test_block_attention_is_attention_on_resplit_sequences(causal, G):
+    # Each G-token block attends only to itself, so block attention over a batch is
+    # plain attention over the batch cut into G-token sequences (same rows, same
+    # key order): forward and backward must agree exactly.
+    lengths = [0, 1, G - 1, G, G + 1, 3 * G + 5, 2 * G]
+    w = W.make_case(lengths, H=2, d=16, dtype=W.F64, seed=70 + G + causal, with_dout=True)
+    rs = W.offsets_from_lengths(_resplit(lengths, G))
+    o1, l1 = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, "softmax", causal, 0, block=G)
+    o2, l2 = oracle.fwd(w.q, w.k, w.v, rs, rs, "softmax", causal, 0)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    g1 = oracle.bwd(w.q, w.k, w.v, w.dout, w.q_offsets, w.k_offsets, "softmax", causal, 0, block=G)
+    g2 = oracle.bwd(w.q, w.k, w.v, w.dout, rs, rs, "softmax", causal, 0)
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_attention_against_sdpa(causal):
+    w = W.make_case([0, 1, 30, 64, 65, 150, 200], H=2, d=32, dtype=W.F64, seed=81 + causal)
+    out, lse = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, "softmax", causal, 0, block=64)
+    ref = dense_reference(w, "softmax", causal, 0, block=64)
+    assert _relerr(out, ref["out"]) < 1e-12
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.max(np.abs(lse[fin] - ref["lse"][fin])) < 1e-12
+
+
+def test_block_attention_gradients_against_autograd():
+    w = W.make_case([5, 64, 100, 130], H=2, d=16, dtype=W.F64, seed=83, with_dout=True)
+    _, _, dq, dk, dv = oracle.bwd(w.q, w.k, w.v, w.dout, w.q_offsets, w.k_offsets, "softmax", True, 0,
+                                  block=64)
+    ref = dense_reference(w, "softmax", True, 0, need_grad=True, dout=w.dout, block=64)
+    for got, want in ((dq, ref["dq"]), (dk, ref["dk"]), (dv, ref["dv"])):
+        assert _relerr(got, want) < 1e-10
