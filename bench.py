@@ -4,9 +4,10 @@
 A step is one full ``jagged_attn_fwd`` call (device tile scheduler + fused attention
 kernel) over the whole synthetic batch, inputs already resident in HBM. The default
 workload is the jagged causal softmax self-attention batch (B=64, lengths
-log-uniform in [128, 4096], H=4, d=128, bf16). ``--workload 3|4|5`` measures the
-other named batches; ``--bwd`` adds the backward (softmax for 2 and 5, the
-pointwise SiLU / GELU backward for 3 and 4).
+log-uniform in [128, 4096], H=4, d=128, bf16). ``--workload 3|4|5|6`` measures the
+other named batches (6: 64-token block-diagonal attention through
+``jagged_block_attn_fwd``); ``--bwd`` adds the backward (softmax for 2, 5 and 6,
+the pointwise SiLU / GELU backward for 3 and 4).
 
 Reported:
   value        useful (unpadded) TFLOP/s of the whole step: 4 d H sum_b pairs_b per
@@ -49,11 +50,16 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def visible_pairs(lq: np.ndarray, lk: np.ndarray, causal: bool, window: int) -> int:
-    """Exact number of visible (query, key) pairs of a jagged batch."""
+def visible_pairs(lq: np.ndarray, lk: np.ndarray, causal: bool, window: int, block: int = 0) -> int:
+    """Exact number of visible (query, key) pairs of a jagged batch (block > 0: the
+    block-diagonal self-attention mask, blocks of `block` tokens)."""
     total = 0
     for Lq, Lk in zip(lq.tolist(), lk.tolist()):
         if Lq <= 0 or Lk <= 0:
+            continue
+        if block > 0:  # self-attention: full blocks plus one short last block
+            sizes = [block] * (Lq // block) + ([Lq % block] if Lq % block else [])
+            total += sum(g * (g + 1) // 2 if causal else g * g for g in sizes)
             continue
         if not causal and window == 0:
             total += Lq * Lk
@@ -94,9 +100,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
     ap.add_argument("--bwd", action="store_true",
-                    help="time forward + backward (softmax for 2 and 5, SiLU / GELU for 3 and 4)")
+                    help="time forward + backward (softmax for 2, 5 and 6, SiLU / GELU for 3 and 4)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -156,20 +162,28 @@ def main() -> int:
                           dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    pairs = visible_pairs(w.lq, w.lk, w.causal, w.window)
+    pairs = visible_pairs(w.lq, w.lk, w.causal, w.window, w.block)
     fwd_flop = 4.0 * w.d * w.H * pairs
     bwd_flop = 10.0 * w.d * w.H * pairs if args.bwd else 0.0
 
     def step(ev=None):
         if ev is not None:
             lib.ja_set_profile_events(ev[0].cuda_event, ev[1].cuda_event)
-        ja.jagged_attn_fwd(q, k, v, qo, ko, act=w.act, causal=w.causal, window=w.window, scale=w.scale,
-                           out=out, lse=lse, workspace=ws, stream=stream)
+        if w.block:
+            ja.jagged_block_attn_fwd(q, k, v, qo, w.block, causal=w.causal, scale=w.scale, out=out, lse=lse,
+                                     workspace=ws, stream=stream)
+        else:
+            ja.jagged_attn_fwd(q, k, v, qo, ko, act=w.act, causal=w.causal, window=w.window, scale=w.scale,
+                               out=out, lse=lse, workspace=ws, stream=stream)
         if args.bwd:
             if ev is not None:
                 lib.ja_set_profile_events(ev[2].cuda_event, ev[3].cuda_event)
-            ja.jagged_attn_bwd(q, k, v, out, dout, lse, qo, ko, act=w.act, causal=w.causal, window=w.window,
-                               scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws, stream=stream)
+            if w.block:
+                ja.jagged_block_attn_bwd(q, k, v, out, dout, lse, qo, w.block, causal=w.causal, scale=w.scale,
+                                         dq=dq, dk=dk, dv=dv, workspace=bws, stream=stream)
+            else:
+                ja.jagged_attn_bwd(q, k, v, out, dout, lse, qo, ko, act=w.act, causal=w.causal, window=w.window,
+                                   scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws, stream=stream)
         if ev is not None:
             lib.ja_set_profile_events(None, None)
 
@@ -208,11 +222,12 @@ def main() -> int:
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(name, f"w{args.workload}"),
                 "kernel": name, "kernel_ms": round(fwd_kernel_ms, 4),
                 "flop_per_launch": fwd_flop}
-    if args.workload in (3, 4):
-        # short key/value (3) and short query (4) batches are HBM-bound: their
-        # minimum traffic is reading Q, K, V once and writing O once.
+    if args.workload in (3, 4, 6):
+        # short key/value (3), short query (4) and 64-token block (6) batches are
+        # HBM-bound: their minimum traffic is reading Q, K, V once and writing O
+        # (and, for softmax, the fp32 lse) once.
         esz = 2
-        min_bytes = esz * w.H * w.d * (2 * Tq + 2 * Tk)
+        min_bytes = esz * w.H * w.d * (2 * Tq + 2 * Tk) + (4 * w.H * Tq if w.act == "softmax" else 0)
         roofline["min_hbm_bytes"] = min_bytes
         roofline["hbm_gbs_at_min_bytes"] = round(min_bytes / (fwd_kernel_ms * 1e-3) / 1e9, 1)
         roofline["hbm_frac"] = round(roofline["hbm_gbs_at_min_bytes"] / PEAK_HBM_GBS, 4)
@@ -233,7 +248,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.extra.get("description", w.name), "B": w.B, "H": w.H, "d": w.d,
-                   "act": w.act, "causal": bool(w.causal), "window": int(w.window), "q_tokens": int(Tq),
+                   "act": w.act, "causal": bool(w.causal), "window": int(w.window), "block": int(w.block),
+                   "q_tokens": int(Tq),
                    "kv_tokens": int(Tk), "visible_pairs": int(pairs), "fwd_flop": fwd_flop,
                    "bwd_flop": bwd_flop, "phases": "fwd+bwd" if args.bwd else "fwd"},
         "roofline": roofline,
@@ -241,9 +257,12 @@ def main() -> int:
     if args.bwd:
         result["bwd"] = {"kernel_ms": round(bwd_kernel_ms, 4),
                          "tflops": round(bwd_flop / (bwd_kernel_ms * 1e-3) / 1e12, 2)}
-        if args.workload in (3, 4):
-            # reading Q, K, V, dO once and writing dQ, dK, dV once
+        if args.workload in (3, 4, 6):
+            # reading Q, K, V, dO once and writing dQ, dK, dV once (softmax: also
+            # reading O and lse)
             min_b = 2 * w.H * w.d * (3 * Tq + 4 * Tk)
+            if w.act == "softmax":
+                min_b += 2 * w.H * w.d * Tq + 4 * w.H * Tq
             result["bwd"]["min_hbm_bytes"] = min_b
             result["bwd"]["hbm_gbs_at_min_bytes"] = round(min_b / (bwd_kernel_ms * 1e-3) / 1e9, 1)
 
@@ -330,7 +349,7 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
     rng = np.random.default_rng(1234)
     B, H = w.B, w.H
     order = [(int(b), int(h)) for b in rng.permutation(B) for h in range(H)]
-    pair_flop = np.array([4.0 * w.d * visible_pairs(w.lq[b:b + 1], w.lk[b:b + 1], w.causal, w.window)
+    pair_flop = np.array([4.0 * w.d * visible_pairs(w.lq[b:b + 1], w.lk[b:b + 1], w.causal, w.window, w.block)
                           for b, _ in order])
     # Calibrate the oracle's rate on a growing prefix of the pair order (at least
     # ~1 s of work), then fill the budget.
@@ -341,7 +360,8 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
         for b, h in order[:n_cal]:
             mask[b, h] = True
         t = time.perf_counter()
-        oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale, pair_mask=mask)
+        oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale, pair_mask=mask,
+                   block=w.block)
         dt = time.perf_counter() - t
         if dt >= 1.0 or n_cal >= len(order):
             rate = max(pair_flop[:n_cal].sum(), 1.0) / max(dt, 1e-4)
@@ -357,7 +377,7 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
     log(f"[bench] cpu baseline: {int(mask.sum())} pairs, {acc:.3g} flop")
     t = time.perf_counter()
     ref, ref_lse = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale,
-                              pair_mask=mask)
+                              pair_mask=mask, block=w.block)
     dt = time.perf_counter() - t
     # parity spot-check of the GPU output on the same pairs
     got = out_gpu.float().cpu().numpy().astype(np.float64)

@@ -16,7 +16,9 @@
  *     pooled multi-head attention (short queries, long keys/values); valid tiles
  *     are enumerated by a software tile scheduler and empty tiles skipped;
  *   - "BlockAttention" section: sliding-window attention that limits each token
- *     to nearby events and skips tiles outside the window.
+ *     to nearby events and skips tiles outside the window, and its block-diagonal
+ *     form (jagged_block_attn_fwd / _bwd) where fixed token blocks attend only
+ *     within themselves.
  *
  * Conventions this library fixes where the post is silent:
  *   - SiLU(x) = x * sigmoid(x); GELU is the tanh form
@@ -123,6 +125,36 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v,
                             int32_t act, int32_t causal, int32_t window, float scale,
                             int32_t dtype, void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Block-diagonal self-attention ("BlockAttention" section of the GEM training
+ * post: the sequence is cut into fixed blocks of tokens and each query block
+ * attends only to the keys and values of its own block, so tiles outside the
+ * blocks on the diagonal are never scheduled). Softmax only; one offsets array
+ * serves queries, keys and values (self-attention, Tq = Tk = T).
+ *   block: tokens per block, a power of two >= 1; query i (local index) sees key
+ *   j iff i / block == j / block (integer division), and with causal also j <= i.
+ *   Blocks restart at every sequence start; the last block of a sequence may be
+ *   shorter than `block`.
+ * Everything else (layout, scale, lse, alignment, ownership, errors) is as for
+ * jagged_attn_fwd with act = JA_ACT_SOFTMAX, window = 0, and its workspace is
+ * ja_fwd_workspace_size(B, H, d, T, T, JA_ACT_SOFTMAX, causal, 0, dtype) bytes.
+ * A block that is not a power of two returns JA_ERR_INVALID_ARG. */
+ja_status_t jagged_block_attn_fwd(const void* q, const void* k, const void* v,
+                                  const int32_t* offsets, int32_t B, int32_t H, int32_t d,
+                                  int64_t T, int32_t block, int32_t causal, float scale,
+                                  int32_t dtype, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of jagged_block_attn_fwd (dtype JA_BF16): as jagged_attn_bwd with
+ * act = JA_ACT_SOFTMAX and window = 0 under the same block mask; needs the
+ * forward's out and lse; workspace: ja_bwd_workspace_size(B, H, d, T, T,
+ * JA_ACT_SOFTMAX, causal, 0, dtype) bytes. */
+ja_status_t jagged_block_attn_bwd(const void* q, const void* k, const void* v,
+                                  const void* out, const void* dout, const float* lse,
+                                  const int32_t* offsets, int32_t B, int32_t H, int32_t d,
+                                  int64_t T, int32_t block, int32_t causal, float scale,
+                                  int32_t dtype, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Runs only the tile scheduler that jagged_attn_fwd runs first ("software tile
  * scheduling for jagged tensors", GDPA section) and copies its work list out:

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) jagged attention: JFA softmax and GDPA SiLU/GELU forward, softmax backward.
+"""MI355X (gfx950) jagged attention: JFA softmax and GDPA SiLU/GELU forward and backward,
+including the block-diagonal BlockAttention form.
 
 The computation runs in ``libjagged_attn.so`` (hand-written HIP kernels behind the C
 ABI of ``include/jagged_attn.h``); this package only marshals torch tensors into it.
@@ -10,12 +11,16 @@ from .ops import (  # noqa: F401
     fwd_workspace_size,
     jagged_attn_bwd,
     jagged_attn_fwd,
+    jagged_block_attn_bwd,
+    jagged_block_attn_fwd,
     validate_offsets,
 )
 
 __all__ = [
     "jagged_attn_fwd",
     "jagged_attn_bwd",
+    "jagged_block_attn_fwd",
+    "jagged_block_attn_bwd",
     "fwd_workspace_size",
     "bwd_workspace_size",
     "fwd_schedule",

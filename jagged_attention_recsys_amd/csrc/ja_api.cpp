@@ -13,6 +13,7 @@
 
 #include "jagged_attn.h"
 #include "ja_internal.h"
+#include "ja_tiles.h"
 
 using namespace ja;
 
@@ -111,7 +112,7 @@ int fwd_occupancy(int dtype, int d, int act, bool split) {
 }
 
 SchedArgs sched_args(const FwdPlan& p, const int32_t* q_offsets, const int32_t* k_offsets, int32_t B,
-                     int32_t H, int32_t causal, int32_t window, void* workspace) {
+                     int32_t H, int32_t causal, int32_t window, int32_t bsh, void* workspace) {
     char* ws = static_cast<char*>(workspace);
     SchedArgs s;
     s.row_off = q_offsets;
@@ -123,6 +124,7 @@ SchedArgs sched_args(const FwdPlan& p, const int32_t* q_offsets, const int32_t* 
     s.causal = causal ? 1 : 0;
     s.window = window;
     s.transposed = 0;
+    s.bsh = bsh;
     s.max_pairs = p.max_pairs;
     s.tbase = reinterpret_cast<int32_t*>(ws + p.off_tbase);
     s.items = reinterpret_cast<int32_t*>(ws + p.off_items);
@@ -130,23 +132,18 @@ SchedArgs sched_args(const FwdPlan& p, const int32_t* q_offsets, const int32_t* 
     return s;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t ja_fwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
-                             int32_t causal, int32_t window, int32_t dtype) {
-    (void)causal;
-    if (check_common(B, H, d, Tq, Tk, act, window, 1.0f, dtype) != JA_OK) return 0;
-    FwdPlan p;
-    if (plan_fwd(B, H, d, Tq, act, dtype, &p) != JA_OK) return 0;
-    return p.bytes;
+// log2 of a block size that is a power of two in [1, 2^30], else -1.
+int block_shift(int32_t block) {
+    if (block < 1 || (block & (block - 1)) != 0) return -1;
+    int sh = 0;
+    while ((1 << sh) < block) ++sh;
+    return sh;
 }
 
-ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
-                            const int32_t* k_offsets, int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
-                            int32_t act, int32_t causal, int32_t window, float scale, int32_t dtype, void* out,
-                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+ja_status_t fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                     const int32_t* k_offsets, int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                     int32_t act, int32_t causal, int32_t window, int32_t bsh, float scale, int32_t dtype, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
     ja_status_t st = check_common(B, H, d, Tq, Tk, act, window, scale, dtype);
     if (st != JA_OK) return st;
     if (B == 0 || Tq == 0) return JA_OK;  // no query rows: nothing to write
@@ -161,7 +158,7 @@ ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v, const i
     if (workspace_bytes < p.bytes) return JA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    SchedArgs sa = sched_args(p, q_offsets, k_offsets, B, H, causal, window, workspace);
+    SchedArgs sa = sched_args(p, q_offsets, k_offsets, B, H, causal, window, bsh, workspace);
     if (launch_sched(sa, s) != hipSuccess) return JA_ERR_HIP;
 
     FwdArgs fa;
@@ -179,6 +176,7 @@ ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v, const i
     fa.Tk = (int32_t)Tk;
     fa.causal = causal ? 1 : 0;
     fa.window = window;
+    fa.bsh = bsh;
     fa.scale = scale;
     const int64_t max_items = p.max_pairs * H;
     int64_t grid = (int64_t)device_cus() * fwd_occupancy(dtype, d, act, p.split);
@@ -190,21 +188,11 @@ ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v, const i
     return JA_OK;
 }
 
-size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
-                             int32_t causal, int32_t window, int32_t dtype) {
-    (void)causal;
-    if (check_common(B, H, d, Tq, Tk, act, window, 1.0f, dtype) != JA_OK) return 0;
-    if (!bwd_supported(dtype, d, act)) return 0;
-    BwdPlan p;
-    if (plan_bwd(B, H, Tq, Tk, &p) != JA_OK) return 0;
-    return p.bytes;
-}
-
-ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                            const float* lse, const int32_t* q_offsets, const int32_t* k_offsets, int32_t B,
-                            int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t causal,
-                            int32_t window, float scale, int32_t dtype, void* dq, void* dk, void* dv,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+ja_status_t bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, const int32_t* q_offsets, const int32_t* k_offsets, int32_t B, int32_t H,
+                     int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t causal, int32_t window, int32_t bsh,
+                     float scale, int32_t dtype, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, void* stream) {
     ja_status_t st = check_common(B, H, d, Tq, Tk, act, window, scale, dtype);
     if (st != JA_OK) return st;
     if (!bwd_supported(dtype, d, act)) return JA_ERR_UNSUPPORTED;
@@ -235,6 +223,7 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const v
     sq.causal = causal ? 1 : 0;
     sq.window = window;
     sq.transposed = 0;
+    sq.bsh = bsh;
     sq.max_pairs = p.max_q_pairs;
     sq.tbase = reinterpret_cast<int32_t*>(ws + p.off_qtbase);
     sq.items = reinterpret_cast<int32_t*>(ws + p.off_qitems);
@@ -272,6 +261,7 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const v
     ba.Tk = (int32_t)Tk;
     ba.causal = causal ? 1 : 0;
     ba.window = window;
+    ba.bsh = bsh;
     ba.scale = scale;
     const int64_t cap_q = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, false);
     const int64_t cap_k = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, true);
@@ -282,6 +272,66 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const v
     if (gk < 1) gk = 1;
     if (launch_bwd(ba, d, act, (int)gq, (int)gk, s, g_prof_before, g_prof_after) != hipSuccess) return JA_ERR_HIP;
     return JA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ja_fwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
+                             int32_t causal, int32_t window, int32_t dtype) {
+    (void)causal;
+    if (check_common(B, H, d, Tq, Tk, act, window, 1.0f, dtype) != JA_OK) return 0;
+    FwdPlan p;
+    if (plan_fwd(B, H, d, Tq, act, dtype, &p) != JA_OK) return 0;
+    return p.bytes;
+}
+
+ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                            const int32_t* k_offsets, int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                            int32_t act, int32_t causal, int32_t window, float scale, int32_t dtype, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_impl(q, k, v, q_offsets, k_offsets, B, H, d, Tq, Tk, act, causal, window, kNoBlock, scale, dtype,
+                    out, lse, workspace, workspace_bytes, stream);
+}
+
+ja_status_t jagged_block_attn_fwd(const void* q, const void* k, const void* v, const int32_t* offsets, int32_t B,
+                                  int32_t H, int32_t d, int64_t T, int32_t block, int32_t causal, float scale,
+                                  int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    const int bsh = block_shift(block);
+    if (bsh < 0) return JA_ERR_INVALID_ARG;
+    return fwd_impl(q, k, v, offsets, offsets, B, H, d, T, T, JA_ACT_SOFTMAX, causal, 0, bsh, scale, dtype, out,
+                    lse, workspace, workspace_bytes, stream);
+}
+
+size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
+                             int32_t causal, int32_t window, int32_t dtype) {
+    (void)causal;
+    if (check_common(B, H, d, Tq, Tk, act, window, 1.0f, dtype) != JA_OK) return 0;
+    if (!bwd_supported(dtype, d, act)) return 0;
+    BwdPlan p;
+    if (plan_bwd(B, H, Tq, Tk, &p) != JA_OK) return 0;
+    return p.bytes;
+}
+
+ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                            const float* lse, const int32_t* q_offsets, const int32_t* k_offsets, int32_t B,
+                            int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t causal,
+                            int32_t window, float scale, int32_t dtype, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl(q, k, v, out, dout, lse, q_offsets, k_offsets, B, H, d, Tq, Tk, act, causal, window, kNoBlock,
+                    scale, dtype, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+ja_status_t jagged_block_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                  const float* lse, const int32_t* offsets, int32_t B, int32_t H, int32_t d,
+                                  int64_t T, int32_t block, int32_t causal, float scale, int32_t dtype, void* dq,
+                                  void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+    const int bsh = block_shift(block);
+    if (bsh < 0) return JA_ERR_INVALID_ARG;
+    return bwd_impl(q, k, v, out, dout, lse, offsets, offsets, B, H, d, T, T, JA_ACT_SOFTMAX, causal, 0, bsh, scale,
+                    dtype, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets, int32_t B, int32_t H, int32_t d,
@@ -297,7 +347,7 @@ ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets, 
     if (max_items < p.max_pairs) return JA_ERR_INVALID_ARG;
     if (workspace_bytes < p.bytes) return JA_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    SchedArgs sa = sched_args(p, q_offsets, k_offsets, B, H, causal, window, workspace);
+    SchedArgs sa = sched_args(p, q_offsets, k_offsets, B, H, causal, window, kNoBlock, workspace);
     if (launch_sched(sa, s) != hipSuccess) return JA_ERR_HIP;
     if (launch_copy_items(sa.counters, sa.items, items, count, max_items, s) != hipSuccess) return JA_ERR_HIP;
     return JA_OK;

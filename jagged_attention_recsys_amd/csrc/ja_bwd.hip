@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
     const int total = a.q_counters[kCtrTotal];
     const int64_t rs = (int64_t)a.H * D;
     const uint32_t rsb = (uint32_t)(rs * (int)sizeof(T));
-    const int causal = a.causal, window = a.window;
+    const int causal = a.causal, window = a.window, bsh = a.bsh;
     const float c_exp = a.scale * kLog2e;
 
     int koff[C::NS];
@@ -97,12 +97,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
         const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
         const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
         const int q0 = qt * kBwdRows;
-        const ColRange cr = visible_cols(Lq, Lk, q0, kBwdRows, causal, window, 0);
+        const ColRange cr = visible_cols(Lq, Lk, q0, kBwdRows, causal, window, 0, bsh);
         const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
         const int kt_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
         const int qw0 = q0 + 32 * wave;
         const int my_row = qw0 + col;
         const bool row_ok = my_row < Lq;
+        const VisRange vis = keys_seen_by(my_row, Lk, causal, window, bsh);
         const int64_t qrow = (qo + my_row) * rs + (int64_t)h * D + KP * grp;
 
         // Q^T and dO^T as B operands; for softmax Di from O and dO in the same
@@ -153,9 +154,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
         auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
             if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
             const int kw0 = kt * kBwdStage;
-            const bool skip = qw0 >= Lq || block_all_masked(qw0, 32, kw0, kBwdStage, Lk, causal, window);
+            const bool skip = wave_skips(vis, row_ok, kw0, kBwdStage);
             if (!skip) {
-                const bool need_mask = block_needs_mask(qw0, 32, kw0, kBwdStage, Lk, causal, window);
+                const bool need_mask = wave_needs_mask(vis, row_ok, kw0, kBwdStage);
                 frag dsf[C::NB][C::NT];
 #pragma unroll
                 for (int nb = 0; nb < C::NB; ++nb) {
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
                         }
                         if (need_mask) {
                             const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
-                            g = visible(my_row, key, Lk, causal, window) ? g : 0.0f;
+                            g = vis.has(key) ? g : 0.0f;
                         }
                         sacc[r] = g;
                     }
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
     const int64_t rs = (int64_t)a.H * D;
     const uint32_t rsb = (uint32_t)(rs * (int)sizeof(T));
     const uint32_t hsb = (uint32_t)(a.H * 4);  // stride of one row of lse / Di, bytes
-    const int causal = a.causal, window = a.window;
+    const int causal = a.causal, window = a.window, bsh = a.bsh;
     const float c_exp = a.scale * kLog2e;
 
     int roff[C::NS];
@@ -272,12 +273,13 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
         const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
         const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
         const int k0 = kt * kBwdRows;
-        const ColRange cr = visible_cols(Lk, Lq, k0, kBwdRows, causal, window, 1);
+        const ColRange cr = visible_cols(Lk, Lq, k0, kBwdRows, causal, window, 1, bsh);
         const int qs_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
         const int qs_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
         const int kw0 = k0 + 32 * wave;
         const int my_key = kw0 + col;
         const bool key_ok = my_key < Lk;
+        const VisRange vis = queries_seeing(my_key, Lq, Lk, causal, window, bsh);
         const int64_t krow = (ko + my_key) * rs + (int64_t)h * D + KP * grp;
 
         const float inv_lk = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
@@ -328,10 +330,9 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
                 const int qb0 = qbase + nb * 32;  // first query of this block
                 // Wave-uniform: lanes past the sequence end still feed the shared
                 // matrix operands (their K/V rows are zero and masked below).
-                const bool skip = qb0 >= Lq || block_all_masked(qb0, 32, kw0, 32, Lk, causal, window);
+                const bool skip = wave_skips(vis, key_ok, qb0, 32);
                 if (skip) continue;
-                const bool need_mask =
-                    qb0 + 32 > Lq || block_needs_mask(qb0, 32, kw0, 32, Lk, causal, window);
+                const bool need_mask = wave_needs_mask(vis, key_ok, qb0, 32);
                 const char* qblk = ql + nb * 32 * C::ROWB;
                 const char* oblk = ol + nb * 32 * C::ROWB;
                 floatx16 sacc = floatx16{}, dpacc = floatx16{};
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
                     }
                     if (need_mask) {
                         const int q = qb0 + key_of_reg<KP>(grp, r);
-                        const bool ok = q < Lq && visible(q, my_key, Lk, causal, window);
+                        const bool ok = vis.has(q);
                         p = ok ? p : 0.0f;
                         g = ok ? g : 0.0f;
                     }

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
     T* __restrict__ Og = (T*)a.out;
     const int64_t rs = (int64_t)a.H * D;          // token row stride, elements
     const uint32_t rsb = (uint32_t)(rs * C::ESZ);  // ... bytes
-    const int causal = a.causal, window = a.window;
+    const int causal = a.causal, window = a.window, bsh = a.bsh;
 
     // Softmax works in the exp2 domain. With scale > 0 the row max is taken on raw
     // scores and folded into one FMA per element; otherwise scores are scaled first.
@@ -152,16 +152,18 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
         const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
         const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
         const int q0 = qt * C::BM;
-        const ColRange cr = visible_cols(Lq, Lk, q0, C::BM, causal, window, 0);
+        const ColRange cr = visible_cols(Lq, Lk, q0, C::BM, causal, window, 0, bsh);
         const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / C::KT) : 0;
         const int kt_hi = cr.hi > cr.lo ? (int)((cr.hi + C::KT - 1) / C::KT) : 0;
         const int qw0 = q0 + 32 * wq;  // first query row of this wave
         const int my_row = qw0 + col;
+        const bool row_ok = my_row < Lq;
+        const VisRange vis = keys_seen_by(my_row, Lk, causal, window, bsh);
 
         // Queries as the B operand of S^T = K Q^T, kept in registers.
         frag qf[C::NS];
         {
-            const bool ok = my_row < Lq;
+            const bool ok = row_ok;
             const T* src = Qg + (qo + my_row) * rs + (int64_t)h * D + KP * grp;
 #pragma unroll
             for (int s = 0; s < C::NS; ++s) qf[s] = ok ? *(const frag*)(src + 2 * KP * s) : Frag<T>::zero();
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
         auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
             if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
             const int kw0 = kt * C::KT + wk * 32 * C::NB;  // first key of this wave's blocks
-            const bool skip = qw0 >= Lq || block_all_masked(qw0, 32, kw0, 32 * C::NB, Lk, causal, window);
+            const bool skip = wave_skips(vis, row_ok, kw0, 32 * C::NB);
             if (!skip) {
                 floatx16 sacc[C::NB];
 #pragma unroll
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
                         sacc[nb] = M::run(C::KVTile::read_rows(kblk, koff[s]), qf[s], sacc[nb]);
                 }
 
-                const bool need_mask = block_needs_mask(qw0, 32, kw0, 32 * C::NB, Lk, causal, window);
+                const bool need_mask = wave_needs_mask(vis, row_ok, kw0, 32 * C::NB);
                 if (ACT == ACT_SOFTMAX) {
                     if (prescale) {
 #pragma unroll
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
-                                sacc[nb][r] = visible(my_row, key, Lk, causal, window) ? sacc[nb][r] : -INFINITY;
+                                sacc[nb][r] = vis.has(key) ? sacc[nb][r] : -INFINITY;
                             }
                     }
                     float mx = -INFINITY;
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
                             float p = pointwise<ACT>(sacc[nb][r] * a.scale);
                             if (need_mask) {
                                 const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
-                                p = visible(my_row, key, Lk, causal, window) ? p : 0.0f;
+                                p = vis.has(key) ? p : 0.0f;
                             }
                             sacc[nb][r] = p;
                         }

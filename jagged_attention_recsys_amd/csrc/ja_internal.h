@@ -19,6 +19,7 @@ struct SchedArgs {
     int32_t B, H;
     int32_t bm, bn;          // row tile, column tile (cost unit)
     int32_t causal, window, transposed;
+    int32_t bsh;             // block shift of the block-diagonal mask (kNoBlock: none)
     int64_t max_pairs;       // capacity of items; a larger enumeration schedules nothing
     int32_t* tbase;          // [B+1] scratch: first flat tile of each sequence
     int32_t* items;          // [2 * max_pairs] (sequence, tile) pairs
@@ -42,6 +43,7 @@ struct FwdArgs {
     int32_t H;
     int32_t Tq, Tk;            // tensor extents: rows outside [0, T) are never touched
     int32_t causal, window;
+    int32_t bsh;               // block shift of the block-diagonal mask (kNoBlock: none)
     float scale;               // applied to Q K^T
 };
 
@@ -80,6 +82,7 @@ struct BwdArgs {
     int32_t H;
     int32_t Tq, Tk;
     int32_t causal, window;
+    int32_t bsh;               // block shift of the block-diagonal mask (kNoBlock: none)
     float scale;
 };
 bool bwd_supported(int dtype, int d, int act);

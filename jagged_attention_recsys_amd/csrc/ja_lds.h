@@ -13,6 +13,7 @@
 #pragma once
 
 #include "ja_common.h"
+#include "ja_tiles.h"
 
 namespace ja {
 
@@ -146,10 +147,14 @@ struct TileLoader {
     }
 };
 
-__device__ __forceinline__ bool visible(int row, int key, int Lk, int causal, int window) {
-    const int diff = row - key;
-    const int adiff = causal ? diff : (diff < 0 ? -diff : diff);
-    return (key < Lk) & (!causal | (key <= row)) & ((window == 0) | (adiff < window));
+// Wave-uniform mask decisions for a block [x0, x0 + n) of the other index, from
+// every lane's visible range; lanes with lane_ok false (rows past the sequence
+// end, never written) take no part.
+__device__ __forceinline__ bool wave_skips(const VisRange& v, bool lane_ok, int x0, int n) {
+    return __all(!lane_ok || v.misses(x0, n));
+}
+__device__ __forceinline__ bool wave_needs_mask(const VisRange& v, bool lane_ok, int x0, int n) {
+    return __any(lane_ok && !v.covers(x0, n));
 }
 
 // Reductions over lanes l and l^32 (the two halves of a C-tile column).

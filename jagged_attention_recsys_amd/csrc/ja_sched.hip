@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
         const int t = f - tb[b];
         const int64_t Lr = (int64_t)ro[b + 1] - ro[b];
         const int64_t Lc = (int64_t)co[b + 1] - co[b];
-        const ColRange cr = visible_cols(Lr, Lc, (int64_t)t * a.bm, a.bm, a.causal, a.window, a.transposed);
+        const ColRange cr = visible_cols(Lr, Lc, (int64_t)t * a.bm, a.bm, a.causal, a.window, a.transposed, a.bsh);
         const int cost = tile_cost(cr, a.bn);
         *pb = b;
         *pt = t;

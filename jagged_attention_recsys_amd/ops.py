@@ -133,6 +133,72 @@ def jagged_attn_bwd(q, k, v, out, dout, lse, q_offsets, k_offsets, act="softmax"
     return dq, dk, dv
 
 
+def jagged_block_attn_fwd(q, k, v, offsets, block, causal=False, scale=None, out=None, lse=None,
+                          workspace=None, stream=None):
+    """Block-diagonal self-attention forward (softmax): each block of ``block`` tokens
+    of a sequence attends only within itself. q, k, v: [T,H,d]; offsets: int32 [B+1].
+
+    Returns (out [T,H,d], lse [T,H] float32)."""
+    lib = _lib.load()
+    _check_tensor("q", q, dim=3)
+    dtype = q.dtype
+    if dtype not in DTYPE:
+        raise ValueError(f"unsupported dtype {dtype}")
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, dtype, 3)
+    _check_tensor("offsets", offsets, torch.int32, 1)
+    T, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must all be [T, H, d]")
+    B = offsets.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, dtype)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    ws_bytes = int(lib.ja_fwd_workspace_size(B, H, d, T, T, 0, int(bool(causal)), 0, DTYPE[dtype]))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    status = lib.jagged_block_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, d, T, int(block),
+                                       int(bool(causal)), float(scale), DTYPE[dtype], _ptr(out), _ptr(lse),
+                                       _ptr(workspace), workspace.numel(), _stream(q.device, stream))
+    _lib.check("jagged_block_attn_fwd", status)
+    return out, lse
+
+
+def jagged_block_attn_bwd(q, k, v, out, dout, lse, offsets, block, causal=False, scale=None, dq=None, dk=None,
+                          dv=None, workspace=None, stream=None):
+    """Backward of jagged_block_attn_fwd. Returns (dq, dk, dv)."""
+    lib = _lib.load()
+    _check_tensor("q", q, dim=3)
+    dtype = q.dtype
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _check_tensor(name, t, dtype, 3)
+    if out is not None:
+        _check_tensor("out", out, dtype, 3)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, 2)
+    T, H, d = q.shape
+    B = offsets.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = int(lib.ja_bwd_workspace_size(B, H, d, T, T, 0, int(bool(causal)), 0, DTYPE[dtype]))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    status = lib.jagged_block_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                       _ptr(offsets), B, H, d, T, int(block), int(bool(causal)), float(scale),
+                                       DTYPE[dtype], _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                       workspace.numel(), _stream(q.device, stream))
+    _lib.check("jagged_block_attn_bwd", status)
+    return dq, dk, dv
+
+
 def fwd_tile_shape(B, d, Tq, act="softmax", dtype=torch.bfloat16):
     import ctypes
     bm, bn = ctypes.c_int32(), ctypes.c_int32()

@@ -5,12 +5,13 @@ tensors, rounded to bf16 where a workload asks for it. It holds none of the
 attention arithmetic, so both the HIP path (through its tests and benchmark) and
 the fp64 oracle can be fed from the same bytes.
 
-The five workloads follow the shapes the engineering post "GEM Training: How Meta
+The six workloads follow the shapes the engineering post "GEM Training: How Meta
 Doubled the Efficiency of Its LLM-Scale Ads Foundation Model" describes in its
 "Challenge 1" section (jagged user histories from hundreds to tens of thousands of
 tokens; self-attention, cross-attention with long queries and short key/value,
 pooled multi-head attention with short queries and long key/value) and in its
-"BlockAttention" section (sliding window over long histories). The pages give no
+"BlockAttention" section (sliding window over long histories, then fixed 64-token
+blocks that attend only within themselves). The pages give no
 sizes; the sizes below are this library's synthetic stand-ins for the production
 traffic they describe.
 
@@ -49,6 +50,7 @@ class Workload:
     causal: bool = False
     window: int = 0
     dout: np.ndarray | None = None
+    block: int = 0  # > 0: block-diagonal mask of this many tokens (self-attention only)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -148,7 +150,7 @@ def _build(rng, name, lq, lk, H, d, dtype, act, causal, window, with_dout, share
                     act=act, causal=causal, window=window, dout=dout)
 
 
-# --- the five named workloads ------------------------------------------------
+# --- the six named workloads ------------------------------------------------
 
 WORKLOADS = {
     1: "tiny jagged softmax self-attention fwd, fp32: B=4 lengths {7,33,64,129}, H=2, d=32 "
@@ -161,11 +163,13 @@ WORKLOADS = {
        "log-uniform [1024,16384], H=8, d=64",
     5: "jagged sliding-window causal softmax self-attention fwd+bwd, bf16: B=32, lengths lognormal "
        "(median 2048, sigma 1, cap 32768), window 1024, H=8, d=128",
+    6: "jagged block-diagonal causal softmax self-attention fwd+bwd (BlockAttention), bf16: B=32, "
+       "lengths lognormal (median 2048, sigma 1, cap 32768), blocks of 64 tokens, H=8, d=128",
 }
 
 
 def workload(n: int, act: str | None = None, seed: int | None = None) -> Workload:
-    """Build workload ``n`` (1..5) from its seed (default: n)."""
+    """Build workload ``n`` (1..6) from its seed (default: n)."""
     rng = np.random.default_rng(n if seed is None else seed)
     if n == 1:
         lq = np.array([7, 33, 64, 129], dtype=np.int64)
@@ -184,6 +188,10 @@ def workload(n: int, act: str | None = None, seed: int | None = None) -> Workloa
     elif n == 5:
         lq = lognormal_lengths(rng, 32, 2048.0, 1.0, 32768)
         w = _build(rng, "w5", lq, lq, 8, 128, BF16, act or "softmax", True, 1024, True, None)
+    elif n == 6:
+        lq = lognormal_lengths(rng, 32, 2048.0, 1.0, 32768)
+        w = _build(rng, "w6", lq, lq, 8, 128, BF16, act or "softmax", True, 0, True, None)
+        w.block = 64
     else:
         raise ValueError(f"unknown workload {n}")
     w.extra["description"] = WORKLOADS[n]

@@ -1,0 +1,158 @@
+"""GPU parity of block-diagonal self-attention (the "BlockAttention" section of the
+GEM training post: fixed token blocks, each query block attending only to the
+keys and values of its own block) against the fp64 oracle.
+
+The HIP forward (jagged_block_attn_fwd) and backward (jagged_block_attn_bwd) run
+through the C ABI; the oracle's fwd / bwd with the same block size are the
+reference. Cases: ragged batches whose lengths are not multiples of the block
+(short last blocks) and span several tiles, block sizes below, at and above the
+forward's 128-row tile, causal and not, d in {32, 64, 128}, fp32 and bf16; many
+short sequences (the split layout); the full block workload on sampled
+(sequence, head) pairs; a block at least as long as every sequence, which must
+give bit for bit the result of the unmasked entry points; and argument errors.
+bf16 results are held to the non-strict bound (absolute 2e-2 plus 2^-8 relative,
+and the mean bound): under a causal block mask the first query of every block
+sees only its own key (P = 1), so dV of that key carries a whole dO row, and with
+one- or two-token blocks so do the outputs; values reach ~7, where the bf16
+rounding of the result alone is up to 2^-6 / 2 = 0.0156.
+"""
+import numpy as np
+import pytest
+import torch
+
+import jagged_attention_recsys_amd as ja
+import oracle
+from jagged_attention_recsys_amd import workloads as W
+from _parity import compare, rows_of_pairs, say, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 2
+RAGGED = [1, 7, 64, 65, 127, 128, 129, 300, 0, 263, 1000]
+
+
+def guarded(shape, dtype):
+    full = torch.full((shape[0] + 2 * GUARD,) + tuple(shape[1:]), float("nan"), dtype=dtype, device="cuda")
+    return full, full[GUARD:GUARD + shape[0]]
+
+
+def _check_guard(full, n):
+    assert torch.isnan(full[:GUARD].float()).all() and torch.isnan(full[GUARD + n:].float()).all(), "guard band"
+
+
+def run_block(w, block, causal, bwd=True):
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    off = to_dev(w.q_offsets)
+    T = q.shape[0]
+    fo, out = guarded(q.shape, q.dtype)
+    out, lse = ja.jagged_block_attn_fwd(q, k, v, off, block, causal=causal, scale=w.scale, out=out)
+    if not bwd:
+        torch.cuda.synchronize()
+        _check_guard(fo, T)
+        return out, lse, None
+    do = to_dev(w.dout)
+    fq, dq = guarded(q.shape, q.dtype)
+    fk, dk = guarded(k.shape, k.dtype)
+    fv, dv = guarded(v.shape, v.dtype)
+    ja.jagged_block_attn_bwd(q, k, v, out, do, lse, off, block, causal=causal, scale=w.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for f in (fo, fq, fk, fv):
+        _check_guard(f, T)
+    return out, lse, (dq, dk, dv)
+
+
+def check(w, block, causal, bwd=True, pair_mask=None, what="", strict=False):
+    say(f"[block] {what} B={w.B} H={w.H} d={w.d} T={w.q.shape[0]} block={block} causal={causal} "
+        f"dtype={w.dtype} bwd={bwd}")
+    out, lse, grads = run_block(w, block, causal, bwd)
+    sel = rows_of_pairs(w.q_offsets, w.H, pair_mask)
+    stats = {}
+    if bwd:
+        ro, rl, rq, rk, rv = oracle.bwd(w.q, w.k, w.v, w.dout, w.q_offsets, w.k_offsets, "softmax", causal, 0,
+                                        w.scale, pair_mask=pair_mask, block=block)
+    else:
+        ro, rl = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, "softmax", causal, 0, w.scale,
+                            pair_mask=pair_mask, block=block)
+    stats["out"] = compare(to_host64(out), ro, w.dtype, f"out {what}", sel, strict=strict)
+    gl = to_host64(lse)[sel]
+    assert np.all(np.isfinite(gl)), "every row sees at least its own key"
+    lse_err = float(np.max(np.abs(gl - rl[sel]))) if gl.size else 0.0
+    lse_tol = (1e-5 if w.dtype == "f32" else 1e-3) * max(1.0, float(np.max(np.abs(rl[sel]))) if gl.size else 1.0)
+    assert lse_err <= lse_tol, f"lse {what}: {lse_err} > {lse_tol}"
+    if bwd:
+        for name, got, ref in (("dq", grads[0], rq), ("dk", grads[1], rk), ("dv", grads[2], rv)):
+            stats[name] = compare(to_host64(got), ref, w.dtype, f"{name} {what}", sel, strict=strict)
+    say(f"      ok lse_err={lse_err:.2e} {stats}")
+
+
+def case(lengths, H=2, d=64, dtype=W.BF16, seed=0):
+    return W.make_case(lengths, None, H=H, d=d, dtype=dtype, seed=seed, with_dout=True)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("block", [32, 64, 256])
+def test_ragged_block_fwd_bwd(d, causal, block):
+    check(case(RAGGED, d=d, seed=600 + d + block + causal), block, causal, what="ragged")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_block_fp32_fwd(d, causal):
+    check(case(RAGGED, d=d, dtype=W.F32, seed=700 + d + causal), 64, causal, bwd=False, what="fp32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_short_sequences_block(d, causal):
+    # mean length <= 48 tokens: the forward uses its split (short-query) layout
+    rng = np.random.default_rng(d)
+    lengths = rng.integers(0, 90, size=300)
+    check(case(lengths, H=3, d=d, seed=800 + d + causal), 64, causal, what="short")
+
+
+@pytest.mark.parametrize("block", [1, 2, 16])
+def test_tiny_blocks(block):
+    check(case([1, 5, 17, 64, 130], H=2, d=64, seed=900 + block), block, True, what="tiny-block")
+
+
+def _sample_pairs(w, n, seed):
+    rng = np.random.default_rng(seed)
+    mask = np.zeros((w.B, w.H), dtype=bool)
+    mask[int(np.argmax(w.lq)), 0] = True
+    mask[int(np.argmin(w.lq)), w.H - 1] = True
+    while mask.sum() < n:
+        mask[int(rng.integers(w.B)), int(rng.integers(w.H))] = True
+    return mask
+
+
+def test_workload6_fwd_bwd_sampled():
+    w = W.workload(6)
+    check(w, w.block, w.causal, pair_mask=_sample_pairs(w, 8, 6), what="w6")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_longer_than_every_sequence_is_plain_attention(causal):
+    w = case([300, 5, 1000, 129], H=2, d=128, seed=950 + causal)
+    out_b, lse_b, g_b = run_block(w, 1024, causal)
+    q, k, v, off, do = to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.q_offsets), to_dev(w.dout)
+    out, lse = ja.jagged_attn_fwd(q, k, v, off, off, causal=causal, scale=w.scale)
+    g = ja.jagged_attn_bwd(q, k, v, out, do, lse, off, off, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_b.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(lse_b, lse)
+    for x, y in zip(g_b, g):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_rejects_bad_block():
+    w = case([10, 20], d=64, seed=990)
+    q, k, v, off = to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.q_offsets)
+    for block in (0, -64, 48, 3):
+        with pytest.raises(RuntimeError):
+            ja.jagged_block_attn_fwd(q, k, v, off, block)
+    out, lse = ja.jagged_block_attn_fwd(q, k, v, off, 64)
+    with pytest.raises(RuntimeError):
+        ja.jagged_block_attn_bwd(q, k, v, out, q, lse, off, 96)
+    with pytest.raises(RuntimeError):  # needs the forward's out and lse
+        ja.jagged_block_attn_bwd(q, k, v, None, q, None, off, 64)
