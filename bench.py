@@ -13,11 +13,13 @@ Reported:
   value        useful (unpadded) TFLOP/s of the whole step: 4 d H sum_b pairs_b per
                forward (10 d H pairs for the backward), pairs_b = visible (query,
                key) pairs of sequence b, over the measured step time;
-  roofline     the attention kernel alone, timed with HIP events recorded on its own
-               stream right before and after its launch (library profiling hook),
-               against the published dense bf16 MFMA peak; `traffic` is HBM bytes per
-               launch from committed rocprofv3 counter runs, or null when the kernel
-               source changed since they were taken;
+  roofline     the forward attention kernel alone, timed with HIP events recorded on
+               its own stream right before and after its launch (library profiling
+               hook): useful TFLOP/s against the published dense bf16 MFMA peak, or,
+               for the HBM-bound batches (3, 4, 6), algorithmic bytes (Q, K, V read
+               and O written once) per second against the published 8 TB/s;
+               `traffic` is HBM bytes per launch from committed rocprofv3 counter
+               runs, or null when the kernel source changed since they were taken;
   cpu_baseline the fp64 oracle on a bounded sample of the same batch, on every host
                core (a reported baseline, not a target); its outputs double as a
                parity spot-check of the GPU result on the sampled pairs.
@@ -39,6 +41,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+HBM_BOUND = (3, 4, 6)         # workloads whose forward is bound by HBM traffic, not the matrix cores
 KERNEL_SOURCES = {
     "ja_fwd_kernel": ["ja_fwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
     "ja_bwd_kernels": ["ja_bwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
@@ -72,6 +75,12 @@ def visible_pairs(lq: np.ndarray, lk: np.ndarray, causal: bool, window: int, blo
             hi = np.full(Lq, Lk - 1, dtype=np.int64) if window == 0 else np.minimum(Lk - 1, i + window - 1)
         total += int(np.maximum(0, hi - lo + 1).sum())
     return total
+
+
+def roofline_kernel(workload: int) -> str:
+    """The kernel the roofline is taken on: the forward attention kernel (every
+    workload, the block one included, runs the same forward)."""
+    return "ja_fwd_kernel"
 
 
 def kernel_sha(name: str) -> str:
@@ -153,13 +162,19 @@ def main() -> int:
     dout = up(w.dout) if args.bwd else None
     Tq, Tk = q.shape[0], k.shape[0]
     out = torch.empty_like(q)
-    lse = torch.empty((Tq, w.H), dtype=torch.float32, device=dev) if w.act == "softmax" else None
-    ws = torch.empty(max(ja.fwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window), 256),
-                     dtype=torch.uint8, device=dev)
+    # The block path (blocks of at most 64 tokens) keeps no log-sum-exp: its
+    # backward recomputes each block's softmax.
+    need_lse = w.act == "softmax" and not (w.block and w.block <= 64)
+    lse = torch.empty((Tq, w.H), dtype=torch.float32, device=dev) if need_lse else None
+    if w.block:
+        ws_fwd = ws_bwd = ja.block_attn_workspace_size(w.B, w.H, w.d, Tq, w.block, w.causal)
+    else:
+        ws_fwd = ja.fwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window)
+        ws_bwd = ja.bwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window) if args.bwd else 0
+    ws = torch.empty(max(ws_fwd, 256), dtype=torch.uint8, device=dev)
     if args.bwd:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        bws = torch.empty(max(ja.bwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window), 256),
-                          dtype=torch.uint8, device=dev)
+        bws = torch.empty(max(ws_bwd, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     pairs = visible_pairs(w.lq, w.lk, w.causal, w.window, w.block)
@@ -171,7 +186,7 @@ def main() -> int:
             lib.ja_set_profile_events(ev[0].cuda_event, ev[1].cuda_event)
         if w.block:
             ja.jagged_block_attn_fwd(q, k, v, qo, w.block, causal=w.causal, scale=w.scale, out=out, lse=lse,
-                                     workspace=ws, stream=stream)
+                                     workspace=ws, stream=stream, return_lse=need_lse)
         else:
             ja.jagged_attn_fwd(q, k, v, qo, ko, act=w.act, causal=w.causal, window=w.window, scale=w.scale,
                                out=out, lse=lse, workspace=ws, stream=stream)
@@ -216,21 +231,23 @@ def main() -> int:
     total_flop = fwd_flop + bwd_flop
     value = total_flop / (ms_per_step * 1e-3) / 1e12
 
-    name = "ja_fwd_kernel"
-    achieved = fwd_flop / (fwd_kernel_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(name, f"w{args.workload}"),
-                "kernel": name, "kernel_ms": round(fwd_kernel_ms, 4),
-                "flop_per_launch": fwd_flop}
-    if args.workload in (3, 4, 6):
+    name = roofline_kernel(args.workload)
+    tflops = fwd_flop / (fwd_kernel_ms * 1e-3) / 1e12
+    if args.workload in HBM_BOUND:
         # short key/value (3), short query (4) and 64-token block (6) batches are
-        # HBM-bound: their minimum traffic is reading Q, K, V once and writing O
-        # (and, for softmax, the fp32 lse) once.
-        esz = 2
-        min_bytes = esz * w.H * w.d * (2 * Tq + 2 * Tk) + (4 * w.H * Tq if w.act == "softmax" else 0)
-        roofline["min_hbm_bytes"] = min_bytes
-        roofline["hbm_gbs_at_min_bytes"] = round(min_bytes / (fwd_kernel_ms * 1e-3) / 1e9, 1)
-        roofline["hbm_frac"] = round(roofline["hbm_gbs_at_min_bytes"] / PEAK_HBM_GBS, 4)
+        # HBM-bound: the algorithmic traffic is reading Q, K, V once and writing O
+        # (and the fp32 lse where the backward needs it) once.
+        min_bytes = 2 * w.H * w.d * (2 * Tq + 2 * Tk) + (4 * w.H * Tq if need_lse else 0)
+        gbs = min_bytes / (fwd_kernel_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": min_bytes,
+                    "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flop_per_launch": fwd_flop}
+    roofline["traffic"] = recorded_traffic(name, f"w{args.workload}")
+    roofline["kernel"] = name
+    roofline["kernel_ms"] = round(fwd_kernel_ms, 4)
 
     result = {
         "metric": METRIC,
@@ -258,10 +275,10 @@ def main() -> int:
         result["bwd"] = {"kernel_ms": round(bwd_kernel_ms, 4),
                          "tflops": round(bwd_flop / (bwd_kernel_ms * 1e-3) / 1e12, 2)}
         if args.workload in (3, 4, 6):
-            # reading Q, K, V, dO once and writing dQ, dK, dV once (softmax: also
-            # reading O and lse)
+            # reading Q, K, V, dO once and writing dQ, dK, dV once (the two-pass
+            # softmax backward also reads O and lse)
             min_b = 2 * w.H * w.d * (3 * Tq + 4 * Tk)
-            if w.act == "softmax":
+            if need_lse:
                 min_b += 2 * w.H * w.d * Tq + 4 * w.H * Tq
             result["bwd"]["min_hbm_bytes"] = min_b
             result["bwd"]["hbm_gbs_at_min_bytes"] = round(min_b / (bwd_kernel_ms * 1e-3) / 1e9, 1)
@@ -298,8 +315,9 @@ def record_traffic(workload: int, fetch_dir: str, write_dir: str, copy_fetch_dir
     copy_bytes = 1024 * (1 << 20)
     cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "elementwise")
     cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "elementwise")
-    kf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", "ja_fwd_kernel")
-    kw = _counter_per_dispatch(write_dir, "WRITE_SIZE", "ja_fwd_kernel")
+    name = roofline_kernel(workload)
+    kf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", name)
+    kw = _counter_per_dispatch(write_dir, "WRITE_SIZE", name)
     if not (cf and cw and kf and kw):
         raise SystemExit("missing dispatches in the counter runs")
     f_scale = copy_bytes / (float(np.median(cf)) * 1024.0)
@@ -310,7 +328,6 @@ def record_traffic(workload: int, fetch_dir: str, write_dir: str, copy_fetch_dir
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         data = {}
-    name = "ja_fwd_kernel"
     data.setdefault(name, {})[f"w{workload}"] = {
         "hbm_bytes_per_launch": round(fetch + write),
         "fetch_bytes": round(fetch), "write_bytes": round(write),

@@ -126,29 +126,42 @@ ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v,
                             int32_t dtype, void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace jagged_block_attn_fwd and jagged_block_attn_bwd
+ * need (either call). Host only; 0 for invalid sizes or a block that is not a
+ * power of two. */
+size_t ja_block_attn_workspace_size(int32_t B, int32_t H, int32_t d, int64_t T, int32_t block,
+                                    int32_t causal, int32_t dtype);
+
 /* Block-diagonal self-attention ("BlockAttention" section of the GEM training
  * post: the sequence is cut into fixed blocks of tokens and each query block
- * attends only to the keys and values of its own block, so tiles outside the
- * blocks on the diagonal are never scheduled). Softmax only; one offsets array
- * serves queries, keys and values (self-attention, Tq = Tk = T).
+ * attends only to the keys and values of its own block, which turns attention
+ * into independent small problems). Softmax only; one offsets array serves
+ * queries, keys and values (self-attention, Tq = Tk = T).
  *   block: tokens per block, a power of two >= 1; query i (local index) sees key
  *   j iff i / block == j / block (integer division), and with causal also j <= i.
  *   Blocks restart at every sequence start; the last block of a sequence may be
  *   shorter than `block`.
- * Everything else (layout, scale, lse, alignment, ownership, errors) is as for
- * jagged_attn_fwd with act = JA_ACT_SOFTMAX, window = 0, and its workspace is
- * ja_fwd_workspace_size(B, H, d, T, T, JA_ACT_SOFTMAX, causal, 0, dtype) bytes.
- * A block that is not a power of two returns JA_ERR_INVALID_ARG. */
+ *   Runs the forward kernel of jagged_attn_fwd under the block mask: tiles off
+ *   the diagonal blocks are never scheduled, and with block <= 64 every row's
+ *   keys lie in one 64-key stage, so the online softmax takes a single step.
+ *   lse [T,H] fp32 may be NULL (then not written; the backward of blocks of at
+ *   most 64 tokens does not need it).
+ * Everything else (layout, scale, alignment, ownership, errors) is as for
+ * jagged_attn_fwd with act = JA_ACT_SOFTMAX and window = 0. workspace: at least
+ * ja_block_attn_workspace_size() bytes. A block that is not a power of two
+ * returns JA_ERR_INVALID_ARG. */
 ja_status_t jagged_block_attn_fwd(const void* q, const void* k, const void* v,
                                   const int32_t* offsets, int32_t B, int32_t H, int32_t d,
                                   int64_t T, int32_t block, int32_t causal, float scale,
                                   int32_t dtype, void* out, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward of jagged_block_attn_fwd (dtype JA_BF16): as jagged_attn_bwd with
- * act = JA_ACT_SOFTMAX and window = 0 under the same block mask; needs the
- * forward's out and lse; workspace: ja_bwd_workspace_size(B, H, d, T, T,
- * JA_ACT_SOFTMAX, causal, 0, dtype) bytes. */
+/* Backward of jagged_block_attn_fwd (dtype JA_BF16). For block <= 64 one fused
+ * kernel per 64-token tile and head recomputes the block's softmax, takes Di as
+ * sum_j P_ij dP_ij, and writes dq, dk and dv once each: out and lse are not read
+ * and may be NULL. Larger blocks run jagged_attn_bwd's two passes under the
+ * block mask and need the forward's out and lse. workspace: at least
+ * ja_block_attn_workspace_size() bytes. */
 ja_status_t jagged_block_attn_bwd(const void* q, const void* k, const void* v,
                                   const void* out, const void* dout, const float* lse,
                                   const int32_t* offsets, int32_t B, int32_t H, int32_t d,

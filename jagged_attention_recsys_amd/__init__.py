@@ -5,6 +5,7 @@ The computation runs in ``libjagged_attn.so`` (hand-written HIP kernels behind t
 ABI of ``include/jagged_attn.h``); this package only marshals torch tensors into it.
 """
 from .ops import (  # noqa: F401
+    block_attn_workspace_size,
     bwd_workspace_size,
     fwd_schedule,
     fwd_tile_shape,
@@ -23,6 +24,7 @@ __all__ = [
     "jagged_block_attn_bwd",
     "fwd_workspace_size",
     "bwd_workspace_size",
+    "block_attn_workspace_size",
     "fwd_schedule",
     "fwd_tile_shape",
     "validate_offsets",

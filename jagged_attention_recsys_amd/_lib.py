@@ -21,6 +21,7 @@ SIGNATURES = {
     "ja_bwd_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32]),
     "jagged_attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32, _i32,
                                _i32, _f32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ja_block_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i32, _i32, _i32]),
     "jagged_block_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _f32, _i32, _vp, _vp,
                                      _vp, _sz, _vp]),
     "jagged_block_attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _f32,

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "jagged_attn.h"
+#include "ja_block.h"
 #include "ja_internal.h"
 #include "ja_tiles.h"
 
@@ -89,6 +90,20 @@ ja_status_t plan_bwd(int32_t B, int32_t H, int64_t Tq, int64_t Tk, BwdPlan* p) {
     return JA_OK;
 }
 
+struct BlkPlan {
+    int64_t max_pairs;  // (sequence, 64-token tile) pairs at most
+    size_t off_tbase, off_items, bytes;
+};
+
+ja_status_t plan_blk(int32_t B, int32_t H, int64_t T, BlkPlan* p) {
+    p->max_pairs = (T + kBlkTile - 1) / kBlkTile + B;
+    if (p->max_pairs * (int64_t)H >= INT32_MAX) return JA_ERR_UNSUPPORTED;
+    p->off_tbase = align_up(sizeof(int32_t) * kCtrCount);
+    p->off_items = align_up(p->off_tbase + sizeof(int32_t) * ((size_t)B + 1));
+    p->bytes = align_up(p->off_items + sizeof(int32_t) * 2 * (size_t)p->max_pairs);
+    return JA_OK;
+}
+
 int device_cus() {
     static std::atomic<int> cache[kMaxDevices];
     int dev = 0;
@@ -107,6 +122,16 @@ int fwd_occupancy(int dtype, int d, int act, bool split) {
     int n = slot.load(std::memory_order_relaxed);
     if (n > 0) return n;
     n = fwd_blocks_per_cu(dtype, d, act, split);
+    slot.store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int blk_occupancy_cached(int d) {
+    static std::atomic<int> cache[3];
+    std::atomic<int>& slot = cache[d == 32 ? 0 : d == 64 ? 1 : 2];
+    int n = slot.load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    n = blk_blocks_per_cu(d);
     slot.store(n, std::memory_order_relaxed);
     return n;
 }
@@ -274,6 +299,45 @@ ja_status_t bwd_impl(const void* q, const void* k, const void* v, const void* ou
     return JA_OK;
 }
 
+// Block-diagonal attention with blocks of at most kBlkTile tokens: the tile
+// scheduler lists the 64-token tiles, then one workgroup per (tile, head).
+ja_status_t blk_schedule(const int32_t* offsets, int32_t B, int32_t H, int64_t T, int32_t causal, int32_t bsh,
+                         void* workspace, size_t workspace_bytes, hipStream_t s, BlkArgs* ba, int64_t* grid) {
+    BlkPlan p;
+    ja_status_t st = plan_blk(B, H, T, &p);
+    if (st != JA_OK) return st;
+    if (workspace_bytes < p.bytes) return JA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    SchedArgs sa;
+    sa.row_off = offsets;
+    sa.col_off = offsets;
+    sa.B = B;
+    sa.H = H;
+    sa.bm = kBlkTile;
+    sa.bn = kBlkTile;
+    sa.causal = causal ? 1 : 0;
+    sa.window = 0;
+    sa.transposed = 0;
+    sa.bsh = bsh;
+    sa.max_pairs = p.max_pairs;
+    sa.tbase = reinterpret_cast<int32_t*>(ws + p.off_tbase);
+    sa.items = reinterpret_cast<int32_t*>(ws + p.off_items);
+    sa.counters = reinterpret_cast<int32_t*>(ws);
+    if (launch_sched(sa, s) != hipSuccess) return JA_ERR_HIP;
+    *ba = BlkArgs{};
+    ba->off = offsets;
+    ba->items = sa.items;
+    ba->counters = sa.counters;
+    ba->B = B;
+    ba->H = H;
+    ba->T = (int32_t)T;
+    ba->causal = causal ? 1 : 0;
+    ba->bsh = bsh;
+    ba->cap = (int32_t)(p.max_pairs * H);
+    *grid = p.max_pairs * H;
+    return JA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -305,6 +369,25 @@ ja_status_t jagged_block_attn_fwd(const void* q, const void* k, const void* v, c
                     lse, workspace, workspace_bytes, stream);
 }
 
+size_t ja_block_attn_workspace_size(int32_t B, int32_t H, int32_t d, int64_t T, int32_t block, int32_t causal,
+                                    int32_t dtype) {
+    (void)causal;
+    if (block_shift(block) < 0) return 0;
+    if (check_common(B, H, d, T, T, JA_ACT_SOFTMAX, 0, 1.0f, dtype) != JA_OK) return 0;
+    size_t bytes = 0;
+    FwdPlan fp;
+    if (plan_fwd(B, H, d, T, JA_ACT_SOFTMAX, dtype, &fp) != JA_OK) return 0;
+    bytes = fp.bytes;
+    if (bwd_supported(dtype, d, JA_ACT_SOFTMAX)) {
+        BwdPlan bp;
+        if (plan_bwd(B, H, T, T, &bp) != JA_OK) return 0;
+        bytes = bp.bytes > bytes ? bp.bytes : bytes;
+    }
+    BlkPlan kp;
+    if (plan_blk(B, H, T, &kp) != JA_OK) return 0;
+    return kp.bytes > bytes ? kp.bytes : bytes;
+}
+
 size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
                              int32_t causal, int32_t window, int32_t dtype) {
     (void)causal;
@@ -330,8 +413,36 @@ ja_status_t jagged_block_attn_bwd(const void* q, const void* k, const void* v, c
                                   void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
     const int bsh = block_shift(block);
     if (bsh < 0) return JA_ERR_INVALID_ARG;
-    return bwd_impl(q, k, v, out, dout, lse, offsets, offsets, B, H, d, T, T, JA_ACT_SOFTMAX, causal, 0, bsh, scale,
-                    dtype, dq, dk, dv, workspace, workspace_bytes, stream);
+    if (!blk_supported(dtype, d, bsh))
+        return bwd_impl(q, k, v, out, dout, lse, offsets, offsets, B, H, d, T, T, JA_ACT_SOFTMAX, causal, 0, bsh,
+                        scale, dtype, dq, dk, dv, workspace, workspace_bytes, stream);
+    ja_status_t st = check_common(B, H, d, T, T, JA_ACT_SOFTMAX, 0, scale, dtype);
+    if (st != JA_OK) return st;
+    if (B == 0 || T == 0) return JA_OK;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || !offsets || !workspace) return JA_ERR_INVALID_ARG;
+    const void* ptrs16[] = {q, k, v, dout, dq, dk, dv, workspace};
+    for (const void* p16 : ptrs16)
+        if (!aligned(p16, 16)) return JA_ERR_INVALID_ARG;
+    if (!aligned(offsets, 4)) return JA_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    BlkArgs ba;
+    int64_t grid = 0;
+    st = blk_schedule(offsets, B, H, T, causal, bsh, workspace, workspace_bytes, s, &ba, &grid);
+    if (st != JA_OK) return st;
+    ba.q = q;
+    ba.k = k;
+    ba.v = v;
+    ba.dout = dout;
+    ba.dq = dq;
+    ba.dk = dk;
+    ba.dv = dv;
+    ba.scale = scale;
+    if (g_prof_before && hipEventRecord(g_prof_before, s) != hipSuccess) return JA_ERR_HIP;
+    const int64_t cap_bwd = (int64_t)device_cus() * blk_occupancy_cached(d);
+    if (grid > cap_bwd) grid = cap_bwd;
+    if (launch_blk_bwd(ba, d, (int)grid, s) != hipSuccess) return JA_ERR_HIP;
+    if (g_prof_after && hipEventRecord(g_prof_after, s) != hipSuccess) return JA_ERR_HIP;
+    return JA_OK;
 }
 
 ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets, int32_t B, int32_t H, int32_t d,

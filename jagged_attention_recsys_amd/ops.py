@@ -133,12 +133,17 @@ def jagged_attn_bwd(q, k, v, out, dout, lse, q_offsets, k_offsets, act="softmax"
     return dq, dk, dv
 
 
+def block_attn_workspace_size(B, H, d, T, block, causal=False, dtype=torch.bfloat16) -> int:
+    return int(_lib.load().ja_block_attn_workspace_size(B, H, d, T, int(block), int(bool(causal)), DTYPE[dtype]))
+
+
 def jagged_block_attn_fwd(q, k, v, offsets, block, causal=False, scale=None, out=None, lse=None,
-                          workspace=None, stream=None):
+                          workspace=None, stream=None, return_lse=True):
     """Block-diagonal self-attention forward (softmax): each block of ``block`` tokens
     of a sequence attends only within itself. q, k, v: [T,H,d]; offsets: int32 [B+1].
 
-    Returns (out [T,H,d], lse [T,H] float32)."""
+    Returns (out [T,H,d], lse [T,H] float32, or None with return_lse=False and no
+    ``lse`` given)."""
     lib = _lib.load()
     _check_tensor("q", q, dim=3)
     dtype = q.dtype
@@ -157,9 +162,9 @@ def jagged_block_attn_fwd(q, k, v, offsets, block, causal=False, scale=None, out
         out = torch.empty_like(q)
     else:
         _check_tensor("out", out, dtype)
-    if lse is None:
+    if lse is None and return_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    ws_bytes = int(lib.ja_fwd_workspace_size(B, H, d, T, T, 0, int(bool(causal)), 0, DTYPE[dtype]))
+    ws_bytes = block_attn_workspace_size(B, H, d, T, block, causal, dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
     status = lib.jagged_block_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, d, T, int(block),
@@ -171,7 +176,10 @@ def jagged_block_attn_fwd(q, k, v, offsets, block, causal=False, scale=None, out
 
 def jagged_block_attn_bwd(q, k, v, out, dout, lse, offsets, block, causal=False, scale=None, dq=None, dk=None,
                           dv=None, workspace=None, stream=None):
-    """Backward of jagged_block_attn_fwd. Returns (dq, dk, dv)."""
+    """Backward of jagged_block_attn_fwd. Returns (dq, dk, dv).
+
+    For bf16 blocks of at most 64 tokens ``out`` and ``lse`` are not read (None is
+    fine); larger blocks need the forward's."""
     lib = _lib.load()
     _check_tensor("q", q, dim=3)
     dtype = q.dtype
@@ -188,7 +196,7 @@ def jagged_block_attn_bwd(q, k, v, out, dout, lse, offsets, block, causal=False,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    ws_bytes = int(lib.ja_bwd_workspace_size(B, H, d, T, T, 0, int(bool(causal)), 0, DTYPE[dtype]))
+    ws_bytes = block_attn_workspace_size(B, H, d, T, block, causal, dtype)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
     status = lib.jagged_block_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),

@@ -4,12 +4,15 @@ keys and values of its own block) against the fp64 oracle.
 
 The HIP forward (jagged_block_attn_fwd) and backward (jagged_block_attn_bwd) run
 through the C ABI; the oracle's fwd / bwd with the same block size are the
-reference. Cases: ragged batches whose lengths are not multiples of the block
-(short last blocks) and span several tiles, block sizes below, at and above the
-forward's 128-row tile, causal and not, d in {32, 64, 128}, fp32 and bf16; many
-short sequences (the split layout); the full block workload on sampled
-(sequence, head) pairs; a block at least as long as every sequence, which must
-give bit for bit the result of the unmasked entry points; and argument errors.
+reference. The forward always runs the general forward kernel under the block
+mask; the bf16 backward of blocks of at most 64 tokens runs the fused per-tile
+kernel (no lse, no Di pass), larger blocks the general two-pass backward. Cases: ragged batches whose lengths are not
+multiples of the block (short last blocks) and span several tiles, blocks of 1
+to 256 tokens, causal and not, d in {32, 64, 128}, fp32 and bf16; many short
+sequences; the full block workload on sampled (sequence, head) pairs; the
+dedicated backward ignoring out and lse; a block at least as long as every
+sequence, which must give bit for bit the result of the unmasked entry points;
+and argument errors.
 bf16 results are held to the non-strict bound (absolute 2e-2 plus 2^-8 relative,
 and the mean bound): under a causal block mask the first query of every block
 sees only its own key (P = 1), so dV of that key carries a whole dO row, and with
@@ -91,7 +94,7 @@ def case(lengths, H=2, d=64, dtype=W.BF16, seed=0):
 
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("block", [32, 64, 256])
+@pytest.mark.parametrize("block", [32, 64, 128, 256])
 def test_ragged_block_fwd_bwd(d, causal, block):
     check(case(RAGGED, d=d, seed=600 + d + block + causal), block, causal, what="ragged")
 
@@ -145,14 +148,29 @@ def test_block_longer_than_every_sequence_is_plain_attention(causal):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_backward_needs_no_lse(d):
+    w = case([200, 64, 7, 130], H=2, d=d, seed=980 + d)
+    q, k, v, off, do = to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.q_offsets), to_dev(w.dout)
+    out, lse = ja.jagged_block_attn_fwd(q, k, v, off, 64, causal=True)
+    out2, none = ja.jagged_block_attn_fwd(q, k, v, off, 64, causal=True, return_lse=False)
+    assert none is None
+    a = ja.jagged_block_attn_bwd(q, k, v, out, do, lse, off, 64, causal=True)
+    b = ja.jagged_block_attn_bwd(q, k, v, None, do, None, off, 64, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 def test_rejects_bad_block():
     w = case([10, 20], d=64, seed=990)
     q, k, v, off = to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.q_offsets)
     for block in (0, -64, 48, 3):
         with pytest.raises(RuntimeError):
             ja.jagged_block_attn_fwd(q, k, v, off, block)
-    out, lse = ja.jagged_block_attn_fwd(q, k, v, off, 64)
+    out, lse = ja.jagged_block_attn_fwd(q, k, v, off, 128)
     with pytest.raises(RuntimeError):
         ja.jagged_block_attn_bwd(q, k, v, out, q, lse, off, 96)
-    with pytest.raises(RuntimeError):  # needs the forward's out and lse
-        ja.jagged_block_attn_bwd(q, k, v, None, q, None, off, 64)
+    with pytest.raises(RuntimeError):  # blocks above 64 tokens need the forward's out and lse
+        ja.jagged_block_attn_bwd(q, k, v, None, q, None, off, 128)
