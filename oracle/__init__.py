@@ -25,9 +25,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ja_oracle.c")
 _LIB = os.path.join(_HERE, "libja_oracle.so")
 
-SOFTMAX, SILU, GELU_TANH = 0, 1, 2
+SOFTMAX, SILU, GELU_TANH, GELU_TAYLOR = 0, 1, 2, 3
 _DT_F32, _DT_BF16, _DT_F64 = 0, 1, 2
-ACTS = {"softmax": SOFTMAX, "silu": SILU, "gelu": GELU_TANH, "gelu_tanh": GELU_TANH}
+ACTS = {"softmax": SOFTMAX, "silu": SILU, "gelu": GELU_TANH, "gelu_tanh": GELU_TANH, "gelu_taylor": GELU_TAYLOR}
 
 _lib = None
 

@@ -52,12 +52,44 @@ static double dact_gelu_tanh(double x) {
     return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * du;
 }
 
+/* GDPA section, ALU-only activation: GELU replaced by its Taylor expansion of
+ * order 6 about 0, for inputs kept small by QK-norm. With c = sqrt(2/pi),
+ * a = 0.044715 and u = c (x + a x^3):
+ *   tanh u = c x + (c a - c^3/3) x^3 + (2 c^5/15 - c^3 a) x^5 + O(x^7),
+ * so 0.5 x (1 + tanh u) = x/2 + k2 x^2 + k4 x^4 + k6 x^6 + O(x^8) with
+ *   k2 = c/2, k4 = (c a - c^3/3)/2, k6 = (2 c^5/15 - c^3 a)/2. */
+static void gelu_taylor_coeffs(double* k2, double* k4, double* k6) {
+    const double c = sqrt(2.0 / M_PI), a = 0.044715;
+    const double c3 = c * c * c, c5 = c3 * c * c;
+    *k2 = c / 2.0;
+    *k4 = (c * a - c3 / 3.0) / 2.0;
+    *k6 = (2.0 * c5 / 15.0 - c3 * a) / 2.0;
+}
+
+static double act_gelu_taylor(double x) {
+    double k2, k4, k6;
+    gelu_taylor_coeffs(&k2, &k4, &k6);
+    const double x2 = x * x;
+    return 0.5 * x + k2 * x2 + k4 * x2 * x2 + k6 * x2 * x2 * x2;
+}
+
+static double dact_gelu_taylor(double x) {
+    double k2, k4, k6;
+    gelu_taylor_coeffs(&k2, &k4, &k6);
+    const double x2 = x * x;
+    return 0.5 + 2.0 * k2 * x + 4.0 * k4 * x2 * x + 6.0 * k6 * x2 * x2 * x;
+}
+
 static double act_apply(int act, double x) {
-    return act == ORA_SILU ? act_silu(x) : act_gelu_tanh(x);
+    if (act == ORA_SILU) return act_silu(x);
+    if (act == ORA_GELU_TAYLOR) return act_gelu_taylor(x);
+    return act_gelu_tanh(x);
 }
 
 static double act_deriv(int act, double x) {
-    return act == ORA_SILU ? dact_silu(x) : dact_gelu_tanh(x);
+    if (act == ORA_SILU) return dact_silu(x);
+    if (act == ORA_GELU_TAYLOR) return dact_gelu_taylor(x);
+    return dact_gelu_tanh(x);
 }
 
 /* ---- visibility ----------------------------------------------------------
@@ -303,7 +335,7 @@ static int run(job_t* J, int nthreads) {
 static int check_common(const int32_t* q_off, const int32_t* k_off, int32_t B, int32_t H,
                         int32_t d, int act, int32_t window) {
     if (!q_off || !k_off || B < 0 || H < 1 || d < 1 || window < 0) return -1;
-    if (act != ORA_SOFTMAX && act != ORA_SILU && act != ORA_GELU_TANH) return -1;
+    if (act != ORA_SOFTMAX && act != ORA_SILU && act != ORA_GELU_TANH && act != ORA_GELU_TAYLOR) return -1;
     if (q_off[0] != 0 || k_off[0] != 0) return -1;
     for (int32_t b = 0; b < B; ++b)
         if (q_off[b + 1] < q_off[b] || k_off[b + 1] < k_off[b]) return -1;

@@ -24,6 +24,10 @@
  *   - the pointwise activations are normalised by 1/Lk_b, Lk_b being the key
  *     count of the sequence;
  *   - GELU is the tanh form (the pages name GELU's tanh);
+ *   - the ALU-only GELU of the same section (ORA_GELU_TAYLOR) is the Taylor
+ *     polynomial of that tanh form about 0 through x^6 (the pages' "6th-order
+ *     Taylor expansion"), used where QK-norm keeps |scale q.k| small: it is
+ *     within 1.2e-3 of the tanh form for |x| <= 1;
  *   - causal is top-left aligned: key j is visible to query i iff j <= i;
  *   - a window W > 0 keeps W keys including the query's own position:
  *     causal: 0 <= i - j < W; non-causal: |i - j| < W; W == 0 means no window;
@@ -45,7 +49,7 @@ extern "C" {
 #endif
 
 enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_F64 = 2 };
-enum { ORA_SOFTMAX = 0, ORA_SILU = 1, ORA_GELU_TANH = 2 };
+enum { ORA_SOFTMAX = 0, ORA_SILU = 1, ORA_GELU_TANH = 2, ORA_GELU_TAYLOR = 3 };
 
 /* Forward. q: [Tq,H,d], k/v: [Tk,H,d] token-major, element type `dtype`
  * (bf16 given as raw uint16 bits). Offsets: [B+1], non-decreasing from 0.
@@ -60,7 +64,7 @@ int ora_fwd(const void* q, const void* k, const void* v, int dtype,
             const uint8_t* pair_mask, double* out, double* lse, int nthreads);
 
 /* Backward of the softmax forward (act must be ORA_SOFTMAX) or of the
- * normalised pointwise forward (ORA_SILU / ORA_GELU_TANH). The oracle
+ * normalised pointwise forward (ORA_SILU / ORA_GELU_TANH / ORA_GELU_TAYLOR). The oracle
  * recomputes its own O and LSE. dout: [Tq,H,d] in `dtype`. Writes out, lse
  * (may be NULL), dq [Tq,H,d], dk and dv [Tk,H,d] for the selected pairs. */
 int ora_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,

@@ -269,6 +269,49 @@ def test_gelu_tanh_close_to_erf_gelu():
     assert np.max(np.abs(np.array(out) - exact)) < 5e-4
 
 
+def _act_values(act, s):
+    """act(s_j) for scores s (len(s) <= 64) read back through the oracle: one query
+    e1, keys s_j sqrt(d) e1 (so scale q.k_j = s_j), values Lk e_j."""
+    s = np.asarray(s, dtype=np.float64)
+    n, d = len(s), 64
+    w = W.make_case([1], [n], H=1, d=d, dtype=W.F64, seed=2)
+    w.q[:] = 0
+    w.q[0, 0, 0] = 1
+    w.k[:] = 0
+    w.k[:, 0, 0] = s * math.sqrt(d)
+    w.v[:] = 0
+    w.v[np.arange(n), 0, np.arange(n)] = n
+    out, _ = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, act)
+    return out[0, 0, :n]
+
+
+def test_gelu_taylor_is_the_order_6_series_of_tanh_gelu():
+    """The ALU-only GELU equals the Taylor series of the tanh form through x^6,
+    derived here symbolically by a library (sympy), to rounding."""
+    sympy = pytest.importorskip("sympy")
+    x = sympy.symbols("x")
+    c = sympy.sqrt(2 / sympy.pi)
+    series = sympy.series(sympy.Rational(1, 2) * x * (1 + sympy.tanh(c * (x + sympy.Rational(44715, 10**6) * x**3))),
+                          x, 0, 7).removeO()
+    f = sympy.lambdify(x, series, "numpy")
+    s = np.linspace(-2.0, 2.0, 41)
+    got = _act_values("gelu_taylor", s)
+    np.testing.assert_allclose(got, f(s), rtol=1e-13, atol=1e-15)
+
+
+def test_gelu_taylor_error_is_order_8_and_bounded():
+    """Against the library's tanh GELU: the error shrinks like x^8 near 0 (a wrong
+    x^4 or x^6 coefficient would leave x^4 or x^6), and stays within 1.2e-3 on the
+    QK-norm range |x| <= 1."""
+    s = np.array([0.1, 0.2, -0.1, -0.2])
+    err = np.abs(_act_values("gelu_taylor", s) - F.gelu(torch.tensor(s), approximate="tanh").numpy())
+    for a, b in ((err[0], err[1]), (err[2], err[3])):
+        assert 0.9 * 2.0 ** 8 <= b / a <= 1.1 * 2.0 ** 8
+    s = np.linspace(-1.0, 1.0, 64)
+    err = np.abs(_act_values("gelu_taylor", s) - F.gelu(torch.tensor(s), approximate="tanh").numpy())
+    assert 1.0e-3 < err.max() <= 1.2e-3
+
+
 @pytest.mark.parametrize("act,causal,window", [("softmax", False, 0), ("softmax", True, 5),
                                                ("silu", False, 0), ("gelu", True, 0)])
 def test_sequence_permutation_is_bitwise_invariant(act, causal, window):
@@ -341,7 +384,8 @@ def _f(w, dout, act, causal, window, q, k, v):
 
 
 @pytest.mark.parametrize("act,causal,window", [("softmax", True, 2), ("softmax", False, 0),
-                                               ("silu", False, 0), ("gelu", True, 0)])
+                                               ("silu", False, 0), ("gelu", True, 0), ("gelu_taylor", False, 0),
+                                               ("gelu_taylor", True, 2)])
 def test_backward_central_differences(act, causal, window):
     w = W.make_case([4, 3], [5, 3], H=1, d=4, dtype=W.F32, seed=21)
     q, k, v = (w.q.astype(np.float64), w.k.astype(np.float64), w.v.astype(np.float64))
