@@ -6,8 +6,9 @@ kernel) over the whole synthetic batch, inputs already resident in HBM. The defa
 workload is the jagged causal softmax self-attention batch (B=64, lengths
 log-uniform in [128, 4096], H=4, d=128, bf16). ``--workload 3|4|5|6`` measures the
 other named batches (6: 64-token block-diagonal attention through
-``jagged_block_attn_fwd``); ``--bwd`` adds the backward (softmax for 2, 5 and 6,
-the pointwise SiLU / GELU backward for 3 and 4).
+``jagged_block_attn_fwd``; 7: QK-normed self-attention with the ALU-only GELU);
+``--bwd`` adds the backward (softmax for 2, 5 and 6, the pointwise SiLU / GELU
+backward for 3, 4 and 7); ``--act`` swaps the activation.
 
 Reported:
   value        useful (unpadded) TFLOP/s of the whole step: 4 d H sum_b pairs_b per
@@ -109,9 +110,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
     ap.add_argument("--bwd", action="store_true",
-                    help="time forward + backward (softmax for 2, 5 and 6, SiLU / GELU for 3 and 4)")
+                    help="time forward + backward (softmax for 2, 5 and 6, SiLU / GELU for 3, 4 and 7)")
+    ap.add_argument("--act", choices=["softmax", "silu", "gelu", "gelu_taylor"], default=None,
+                    help="run the workload with another activation (e.g. 7 with the tanh GELU)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -147,7 +150,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
 
     log(f"[bench] generating workload {args.workload}")
-    w = W.workload(args.workload)
+    w = W.workload(args.workload, act=args.act)
     if args.bwd and w.dout is None:
         W.with_upstream_gradient(w, 1000 + args.workload)  # seeded dO for the batches that draw none
 
@@ -266,6 +269,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.extra.get("description", w.name), "B": w.B, "H": w.H, "d": w.d,
                    "act": w.act, "causal": bool(w.causal), "window": int(w.window), "block": int(w.block),
+                   "scale": round(w.scale, 6),
                    "q_tokens": int(Tq),
                    "kv_tokens": int(Tk), "visible_pairs": int(pairs), "fwd_flop": fwd_flop,
                    "bwd_flop": bwd_flop, "phases": "fwd+bwd" if args.bwd else "fwd"},

@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
     JA_OK = 0,
     JA_ERR_INVALID_ARG = 1,     /* null pointer, bad size, window < 0, scale not finite, misalignment */
-    JA_ERR_UNSUPPORTED = 2,     /* d not in {32, 64, 128}, unknown dtype/act, bwd of an unsupported act */
+    JA_ERR_UNSUPPORTED = 2,     /* d not in {32, 64, 128}, unknown dtype/act, bwd of fp32 */
     JA_ERR_WORKSPACE = 3,       /* workspace smaller than the matching *_workspace_size() */
     JA_ERR_INVALID_OFFSETS = 4, /* ja_validate_offsets found malformed offsets */
     JA_ERR_HIP = 5              /* a HIP runtime call or kernel launch failed */
@@ -72,7 +72,14 @@ typedef enum {
 typedef enum {
     JA_ACT_SOFTMAX = 0,  /* online softmax over the visible keys (JFA) */
     JA_ACT_SILU = 1,     /* x*sigmoid(x), times 1/Lk_b (GDPA) */
-    JA_ACT_GELU_TANH = 2 /* tanh-form GELU, times 1/Lk_b (GDPA) */
+    JA_ACT_GELU_TANH = 2,  /* tanh-form GELU, times 1/Lk_b (GDPA) */
+    JA_ACT_GELU_TAYLOR = 3 /* ALU-only GELU, times 1/Lk_b (GDPA): the Taylor polynomial of the tanh
+                              form about 0 through x^6, x/2 + k2 x^2 + k4 x^4 + k6 x^6 with
+                              c = sqrt(2/pi): k2 = c/2, k4 = (0.044715 c - c^3/3)/2,
+                              k6 = (2 c^5/15 - 0.044715 c^3)/2; no transcendental instruction.
+                              Within 1.2e-3 of JA_ACT_GELU_TANH for |scale q.k| <= 1, the range
+                              unit-norm (QK-normed) queries and keys give with scale <= 1;
+                              diverges from it beyond about |x| = 1.5. */
 } ja_act_t;
 
 typedef enum {
@@ -113,7 +120,7 @@ size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_
  * row from a key-stationary pass; no atomics on any gradient.
  *   act == JA_ACT_SOFTMAX: needs the forward's out and lse (same scale); Di =
  *     rowsum(dO * O) is computed inside the dQ pass into the workspace.
- *   act == JA_ACT_SILU / JA_ACT_GELU_TANH: with Z = scale Q K^T, P = act(Z)/Lk
+ *   act == JA_ACT_SILU / _GELU_TANH / _GELU_TAYLOR: with Z = scale Q K^T, P = act(Z)/Lk
  *     and dS = act'(Z) * (dO V^T) / Lk; out and lse are not read and may be
  *     NULL.
  *   dout [Tq,H,d]: upstream gradient; dq [Tq,H,d], dk/dv [Tk,H,d]: outputs,

@@ -116,7 +116,7 @@ int device_cus() {
 }
 
 int fwd_occupancy(int dtype, int d, int act, bool split) {
-    static std::atomic<int> cache[2][3][3][2];
+    static std::atomic<int> cache[2][3][4][2];
     const int di = d == 32 ? 0 : d == 64 ? 1 : 2;
     std::atomic<int>& slot = cache[dtype][di][act][split ? 1 : 0];
     int n = slot.load(std::memory_order_relaxed);

@@ -455,7 +455,7 @@ int occupancy_d(bool dkdv) {
 }  // namespace
 
 bool bwd_supported(int dtype, int d, int act) {
-    return dtype == 1 && (d == 32 || d == 64 || d == 128) && act >= ACT_SOFTMAX && act <= ACT_GELU;
+    return dtype == 1 && (d == 32 || d == 64 || d == 128) && act >= ACT_SOFTMAX && act <= ACT_GELU_TAYLOR;
 }
 
 int bwd_rows_per_item() { return kBwdRows; }
@@ -488,6 +488,7 @@ hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, 
         case ACT_SOFTMAX: return launch_a<ACT_SOFTMAX>(a, d, grid_q, grid_k, stream, before, after);
         case ACT_SILU: return launch_a<ACT_SILU>(a, d, grid_q, grid_k, stream, before, after);
         case ACT_GELU: return launch_a<ACT_GELU>(a, d, grid_q, grid_k, stream, before, after);
+        case ACT_GELU_TAYLOR: return launch_a<ACT_GELU_TAYLOR>(a, d, grid_q, grid_k, stream, before, after);
         default: return hipErrorInvalidValue;
     }
 }
@@ -497,6 +498,7 @@ int bwd_blocks_per_cu(int d, int act, bool dkdv) {
         case ACT_SOFTMAX: return occupancy_a<ACT_SOFTMAX>(d, dkdv);
         case ACT_SILU: return occupancy_a<ACT_SILU>(d, dkdv);
         case ACT_GELU: return occupancy_a<ACT_GELU>(d, dkdv);
+        case ACT_GELU_TAYLOR: return occupancy_a<ACT_GELU_TAYLOR>(d, dkdv);
         default: return 1;
     }
 }

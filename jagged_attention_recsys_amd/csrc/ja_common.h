@@ -73,10 +73,24 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 
 // Pointwise activations in the GDPA form: x * sigmoid(z), with z = x for SiLU and
 // z = 2 sqrt(2/pi) (x + 0.044715 x^3) for tanh-GELU (0.5 (1 + tanh u) = sigmoid(2u)).
-enum { ACT_SOFTMAX = 0, ACT_SILU = 1, ACT_GELU = 2 };
+// ACT_GELU_TAYLOR is the ALU-only GELU of the same section: the Taylor
+// polynomial of the tanh form about 0 through x^6, x/2 + k2 x^2 + k4 x^4 + k6 x^6
+// with c = sqrt(2/pi), a = 0.044715: k2 = c/2, k4 = (c a - c^3/3)/2,
+// k6 = (2 c^5/15 - c^3 a)/2. No transcendental instruction; meant for inputs
+// that QK-norm keeps small (within 1.2e-3 of the tanh form for |x| <= 1).
+enum { ACT_SOFTMAX = 0, ACT_SILU = 1, ACT_GELU = 2, ACT_GELU_TAYLOR = 3 };
+
+constexpr float kGeluK2 = 0.398942280401432678f;
+constexpr float kGeluK4 = -0.0668194771775045642f;
+constexpr float kGeluK6 = 0.0102015571062664970f;
 
 template <int ACT>
 __device__ __forceinline__ float pointwise(float x) {
+    if (ACT == ACT_GELU_TAYLOR) {
+        const float t = x * x;
+        const float u = fmaf(fmaf(kGeluK6, t, kGeluK4), t, kGeluK2);
+        return fmaf(t, u, 0.5f * x);
+    }
     float z;
     if (ACT == ACT_SILU) {
         z = x;
@@ -94,6 +108,12 @@ __device__ __forceinline__ float pointwise(float x) {
 // exactly 0 or 1 and both results stay finite.
 template <int ACT>
 __device__ __forceinline__ void pointwise_grad(float x, float& a, float& da) {
+    if (ACT == ACT_GELU_TAYLOR) {
+        const float t = x * x;
+        a = fmaf(t, fmaf(fmaf(kGeluK6, t, kGeluK4), t, kGeluK2), 0.5f * x);
+        da = fmaf(x, fmaf(fmaf(6.0f * kGeluK6, t, 4.0f * kGeluK4), t, 2.0f * kGeluK2), 0.5f);
+        return;
+    }
     float w, dw;
     if (ACT == ACT_SILU) {
         w = x;

@@ -383,6 +383,7 @@ R dispatch(int dtype, int d, int act, bool split, R fail, Args... args) {
         case ACT_SOFTMAX: return F<T, D, ACT_SOFTMAX, S>::call(args...); \
         case ACT_SILU: return F<T, D, ACT_SILU, S>::call(args...);       \
         case ACT_GELU: return F<T, D, ACT_GELU, S>::call(args...);       \
+        case ACT_GELU_TAYLOR: return F<T, D, ACT_GELU_TAYLOR, S>::call(args...); \
         default: return fail;                                            \
     }
 #define JA_DIMS(T, S)              \
@@ -418,7 +419,7 @@ struct ShapeF {
 }  // namespace
 
 bool fwd_supported(int dtype, int d, int act) {
-    return (dtype == 0 || dtype == 1) && (d == 32 || d == 64 || d == 128) && act >= 0 && act <= 2;
+    return (dtype == 0 || dtype == 1) && (d == 32 || d == 64 || d == 128) && act >= ACT_SOFTMAX && act <= ACT_GELU_TAYLOR;
 }
 
 FwdShape fwd_shape(int dtype, int d, int act, bool split) {

@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 
-ACT = {"softmax": 0, "silu": 1, "gelu": 2, "gelu_tanh": 2}
+ACT = {"softmax": 0, "silu": 1, "gelu": 2, "gelu_tanh": 2, "gelu_taylor": 3}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 

@@ -5,20 +5,21 @@ tensors, rounded to bf16 where a workload asks for it. It holds none of the
 attention arithmetic, so both the HIP path (through its tests and benchmark) and
 the fp64 oracle can be fed from the same bytes.
 
-The six workloads follow the shapes the engineering post "GEM Training: How Meta
+The seven workloads follow the shapes the engineering post "GEM Training: How Meta
 Doubled the Efficiency of Its LLM-Scale Ads Foundation Model" describes in its
 "Challenge 1" section (jagged user histories from hundreds to tens of thousands of
 tokens; self-attention, cross-attention with long queries and short key/value,
 pooled multi-head attention with short queries and long key/value) and in its
 "BlockAttention" section (sliding window over long histories, then fixed 64-token
-blocks that attend only within themselves). The pages give no
-sizes; the sizes below are this library's synthetic stand-ins for the production
-traffic they describe.
+blocks that attend only within themselves), and the GDPA section's ALU-only GELU
+on inputs bounded by QK-norm. The pages give no sizes; the sizes below are this
+library's synthetic stand-ins for the production traffic they describe.
 
 Recipe (one ``numpy.random.default_rng(seed)`` stream per workload, seed = its
 number): lengths first, then Q, K, V and dO, each one ``standard_normal(float32)``
 draw of shape [T, H, d] (drawn in row chunks, which consumes the stream exactly as
-one call would), then round-to-nearest-even to bf16 for the bf16 workloads.
+one call would), for QK-normed batches each Q and K row (token, head) divided by
+its L2 norm, then round-to-nearest-even to bf16 for the bf16 workloads.
 """
 from __future__ import annotations
 
@@ -51,6 +52,7 @@ class Workload:
     window: int = 0
     dout: np.ndarray | None = None
     block: int = 0  # > 0: block-diagonal mask of this many tokens (self-attention only)
+    attn_scale: float = 0.0  # > 0: the scale applied to Q K^T; 0: 1/sqrt(d)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -59,7 +61,7 @@ class Workload:
 
     @property
     def scale(self) -> float:
-        return float(1.0 / np.sqrt(self.d))
+        return float(self.attn_scale) if self.attn_scale > 0 else float(1.0 / np.sqrt(self.d))
 
     @property
     def lq(self) -> np.ndarray:
@@ -91,13 +93,17 @@ def offsets_from_lengths(lengths) -> np.ndarray:
     return off.astype(np.int32)
 
 
-def _normal(rng: np.random.Generator, T: int, H: int, d: int, dtype: str) -> np.ndarray:
-    """One [T,H,d] standard-normal float32 draw, converted chunk by chunk to bound memory."""
+def _normal(rng: np.random.Generator, T: int, H: int, d: int, dtype: str, unit_rows: bool = False) -> np.ndarray:
+    """One [T,H,d] standard-normal float32 draw, converted chunk by chunk to bound memory.
+    unit_rows: each (token, head) row scaled to unit L2 norm before rounding (the
+    QK-norm stand-in); the draw itself is the same."""
     npdt = {BF16: np.uint16, F32: np.float32, F64: np.float64}[dtype]
     out = np.empty((T, H, d), dtype=npdt)
     for r0 in range(0, T, _CHUNK_ROWS):
         r1 = min(T, r0 + _CHUNK_ROWS)
         x = rng.standard_normal((r1 - r0, H, d), dtype=np.float32)
+        if unit_rows:
+            x = x / np.linalg.norm(x, axis=-1, keepdims=True)
         out[r0:r1] = f32_to_bf16_bits(x) if dtype == BF16 else x
     return out
 
@@ -112,7 +118,8 @@ def lognormal_lengths(rng: np.random.Generator, n: int, median: float, sigma: fl
 
 
 def make_case(lq, lk=None, H=1, d=32, dtype=BF16, seed=0, act="softmax", causal=False,
-              window=0, with_dout=False, shared_q_rows: int | None = None, name="case") -> Workload:
+              window=0, with_dout=False, shared_q_rows: int | None = None, name="case",
+              qk_norm: bool = False) -> Workload:
     """A generic seeded jagged batch with given per-sequence lengths.
 
     ``lk=None`` means self-attention (lk = lq). ``shared_q_rows=r`` draws one [r,H,d]
@@ -125,7 +132,7 @@ def make_case(lq, lk=None, H=1, d=32, dtype=BF16, seed=0, act="softmax", causal=
         lq_arr = np.full(lk_arr.shape[0], shared_q_rows, dtype=np.int64)
     else:
         lq_arr = np.asarray(lq, dtype=np.int64)
-    return _build(rng, name, lq_arr, lk_arr, H, d, dtype, act, causal, window, with_dout, shared_q_rows)
+    return _build(rng, name, lq_arr, lk_arr, H, d, dtype, act, causal, window, with_dout, shared_q_rows, qk_norm)
 
 
 def with_upstream_gradient(w: Workload, seed: int) -> Workload:
@@ -135,22 +142,22 @@ def with_upstream_gradient(w: Workload, seed: int) -> Workload:
     return w
 
 
-def _build(rng, name, lq, lk, H, d, dtype, act, causal, window, with_dout, shared_q_rows):
+def _build(rng, name, lq, lk, H, d, dtype, act, causal, window, with_dout, shared_q_rows, qk_norm=False):
     qo, ko = offsets_from_lengths(lq), offsets_from_lengths(lk)
     Tq, Tk = int(qo[-1]), int(ko[-1])
     if shared_q_rows is not None:
-        seeds = _normal(rng, shared_q_rows, H, d, dtype)
+        seeds = _normal(rng, shared_q_rows, H, d, dtype, qk_norm)
         q = np.tile(seeds, (lq.shape[0], 1, 1)) if lq.shape[0] > 0 else seeds[:0].copy()
     else:
-        q = _normal(rng, Tq, H, d, dtype)
-    k = _normal(rng, Tk, H, d, dtype)
+        q = _normal(rng, Tq, H, d, dtype, qk_norm)
+    k = _normal(rng, Tk, H, d, dtype, qk_norm)
     v = _normal(rng, Tk, H, d, dtype)
     dout = _normal(rng, Tq, H, d, dtype) if with_dout else None
     return Workload(name=name, q=q, k=k, v=v, q_offsets=qo, k_offsets=ko, H=H, d=d, dtype=dtype,
                     act=act, causal=causal, window=window, dout=dout)
 
 
-# --- the six named workloads ------------------------------------------------
+# --- the seven named workloads ------------------------------------------------
 
 WORKLOADS = {
     1: "tiny jagged softmax self-attention fwd, fp32: B=4 lengths {7,33,64,129}, H=2, d=32 "
@@ -165,11 +172,13 @@ WORKLOADS = {
        "(median 2048, sigma 1, cap 32768), window 1024, H=8, d=128",
     6: "jagged block-diagonal causal softmax self-attention fwd+bwd (BlockAttention), bf16: B=32, "
        "lengths lognormal (median 2048, sigma 1, cap 32768), blocks of 64 tokens, H=8, d=128",
+    7: "GDPA causal self-attention with the ALU-only GELU (order-6 Taylor), QK-normed (unit-norm) "
+       "queries and keys, scale 1, fwd+bwd, bf16: B=64, lengths log-uniform [128,4096], H=4, d=128",
 }
 
 
 def workload(n: int, act: str | None = None, seed: int | None = None) -> Workload:
-    """Build workload ``n`` (1..6) from its seed (default: n)."""
+    """Build workload ``n`` (1..7) from its seed (default: n)."""
     rng = np.random.default_rng(n if seed is None else seed)
     if n == 1:
         lq = np.array([7, 33, 64, 129], dtype=np.int64)
@@ -192,6 +201,10 @@ def workload(n: int, act: str | None = None, seed: int | None = None) -> Workloa
         lq = lognormal_lengths(rng, 32, 2048.0, 1.0, 32768)
         w = _build(rng, "w6", lq, lq, 8, 128, BF16, act or "softmax", True, 0, True, None)
         w.block = 64
+    elif n == 7:
+        lq = log_uniform_lengths(rng, 64, 128, 4096)
+        w = _build(rng, "w7", lq, lq, 4, 128, BF16, act or "gelu_taylor", True, 0, True, None, qk_norm=True)
+        w.attn_scale = 1.0
     else:
         raise ValueError(f"unknown workload {n}")
     w.extra["description"] = WORKLOADS[n]

@@ -83,6 +83,11 @@ def pointwise_term_sums(w, act, causal, window, pair_mask=None):
             if act == "silu":
                 sg = 1.0 / (1.0 + np.exp(-z))
                 a, da = z * sg, sg + z * sg * (1.0 - sg)
+            elif act == "gelu_taylor":  # only the scale of the terms matters here
+                c = np.sqrt(2.0 / np.pi)
+                k2, k4, k6 = c / 2, (c * 0.044715 - c ** 3 / 3) / 2, (2 * c ** 5 / 15 - c ** 3 * 0.044715) / 2
+                a = 0.5 * z + k2 * z ** 2 + k4 * z ** 4 + k6 * z ** 6
+                da = 0.5 + 2 * k2 * z + 4 * k4 * z ** 3 + 6 * k6 * z ** 5
             else:
                 c = np.sqrt(2.0 / np.pi)
                 t = np.tanh(c * (z + 0.044715 * z ** 3))

@@ -1,0 +1,108 @@
+"""GPU parity of the ALU-only GELU (order-6 Taylor polynomial of the tanh form;
+"Generalized Dot-Product Attention (GDPA)" section of the GEM training post)
+against the fp64 oracle, forward and backward.
+
+Inputs are QK-normed (unit-norm query and key rows) with scale 1, so every score
+lies in [-1, 1], the range on which the polynomial is meant to replace the tanh
+form. Cases: ragged self- and cross-attention batches (d 32 / 64 / 128, causal,
+windowed, fp32 and bf16 forward, bf16 backward), a batch whose scores reach
++-1 exactly (keys equal to or opposite their queries), the QK-normed workload on
+sampled (sequence, head) pairs, and the distance of the result to the exact tanh
+GELU on that range (at most the polynomial's 1.2e-3 error per weight).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from jagged_attention_recsys_amd import workloads as W
+from _parity import compare, rows_of_pairs, say, to_host64
+from test_gpu_bwd import check as check_bwd
+from test_gpu_fwd import check_against_oracle, run_fwd
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 7, 64, 65, 127, 128, 129, 300, 0, 263]
+
+
+def qk_case(lq, lk=None, H=2, d=64, dtype=W.BF16, seed=0):
+    w = W.make_case(lq, lk, H=H, d=d, dtype=dtype, seed=seed, with_dout=True, qk_norm=True)
+    w.attn_scale = 1.0
+    return w
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 37)])
+def test_ragged_fwd(d, causal, window):
+    for dtype in (W.F32, W.BF16):
+        w = qk_case(RAGGED, d=d, dtype=dtype, seed=1100 + d + window)
+        check_against_oracle(w, "gelu_taylor", causal, window, what="ragged", strict=dtype == W.BF16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_cross_fwd_bwd(d):
+    lq = [200, 1, 0, 77, 130, 129, 5]
+    lk = [64, 300, 5, 0, 1, 257, 140]
+    w = qk_case(lq, lk, H=3, d=d, seed=1200 + d)
+    check_against_oracle(w, "gelu_taylor", False, 0, what="cross", strict=True)
+    check_bwd(w, False, 0, what="cross", act="gelu_taylor")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 50)])
+def test_ragged_bwd(d, causal, window):
+    check_bwd(qk_case(RAGGED, d=d, seed=1300 + d + window), causal, window, what="ragged", act="gelu_taylor")
+
+
+def _extreme_scores(d, seed):
+    """Keys equal to (even tokens) or opposite (odd tokens) their own queries, so
+    the diagonal scores are +1 and -1 exactly, the ends of the range."""
+    w = qk_case([96, 33], H=2, d=d, seed=seed)
+    bits = w.q.copy()
+    bits[1::2] ^= np.uint16(0x8000)  # negate odd rows
+    w.k[:] = bits
+    return w
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_scores_at_the_ends_of_the_range(d):
+    w = _extreme_scores(d, 1400 + d)
+    check_against_oracle(w, "gelu_taylor", True, 0, what="extreme", strict=True)
+    check_bwd(w, True, 0, what="extreme", act="gelu_taylor")
+
+
+def test_close_to_tanh_gelu_on_the_qknorm_range():
+    """|out_taylor - out_tanh| <= 1.2e-3 sum_j |v_j| / Lk per element (the
+    polynomial's error bound on [-1, 1]), plus the bf16 bound, for the kernel's
+    result against the oracle's exact tanh GELU."""
+    w = _extreme_scores(128, 1500)
+    out, _ = run_fwd(w, "gelu_taylor", True, 0)
+    ref, _ = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, "gelu", True, 0, w.scale)
+    v = W.bf16_bits_to_f32(w.v).astype(np.float64)
+    bound = np.zeros_like(ref)
+    for b in range(w.B):
+        k0, k1 = int(w.k_offsets[b]), int(w.k_offsets[b + 1])
+        q0, q1 = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+        lk = k1 - k0
+        # causal: row i averages over keys 0..i with weight 1/Lk each
+        cum = np.cumsum(np.abs(v[k0:k1]), axis=0)
+        bound[q0:q1] = 1.2e-3 * cum[: q1 - q0] / lk
+    err = np.abs(to_host64(out) - ref)
+    assert np.all(err <= bound + 2e-2 + 2.0 ** -8 * np.abs(ref))
+    say(f"      max |taylor - tanh| = {err.max():.3e}")
+
+
+def _sample(w, n, seed):
+    rng = np.random.default_rng(seed)
+    mask = np.zeros((w.B, w.H), dtype=bool)
+    mask[int(np.argmax(w.lq)), 0] = True
+    mask[int(np.argmin(w.lq)), w.H - 1] = True
+    while mask.sum() < n:
+        mask[int(rng.integers(w.B)), int(rng.integers(w.H))] = True
+    return mask
+
+
+def test_workload7_fwd_bwd_sampled():
+    w = W.workload(7)
+    mask = _sample(w, 6, 7)
+    check_against_oracle(w, w.act, w.causal, w.window, pair_mask=mask, what="w7", strict=True)
+    check_bwd(w, w.causal, w.window, pair_mask=mask, what="w7", strict=True, act=w.act)
