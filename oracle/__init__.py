@@ -62,6 +62,15 @@ def _load():
         lib.ora_tile_list_block.argtypes = [i32p, i32p, i32, i32, i32, ctypes.c_int, i32, i32,
                                             ctypes.c_int, i32, i32p, i32p, i64]
         lib.ora_tile_list_block.restype = ctypes.c_int64
+        lib.ora_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.ora_e4m3_decode.restype = f64
+        lib.ora_e4m3_encode.argtypes = [f64]
+        lib.ora_e4m3_encode.restype = ctypes.c_uint8
+        lib.ora_mxfp8_quantize.argtypes = [vp, ctypes.c_int, i32p, i32, i32, i32, u8p, u8p, i32p]
+        lib.ora_mxfp8_quantize.restype = ctypes.c_int
+        lib.ora_fwd_mxfp8.argtypes = [u8p, u8p, i32p, u8p, u8p, i32p, u8p, u8p, i32p, i32p, i32, i32, i32,
+                                      ctypes.c_int, i32, f64, ctypes.c_int, u8p, f64p, f64p, ctypes.c_int]
+        lib.ora_fwd_mxfp8.restype = ctypes.c_int
         lib.ora_num_threads.argtypes = []
         lib.ora_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -152,6 +161,62 @@ def bwd(q, k, v, dout, q_offsets, k_offsets, act="softmax", causal=False, window
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out, lse, dq, dk, dv
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 codes (ties to even) of values in [-448, 448]."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([lib.ora_e4m3_encode(float(v)) for v in x.reshape(-1)], dtype=np.uint8).reshape(x.shape)
+
+
+def e4m3_decode(b) -> np.ndarray:
+    lib = _load()
+    b = np.asarray(b, dtype=np.uint8)
+    return np.array([lib.ora_e4m3_decode(int(v)) for v in b.reshape(-1)], dtype=np.float64).reshape(b.shape)
+
+
+def mxfp8_quantize(x, offsets, block_rows: int = 32):
+    """MXFP8 with [32, 32] blocks per sequence and head: returns (x8 [T,H,d] uint8 E4M3
+    codes, scales [NB,H,d/32] uint8 E8M0, soff [B+1] int32 first block of each sequence)."""
+    assert block_rows == 32
+    lib = _load()
+    x, dt = _as_input(x)
+    off = _offsets(offsets)
+    B = off.shape[0] - 1
+    T, H, d = x.shape
+    soff = np.zeros(B + 1, dtype=np.int32)
+    nb = int(np.sum((np.diff(off.astype(np.int64)) + 31) // 32))
+    x8 = np.zeros((T, H, d), dtype=np.uint8)
+    scales = np.zeros((max(nb, 1), H, d // 32), dtype=np.uint8)
+    rc = lib.ora_mxfp8_quantize(_ptr(x), dt, _ptr(off), B, H, d, _ptr(x8), _ptr(scales), _ptr(soff))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return x8, scales[:nb], soff
+
+
+def fwd_mxfp8(q8, qs, q_soff, k8, ks, k_soff, v8, vs, q_offsets, k_offsets, causal=False, window=0,
+              scale=None, pquant=True, pair_mask=None, nthreads=0):
+    """Softmax attention forward on MXFP8 inputs (K and V share k_soff); with pquant the
+    softmax weights are rounded to E4M3 at scale 2^-8 before P V. Returns (out, lse) float64."""
+    lib = _load()
+    arrs = [np.ascontiguousarray(a, dtype=np.uint8) for a in (q8, qs, k8, ks, v8, vs)]
+    q8, qs, k8, ks, v8, vs = arrs
+    qso, kso = _offsets(q_soff), _offsets(k_soff)
+    qo, ko = _offsets(q_offsets), _offsets(k_offsets)
+    B = qo.shape[0] - 1
+    Tq, H, d = q8.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.full((Tq, H, d), np.nan, dtype=np.float64)
+    lse = np.full((Tq, H), np.nan, dtype=np.float64)
+    pm = None if pair_mask is None else np.ascontiguousarray(np.asarray(pair_mask, dtype=np.uint8).reshape(-1))
+    rc = lib.ora_fwd_mxfp8(_ptr(q8), _ptr(qs), _ptr(qso), _ptr(k8), _ptr(ks), _ptr(kso), _ptr(v8), _ptr(vs),
+                           _ptr(qo), _ptr(ko), B, H, d, int(bool(causal)), int(window), float(scale),
+                           int(bool(pquant)), _ptr(pm), _ptr(out), _ptr(lse), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out, lse
 
 
 def tile_list(row_offsets, col_offsets, BM, BN, causal=False, window=0, transposed=False, cap=1 << 30,

@@ -92,6 +92,101 @@ static double act_deriv(int act, double x) {
     return dact_gelu_tanh(x);
 }
 
+/* ---- MXFP8 ("Mixed Ultra-Low-Precision Training" section) -----------------
+ * E4M3 in its "fn" form (no infinities; the top code is NaN; largest finite
+ * 448 = 1.75 * 2^8): 1 sign bit, 4 exponent bits biased by 7, 3 mantissa bits;
+ * exponent field 0 holds subnormals m * 2^-9. */
+double ora_e4m3_decode(uint8_t b) {
+    const int sgn = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* Nearest E4M3 value, ties to even, of x in [-448, 448]. */
+uint8_t ora_e4m3_encode(double x) {
+    const uint8_t sgn = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a < ldexp(1.0, -6)) {                 /* subnormal step 2^-9; 8 steps = 2^-6 = code 0x08 */
+        const double mi = nearbyint(ldexp(a, 9));
+        return (uint8_t)(sgn | (uint8_t)mi);
+    }
+    int ex;
+    (void)frexp(a, &ex);                      /* a = f 2^ex, f in [0.5, 1) */
+    int e = ex - 1;                           /* a in [2^e, 2^(e+1)) */
+    double mi = nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+    if (mi == 8.0) { mi = 0.0; ++e; }
+    return (uint8_t)(sgn | (uint8_t)((e + 7) << 3) | (uint8_t)mi);
+}
+
+/* Scale exponent of one [32 x 32] block with largest magnitude amax: the shared
+ * exponent floor(log2(amax)) minus E4M3's largest exponent 8, limited to the
+ * E8M0 range [-127, 127]; an all-zero block takes -127. */
+static int mx_block_exponent(double amax) {
+    if (!(amax > 0.0)) return -127;
+    int ex;
+    (void)frexp(amax, &ex);
+    int e = (ex - 1) - 8;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+int ora_mxfp8_quantize(const void* x, int dtype, const int32_t* off, int32_t B, int32_t H, int32_t d,
+                       uint8_t* x8, uint8_t* scales, int32_t* soff) {
+    if (!x || !off || !x8 || !scales || !soff || B < 0 || H < 1 || d < 32 || d % 32 != 0) return -1;
+    if (dtype != ORA_F32 && dtype != ORA_BF16 && dtype != ORA_F64) return -1;
+    if (off[0] != 0) return -1;
+    soff[0] = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        if (off[b + 1] < off[b]) return -1;
+        soff[b + 1] = soff[b] + (off[b + 1] - off[b] + 31) / 32;
+    }
+    const int32_t nd = d / 32;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t r0 = off[b], L = off[b + 1] - off[b];
+        for (int64_t jb = 0; jb * 32 < L; ++jb)
+            for (int32_t h = 0; h < H; ++h)
+                for (int32_t c = 0; c < nd; ++c) {
+                    const int64_t rows = L - jb * 32 < 32 ? L - jb * 32 : 32;
+                    double amax = 0.0;
+                    for (int64_t r = 0; r < rows; ++r)
+                        for (int32_t e = 0; e < 32; ++e) {
+                            const double a = fabs(elem(x, dtype, ((r0 + jb * 32 + r) * H + h) * d + c * 32 + e));
+                            if (a > amax) amax = a;
+                        }
+                    const int ex = mx_block_exponent(amax);
+                    scales[((int64_t)(soff[b] + jb) * H + h) * nd + c] = (uint8_t)(ex + 127);
+                    for (int64_t r = 0; r < rows; ++r)
+                        for (int32_t e = 0; e < 32; ++e) {
+                            const int64_t i = ((r0 + jb * 32 + r) * H + h) * d + c * 32 + e;
+                            double v = ldexp(elem(x, dtype, i), -ex);
+                            if (v > 448.0) v = 448.0;
+                            if (v < -448.0) v = -448.0;
+                            x8[i] = ora_e4m3_encode(v);
+                        }
+                }
+    }
+    return 0;
+}
+
+/* Dequantized tensor: x = e4m3(x8) * 2^(scale - 127) of its [32 x 32] block. */
+static double* mx_dequantize(const uint8_t* x8, const uint8_t* scales, const int32_t* soff,
+                             const int32_t* off, int32_t B, int32_t H, int32_t d) {
+    const int64_t T = off[B], nd = d / 32;
+    double* x = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T * H * d : 1));
+    if (!x) return NULL;
+    for (int32_t b = 0; b < B; ++b)
+        for (int64_t r = off[b]; r < off[b + 1]; ++r)
+            for (int32_t h = 0; h < H; ++h)
+                for (int32_t c = 0; c < d; ++c) {
+                    const int64_t jb = soff[b] + (r - off[b]) / 32;
+                    const int sc = scales[(jb * H + h) * nd + c / 32];
+                    const int64_t i = (r * H + h) * d + c;
+                    x[i] = ldexp(ora_e4m3_decode(x8[i]), sc - 127);
+                }
+    return x;
+}
+
 /* ---- visibility ----------------------------------------------------------
  * Query i sees key j (both local to their sequence) iff j < Lk, and
  * causal => j <= i, and window W > 0 => (causal ? i - j < W : |i - j| < W),
@@ -120,6 +215,7 @@ typedef struct {
     int act, causal;
     int32_t window;
     int32_t block;
+    int pquant; /* softmax: P rounded to MXFP8 (E4M3 at the fixed scale 2^-8) in P V */
     double scale;
     const uint8_t* pair_mask;
     double *out, *lse, *dq, *dk, *dv;
@@ -167,6 +263,7 @@ static void fwd_rows(job_t* J, int32_t b, int32_t h, int64_t i0, int64_t i1) {
                 for (int64_t j = 0; j < Lk; ++j) {
                     if (!visible(i, j, Lk, J->causal, J->window, J->block)) continue;
                     double p = exp(s[j] - m);
+                    if (J->pquant) p = ldexp(ora_e4m3_decode(ora_e4m3_encode(ldexp(p, 8))), -8);
                     for (int64_t c = 0; c < d; ++c)
                         o[c] += p * elem(J->v, J->dtype, ((ko + j) * H + h) * d + c);
                 }
@@ -365,6 +462,34 @@ int ora_fwd(const void* q, const void* k, const void* v, int dtype,
             const uint8_t* pair_mask, double* out, double* lse, int nthreads) {
     return ora_fwd_block(q, k, v, dtype, q_off, k_off, B, H, d, act, causal, window, 0, scale,
                          pair_mask, out, lse, nthreads);
+}
+
+int ora_fwd_mxfp8(const uint8_t* q8, const uint8_t* qs, const int32_t* q_soff,
+                  const uint8_t* k8, const uint8_t* ks, const int32_t* k_soff,
+                  const uint8_t* v8, const uint8_t* vs,
+                  const int32_t* q_off, const int32_t* k_off, int32_t B, int32_t H, int32_t d,
+                  int causal, int32_t window, double scale, int pquant,
+                  const uint8_t* pair_mask, double* out, double* lse, int nthreads) {
+    if (check_common(q_off, k_off, B, H, d, ORA_SOFTMAX, window) || !out || d % 32 != 0) return -1;
+    if (!q8 || !qs || !q_soff || !k8 || !ks || !k_soff || !v8 || !vs) return -1;
+    double* q = mx_dequantize(q8, qs, q_soff, q_off, B, H, d);
+    double* k = mx_dequantize(k8, ks, k_soff, k_off, B, H, d);
+    double* v = mx_dequantize(v8, vs, k_soff, k_off, B, H, d);
+    int rc = -1;
+    if (q && k && v) {
+        job_t J;
+        memset(&J, 0, sizeof J);
+        J.q = q; J.k = k; J.v = v; J.dtype = ORA_F64;
+        J.q_off = q_off; J.k_off = k_off; J.B = B; J.H = H; J.d = d;
+        J.act = ORA_SOFTMAX; J.causal = causal != 0; J.window = window; J.scale = scale;
+        J.pquant = pquant != 0;
+        J.pair_mask = pair_mask; J.out = out; J.lse = lse;
+        rc = run(&J, nthreads);
+    }
+    free(q);
+    free(k);
+    free(v);
+    return rc;
 }
 
 int ora_bwd_block(const void* q, const void* k, const void* v, const void* dout, int dtype,

@@ -111,6 +111,37 @@ int64_t ora_tile_list_block(const int32_t* row_off, const int32_t* col_off, int3
                             int transposed, int32_t cap,
                             int32_t* items, int32_t* costs, int64_t max_items);
 
+/* MXFP8 ("Mixed Ultra-Low-Precision Training" section: block-scaled FP8
+ * attention, one scale per [32, 32] block so that a tensor and its transpose
+ * share one quantization). Readings: elements are E4M3 ("fn": largest finite
+ * 448, no infinities), scales E8M0 powers of two; a block covers 32 consecutive
+ * tokens of one sequence (blocks restart at every sequence start, the last may
+ * be short) times 32 consecutive channels of one head; its scale exponent is
+ * floor(log2(amax)) - 8 (E4M3's largest exponent), limited to [-127, 127]
+ * (-127 for an all-zero block), and each element is x / 2^e clamped to +-448
+ * and rounded to the nearest E4M3 value, ties to even.
+ * ora_e4m3_encode: nearest E4M3 code of x in [-448, 448]; ora_e4m3_decode: its
+ * value (NaN for the NaN codes). */
+double ora_e4m3_decode(uint8_t b);
+uint8_t ora_e4m3_encode(double x);
+/* x [T,H,d] -> x8 [T,H,d] E4M3 codes, scales [NB,H,d/32] (byte = exponent + 127),
+ * soff [B+1]: first 32-token block of each sequence (NB = soff[B]). */
+int ora_mxfp8_quantize(const void* x, int dtype, const int32_t* off, int32_t B, int32_t H, int32_t d,
+                       uint8_t* x8, uint8_t* scales, int32_t* soff);
+/* Softmax attention forward on dequantized MXFP8 Q, K, V (K and V share
+ * k_soff): S = scale Q K^T, the row max m and sum l = sum_j exp(S_ij - m) of
+ * the visible keys, then with pquant the weights exp(S_ij - m) rounded to E4M3
+ * at the fixed scale 2^-8 (they are at most 1, so no per-block amax is needed:
+ * the softmax's own row max sets the scale) before the product with V;
+ * out = sum_j P_ij V_j / l, lse = m + ln l. pquant = 0 gives plain softmax
+ * attention on the dequantized tensors. */
+int ora_fwd_mxfp8(const uint8_t* q8, const uint8_t* qs, const int32_t* q_soff,
+                  const uint8_t* k8, const uint8_t* ks, const int32_t* k_soff,
+                  const uint8_t* v8, const uint8_t* vs,
+                  const int32_t* q_off, const int32_t* k_off, int32_t B, int32_t H, int32_t d,
+                  int causal, int32_t window, double scale, int pquant,
+                  const uint8_t* pair_mask, double* out, double* lse, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -551,3 +551,177 @@ def test_block_attention_gradients_against_autograd():
     ref = dense_reference(w, "softmax", True, 0, need_grad=True, dout=w.dout, block=64)
     for got, want in ((dq, ref["dq"]), (dk, ref["dk"]), (dv, ref["dv"])):
         assert _relerr(got, want) < 1e-10
+
+
+# --------------------------------------------------------------------------
+# MXFP8 pins
+# --------------------------------------------------------------------------
+
+def _torch_e4m3(x):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_codes_match_torch():
+    """Every finite code decodes as torch's float8_e4m3fn does, and encoding (ties to
+    even) agrees with torch's conversion on every code, every midpoint between
+    neighbouring codes and random values in [-448, 448]."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    ref = torch.tensor(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(vals, ref)
+    pos = np.sort(np.unique(np.abs(vals)))
+    mids = (pos[1:] + pos[:-1]) / 2
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([vals, mids, -mids, rng.uniform(-448, 448, 2000), rng.uniform(-1e-2, 1e-2, 500)])
+    np.testing.assert_array_equal(oracle.e4m3_encode(xs), _torch_e4m3(xs))
+
+
+def _mx_reference(x, off):
+    """Block scale exponent floor(log2 amax) - 8 (numpy frexp) and element rounding by
+    torch's float8_e4m3fn conversion, block by block."""
+    xf = W.bf16_bits_to_f32(x).astype(np.float64) if x.dtype == np.uint16 else np.asarray(x, np.float64)
+    T, H, d = xf.shape
+    x8 = np.zeros((T, H, d), np.uint8)
+    scales = []
+    for b in range(len(off) - 1):
+        for r0 in range(off[b], off[b + 1], 32):
+            r1 = min(r0 + 32, off[b + 1])
+            blk = xf[r0:r1].reshape(r1 - r0, H, d // 32, 32)
+            amax = np.abs(blk).max(axis=(0, 3))  # [H, d/32]
+            _, ex = np.frexp(amax)
+            e = np.where(amax > 0, np.clip(ex - 1 - 8, -127, 127), -127)
+            scales.append((e + 127).astype(np.uint8))
+            v = np.clip(blk / np.exp2(e)[None, :, :, None], -448, 448)
+            x8[r0:r1] = _torch_e4m3(v).reshape(r1 - r0, H, d)
+    return x8, np.array(scales, dtype=np.uint8).reshape(-1, H, d // 32)
+
+
+def test_mxfp8_quantize_against_library_reference():
+    w = W.make_case([1, 31, 32, 33, 100, 0, 64], H=3, d=64, dtype=W.BF16, seed=40)
+    x = w.q.copy()
+    x[5:7] = 0  # a block with zero rows and channels
+    x8, sc, soff = oracle.mxfp8_quantize(x, w.q_offsets)
+    rx8, rsc = _mx_reference(x, w.q_offsets)
+    np.testing.assert_array_equal(x8, rx8)
+    np.testing.assert_array_equal(sc, rsc)
+    np.testing.assert_array_equal(soff, np.concatenate([[0], np.cumsum((w.lq + 31) // 32)]))
+
+
+def test_mxfp8_quantize_closed_forms():
+    off = np.array([0, 40], dtype=np.int32)
+    x = np.zeros((40, 1, 32), dtype=np.float64)
+    x[3, 0, 5] = 2.0 ** -3          # block 0: amax a power of two -> stored as 256 (code 0x78)
+    x[7, 0, 9] = -2.0 ** -4
+    x[35, 0, 0] = 3.0               # block 1: amax 3 = 1.5 * 2 -> exponent 1 - 8, stored 384
+    x8, sc, soff = oracle.mxfp8_quantize(x, off)
+    assert list(sc[:, 0, 0]) == [127 - 3 - 8, 127 + 1 - 8]
+    assert x8[3, 0, 5] == 0x78 and x8[7, 0, 9] == 0xF0 and x8[35, 0, 0] == oracle.e4m3_encode([384.0])[0]
+    assert np.count_nonzero(x8) == 3
+    z8, zs, _ = oracle.mxfp8_quantize(np.zeros((5, 2, 32)), np.array([0, 5], np.int32))
+    assert not z8.any() and not zs.any()  # all-zero blocks: scale byte 0, zero codes
+
+
+def test_mxfp8_quantize_error_bound_and_sequence_independence():
+    w = W.make_case([70, 33, 5], H=2, d=64, dtype=W.F32, seed=41)
+    x8, sc, soff = oracle.mxfp8_quantize(w.q, w.q_offsets)
+    deq = np.zeros_like(w.q, dtype=np.float64)
+    for b in range(w.B):
+        for r in range(w.q_offsets[b], w.q_offsets[b + 1]):
+            blk = soff[b] + (r - w.q_offsets[b]) // 32
+            deq[r] = oracle.e4m3_decode(x8[r]) * np.exp2(np.repeat(sc[blk].astype(np.float64) - 127, 32, axis=1))
+    x = w.q.astype(np.float64)
+    # each block's largest element lands in [256, 448] (values above 448 times the scale
+    # saturate); the rest lose at most half a unit of E4M3's last place, 2^-4 relative,
+    # or 2^-10 of the scale below the normal range
+    for b in range(w.B):
+        for blk in range(soff[b], soff[b + 1]):
+            for h in range(w.H):
+                for c in range(w.d // 32):
+                    codes = x8[w.q_offsets[b] + 32 * (blk - soff[b]):, h, 32 * c:32 * c + 32][:32]
+                    codes = codes[:max(0, min(32, w.q_offsets[b + 1] - w.q_offsets[b] - 32 * (blk - soff[b])))]
+                    assert 256 <= np.abs(oracle.e4m3_decode(codes)).max() <= 448
+    scale_of = np.zeros_like(x)
+    for b in range(w.B):
+        for r in range(w.q_offsets[b], w.q_offsets[b + 1]):
+            scale_of[r] = np.exp2(np.repeat(sc[soff[b] + (r - w.q_offsets[b]) // 32].astype(np.float64) - 127, 32, axis=1))
+    sat = np.abs(x) > 448 * scale_of  # the top of a block's range saturates at 448 (<= 1/8 of it)
+    assert np.all(np.abs(deq[sat]) == 448 * scale_of[sat])
+    assert np.all(np.abs(deq - x)[~sat] <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * scale_of)[~sat])
+    # blocks restart at each sequence: quantizing one sequence alone gives the same codes
+    s1, s2 = int(w.q_offsets[1]), int(w.q_offsets[2])
+    a8, asc, _ = oracle.mxfp8_quantize(w.q[s1:s2], np.array([0, s2 - s1], np.int32))
+    np.testing.assert_array_equal(a8, x8[s1:s2])
+    np.testing.assert_array_equal(asc, sc[soff[1]:soff[2]])
+
+
+def _mx_case(lq, lk, d=64, H=2, seed=0):
+    w = W.make_case(lq, lk, H=H, d=d, dtype=W.BF16, seed=seed)
+    q = oracle.mxfp8_quantize(w.q, w.q_offsets)
+    k = oracle.mxfp8_quantize(w.k, w.k_offsets)
+    v = oracle.mxfp8_quantize(w.v, w.k_offsets)
+    return w, q, k, v
+
+
+def _dequant(t, off):
+    x8, sc, soff = t
+    out = np.zeros(x8.shape, np.float64)
+    for b in range(len(off) - 1):
+        for r in range(off[b], off[b + 1]):
+            out[r] = oracle.e4m3_decode(x8[r]) * np.exp2(np.repeat(sc[soff[b] + (r - off[b]) // 32].astype(np.float64) - 127, 32, axis=1))
+    return out
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 9)])
+def test_fwd_mxfp8_without_p_rounding_is_attention_on_dequantized_inputs(causal, window):
+    w, q, k, v = _mx_case([37, 64, 1, 90], [37, 64, 1, 90], seed=42)
+    out, lse = oracle.fwd_mxfp8(q[0], q[1], q[2], k[0], k[1], k[2], v[0], v[1], w.q_offsets, w.k_offsets,
+                                causal, window, w.scale, pquant=False)
+    qd, kd, vd = _dequant(q, w.q_offsets), _dequant(k, w.k_offsets), _dequant(v, w.k_offsets)
+    ref, rlse = oracle.fwd(qd, kd, vd, w.q_offsets, w.k_offsets, "softmax", causal, window, w.scale)
+    np.testing.assert_array_equal(out, ref)
+    np.testing.assert_array_equal(lse, rlse)
+    # and that is torch SDPA on the dequantized tensors
+    wd = W.Workload("deq", qd, kd, vd, w.q_offsets, w.k_offsets, w.H, w.d, W.F64)
+    dense = dense_reference(wd, "softmax", causal, window)
+    assert _relerr(out, dense["out"]) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_mxfp8_p_rounding_within_its_bound(causal):
+    """Rounding P (<= 1) to E4M3 at scale 2^-8 moves each weight by at most 2^-4 of
+    itself (or 2^-18 absolute below the normal range): |dO_i| <= sum_j dP_ij |V_j| / l_i."""
+    w, q, k, v = _mx_case([90, 33], [90, 70], seed=43)
+    args = (q[0], q[1], q[2], k[0], k[1], k[2], v[0], v[1], w.q_offsets, w.k_offsets, causal, 0, w.scale)
+    out, lse = oracle.fwd_mxfp8(*args, pquant=True)
+    ref, rlse = oracle.fwd_mxfp8(*args, pquant=False)
+    np.testing.assert_array_equal(lse, rlse)
+    qd, kd, vd = _dequant(q, w.q_offsets), _dequant(k, w.k_offsets), _dequant(v, w.k_offsets)
+    for b in range(w.B):
+        q0, q1 = w.q_offsets[b], w.q_offsets[b + 1]
+        k0, k1 = w.k_offsets[b], w.k_offsets[b + 1]
+        for h in range(w.H):
+            s = w.scale * qd[q0:q1, h] @ kd[k0:k1, h].T
+            vis = np.ones_like(s, dtype=bool)
+            if causal:
+                vis &= np.arange(k1 - k0)[None, :] <= np.arange(q1 - q0)[:, None]
+            s = np.where(vis, s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            l = p.sum(axis=1, keepdims=True)
+            bound = (np.maximum(2.0 ** -4 * p, 2.0 ** -18) * vis) @ np.abs(vd[k0:k1, h]) / l
+            err = np.abs(out[q0:q1, h] - ref[q0:q1, h])
+            assert np.all(err <= bound * (1 + 1e-12) + 1e-15)
+            assert err.max() > 0  # the rounding does act
+
+
+def test_fwd_mxfp8_exact_when_weights_are_representable():
+    """Identical keys: every visible weight is exp(0) = 1, stored exactly (256 at scale
+    2^-8), so rounding P changes nothing."""
+    w, q, k, v = _mx_case([20, 45], [20, 45], seed=44)
+    k8 = k[0].copy()
+    k8[:] = k8[0]
+    ks = k[1].copy()
+    ks[:] = ks[0]
+    args = (q[0], q[1], q[2], k8, ks, k[2], v[0], v[1], w.q_offsets, w.k_offsets, True, 0, w.scale)
+    a, _ = oracle.fwd_mxfp8(*args, pquant=True)
+    b, _ = oracle.fwd_mxfp8(*args, pquant=False)
+    np.testing.assert_array_equal(a, b)
