@@ -40,11 +40,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 HBM_BOUND = (3, 4, 6)         # workloads whose forward is bound by HBM traffic, not the matrix cores
 KERNEL_SOURCES = {
     "ja_fwd_kernel": ["ja_fwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
+    "ja_mx_fwd_kernel": ["ja_mx.hip", "ja_mx.h", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
     "ja_bwd_kernels": ["ja_bwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
 }
 METRIC = "useful (unpadded) bf16 TFLOP/s of jagged attn fwd; % of MI355X MFMA peak"
@@ -79,9 +81,10 @@ def visible_pairs(lq: np.ndarray, lk: np.ndarray, causal: bool, window: int, blo
 
 
 def roofline_kernel(workload: int) -> str:
-    """The kernel the roofline is taken on: the forward attention kernel (every
-    workload, the block one included, runs the same forward)."""
-    return "ja_fwd_kernel"
+    """The kernel the roofline is taken on: the forward attention kernel (the MXFP8
+    forward for workload 8; every other workload, the block one included, runs the
+    general forward)."""
+    return "ja_mx_fwd_kernel" if workload == 8 else "ja_fwd_kernel"
 
 
 def kernel_sha(name: str) -> str:
@@ -110,7 +113,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--bwd", action="store_true",
                     help="time forward + backward (softmax for 2, 5 and 6, SiLU / GELU for 3, 4 and 7)")
     ap.add_argument("--act", choices=["softmax", "silu", "gelu", "gelu_taylor"], default=None,
@@ -163,13 +166,24 @@ def main() -> int:
     q, k, v = up(w.q), up(w.k), up(w.v)
     qo, ko = up(w.q_offsets), up(w.k_offsets)
     dout = up(w.dout) if args.bwd else None
+    mx = bool(w.extra.get("mxfp8"))
+    if mx:
+        if args.bwd:
+            print("the MXFP8 path has no backward", file=sys.stderr)
+            return 2
+        # Quantized once, outside the timed steps (upstream kernels emit MXFP8).
+        qm = ja.mxfp8_quantize(q, qo)
+        km = ja.mxfp8_quantize(k, ko)
+        vm = ja.mxfp8_quantize(v, ko)
     Tq, Tk = q.shape[0], k.shape[0]
     out = torch.empty_like(q)
     # The block path (blocks of at most 64 tokens) keeps no log-sum-exp: its
     # backward recomputes each block's softmax.
     need_lse = w.act == "softmax" and not (w.block and w.block <= 64)
     lse = torch.empty((Tq, w.H), dtype=torch.float32, device=dev) if need_lse else None
-    if w.block:
+    if mx:
+        ws_fwd, ws_bwd = int(lib.ja_fwd_mxfp8_workspace_size(w.B, w.H, w.d, Tq, Tk)), 0
+    elif w.block:
         ws_fwd = ws_bwd = ja.block_attn_workspace_size(w.B, w.H, w.d, Tq, w.block, w.causal)
     else:
         ws_fwd = ja.fwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window)
@@ -187,7 +201,11 @@ def main() -> int:
     def step(ev=None):
         if ev is not None:
             lib.ja_set_profile_events(ev[0].cuda_event, ev[1].cuda_event)
-        if w.block:
+        if mx:
+            ja.jagged_attn_fwd_mxfp8(qm[0], qm[1], qm[2], km[0], km[1], km[2], vm[0], vm[1], qo, ko,
+                                     causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse,
+                                     workspace=ws, stream=stream)
+        elif w.block:
             ja.jagged_block_attn_fwd(q, k, v, qo, w.block, causal=w.causal, scale=w.scale, out=out, lse=lse,
                                      workspace=ws, stream=stream, return_lse=need_lse)
         else:
@@ -246,8 +264,9 @@ def main() -> int:
                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": min_bytes,
                     "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
     else:
-        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flop_per_launch": fwd_flop}
+        peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4), "flop_per_launch": fwd_flop}
     roofline["traffic"] = recorded_traffic(name, f"w{args.workload}")
     roofline["kernel"] = name
     roofline["kernel_ms"] = round(fwd_kernel_ms, 4)
@@ -264,8 +283,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "dtype": "bf16",
+        "pct_of_peak": round(100.0 * value / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS), 2),
+        "dtype": "fp8-e4m3 (MX, [32,32] block scales)" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": w.extra.get("description", w.name), "B": w.B, "H": w.H, "d": w.d,
                    "act": w.act, "causal": bool(w.causal), "window": int(w.window), "block": int(w.block),
@@ -367,6 +386,21 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
     """Time the fp64 oracle on a bounded sample of (sequence, head) pairs of the batch."""
     import oracle  # test infrastructure: used here for the CPU baseline only
 
+    if w.extra.get("mxfp8"):
+        # the MXFP8 forward on the oracle's quantization of the batch (bit-identical to
+        # the library's, which the tests check); the quantization itself is upstream
+        qm = oracle.mxfp8_quantize(w.q, w.q_offsets)
+        km = oracle.mxfp8_quantize(w.k, w.k_offsets)
+        vm = oracle.mxfp8_quantize(w.v, w.k_offsets)
+
+        def run_oracle(mask):
+            return oracle.fwd_mxfp8(qm[0], qm[1], qm[2], km[0], km[1], km[2], vm[0], vm[1], w.q_offsets,
+                                    w.k_offsets, w.causal, w.window, w.scale, pquant=True, pair_mask=mask)
+    else:
+        def run_oracle(mask):
+            return oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale,
+                              pair_mask=mask, block=w.block)
+
     rng = np.random.default_rng(1234)
     B, H = w.B, w.H
     order = [(int(b), int(h)) for b in rng.permutation(B) for h in range(H)]
@@ -381,8 +415,7 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
         for b, h in order[:n_cal]:
             mask[b, h] = True
         t = time.perf_counter()
-        oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale, pair_mask=mask,
-                   block=w.block)
+        run_oracle(mask)
         dt = time.perf_counter() - t
         if dt >= 1.0 or n_cal >= len(order):
             rate = max(pair_flop[:n_cal].sum(), 1.0) / max(dt, 1e-4)
@@ -397,8 +430,7 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
         acc += pair_flop[i]
     log(f"[bench] cpu baseline: {int(mask.sum())} pairs, {acc:.3g} flop")
     t = time.perf_counter()
-    ref, ref_lse = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale,
-                              pair_mask=mask, block=w.block)
+    ref, ref_lse = run_oracle(mask)
     dt = time.perf_counter() - t
     # parity spot-check of the GPU output on the same pairs
     got = out_gpu.float().cpu().numpy().astype(np.float64)

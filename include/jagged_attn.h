@@ -176,6 +176,49 @@ ja_status_t jagged_block_attn_bwd(const void* q, const void* k, const void* v,
                                   int32_t dtype, void* dq, void* dk, void* dv,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* MXFP8 ("Mixed Ultra-Low-Precision Training" section of the GEM training post:
+ * attention on block-scaled FP8 with one scale per [32, 32] block, so a tensor
+ * and its transpose share one quantization). Format (OCP MX): E4M3 elements
+ * ("fn": largest finite 448), E8M0 scales (byte = exponent + 127). A block is 32
+ * consecutive tokens of one sequence (blocks restart at every sequence start,
+ * the last may be short) by 32 consecutive channels of one head; its exponent
+ * is floor(log2(amax)) - 8 limited to [-127, 127] (-127 for an all-zero block),
+ * and each element is x / 2^e clamped to +-448, rounded to nearest even. */
+
+/* Bytes of workspace ja_mxfp8_quantize needs. Host only. */
+size_t ja_mxfp8_quantize_workspace_size(int32_t B, int64_t T);
+
+/* Quantizes x (JA_BF16 [T,H,d], d a multiple of 32, 16-byte aligned) to
+ *   x8 [T,H,d] E4M3 codes (16-byte aligned),
+ *   scales [NB,H,d/32] E8M0 bytes, sized for NB = ceil(T/32) + B rows (the first
+ *   scale_offsets[B] rows are written),
+ *   scale_offsets [B+1] int32: first scale row of each sequence (written).
+ * Enqueued on stream, no synchronisation. */
+ja_status_t ja_mxfp8_quantize(const void* x, int32_t dtype, const int32_t* offsets,
+                              int32_t B, int32_t H, int32_t d, int64_t T,
+                              void* x8, void* scales, int32_t* scale_offsets,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace jagged_attn_fwd_mxfp8 needs (0 for unsupported sizes). */
+size_t ja_fwd_mxfp8_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk);
+
+/* Softmax attention forward on MXFP8 inputs as ja_mxfp8_quantize writes them
+ * (K and V share k_scale_offsets), d = 128. Both products run on the MX-scaled
+ * FP8 matrix cores with the blocks' scales; the softmax keeps an exact running
+ * max, so every weight exp(s - m) is at most 1, and is rounded to E4M3 at the
+ * fixed scale 2^-8 before the product with V (the row max sets its scale); the
+ * normaliser sums the unrounded weights. out [Tq,H,d] is bf16, lse [Tq,H] fp32
+ * natural log (may be NULL). Masks, offsets, scale, ownership and errors as
+ * jagged_attn_fwd (act = softmax); d other than 128 returns JA_ERR_UNSUPPORTED. */
+ja_status_t jagged_attn_fwd_mxfp8(const void* q8, const void* q_scales, const int32_t* q_scale_offsets,
+                                  const void* k8, const void* k_scales, const int32_t* k_scale_offsets,
+                                  const void* v8, const void* v_scales,
+                                  const int32_t* q_offsets, const int32_t* k_offsets,
+                                  int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                                  int32_t causal, int32_t window, float scale,
+                                  void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Runs only the tile scheduler that jagged_attn_fwd runs first ("software tile
  * scheduling for jagged tensors", GDPA section) and copies its work list out:
  * items (device int32 [2*max_items]) receives (sequence, query-tile) pairs in the

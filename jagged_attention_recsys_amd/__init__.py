@@ -14,6 +14,8 @@ from .ops import (  # noqa: F401
     jagged_attn_fwd,
     jagged_block_attn_bwd,
     jagged_block_attn_fwd,
+    jagged_attn_fwd_mxfp8,
+    mxfp8_quantize,
     validate_offsets,
 )
 
@@ -22,6 +24,8 @@ __all__ = [
     "jagged_attn_bwd",
     "jagged_block_attn_fwd",
     "jagged_block_attn_bwd",
+    "jagged_attn_fwd_mxfp8",
+    "mxfp8_quantize",
     "fwd_workspace_size",
     "bwd_workspace_size",
     "block_attn_workspace_size",

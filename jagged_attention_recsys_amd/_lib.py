@@ -26,6 +26,11 @@ SIGNATURES = {
                                      _vp, _sz, _vp]),
     "jagged_block_attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
                                      _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ja_mxfp8_quantize_workspace_size": (_sz, [_i32, _i64]),
+    "ja_mxfp8_quantize": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ja_fwd_mxfp8_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i64]),
+    "jagged_attn_fwd_mxfp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64,
+                                     _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "ja_fwd_schedule": (_i32, [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
                                _vp, _sz, _vp]),
     "ja_fwd_tile_shape": (_i32, [_i32, _i32, _i64, _i32, _i32, _vp, _vp]),

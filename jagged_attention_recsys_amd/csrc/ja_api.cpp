@@ -14,6 +14,7 @@
 #include "jagged_attn.h"
 #include "ja_block.h"
 #include "ja_internal.h"
+#include "ja_mx.h"
 #include "ja_tiles.h"
 
 using namespace ja;
@@ -441,6 +442,129 @@ ja_status_t jagged_block_attn_bwd(const void* q, const void* k, const void* v, c
     const int64_t cap_bwd = (int64_t)device_cus() * blk_occupancy_cached(d);
     if (grid > cap_bwd) grid = cap_bwd;
     if (launch_blk_bwd(ba, d, (int)grid, s) != hipSuccess) return JA_ERR_HIP;
+    if (g_prof_after && hipEventRecord(g_prof_after, s) != hipSuccess) return JA_ERR_HIP;
+    return JA_OK;
+}
+
+size_t ja_mxfp8_quantize_workspace_size(int32_t B, int64_t T) {
+    if (B < 0 || T < 0) return 0;
+    const int64_t blocks = (T + kMxBlock - 1) / kMxBlock + B;
+    if (blocks >= INT32_MAX) return 0;
+    return align_up(sizeof(int32_t) * (size_t)(blocks > 0 ? blocks : 1));
+}
+
+ja_status_t ja_mxfp8_quantize(const void* x, int32_t dtype, const int32_t* offsets, int32_t B, int32_t H, int32_t d,
+                              int64_t T, void* x8, void* scales, int32_t* scale_offsets, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (B < 0 || H < 1 || T < 0 || d < kMxBlock || d % kMxBlock != 0) return JA_ERR_INVALID_ARG;
+    if (dtype != JA_BF16) return JA_ERR_UNSUPPORTED;
+    if (T > INT32_MAX) return JA_ERR_UNSUPPORTED;
+    if (!offsets || !scale_offsets || (T > 0 && (!x || !x8 || !scales)) || !workspace) return JA_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(offsets, 4) || !aligned(scale_offsets, 4) ||
+        !aligned(workspace, 4))
+        return JA_ERR_INVALID_ARG;
+    const int64_t blocks = (T + kMxBlock - 1) / kMxBlock + B;
+    if (blocks >= INT32_MAX || blocks * H * (d / kMxBlock) >= INT32_MAX) return JA_ERR_UNSUPPORTED;
+    if (workspace_bytes < sizeof(int32_t) * (size_t)(blocks > 0 ? blocks : 1)) return JA_ERR_WORKSPACE;
+    MxQuantArgs a;
+    a.x = x;
+    a.off = offsets;
+    a.x8 = static_cast<uint8_t*>(x8);
+    a.scales = static_cast<uint8_t*>(scales);
+    a.soff = scale_offsets;
+    a.blk_seq = static_cast<int32_t*>(workspace);
+    a.B = B;
+    a.H = H;
+    a.d = d;
+    a.T = (int32_t)T;
+    a.max_blocks = (int32_t)blocks;
+    if (launch_mx_quant(a, static_cast<hipStream_t>(stream)) != hipSuccess) return JA_ERR_HIP;
+    return JA_OK;
+}
+
+size_t ja_fwd_mxfp8_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk) {
+    if (B < 0 || H < 1 || d != kMxD || Tq < 0 || Tk < 0 || Tq > INT32_MAX || Tk > INT32_MAX) return 0;
+    const int64_t max_pairs = (Tq + kMxBM - 1) / kMxBM + B;
+    if (max_pairs * (int64_t)H >= INT32_MAX) return 0;
+    const size_t off_tbase = align_up(sizeof(int32_t) * kCtrCount);
+    const size_t off_items = align_up(off_tbase + sizeof(int32_t) * ((size_t)B + 1));
+    return align_up(off_items + sizeof(int32_t) * 2 * (size_t)max_pairs);
+}
+
+ja_status_t jagged_attn_fwd_mxfp8(const void* q8, const void* q_scales, const int32_t* q_scale_offsets,
+                                  const void* k8, const void* k_scales, const int32_t* k_scale_offsets,
+                                  const void* v8, const void* v_scales, const int32_t* q_offsets,
+                                  const int32_t* k_offsets, int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                                  int32_t causal, int32_t window, float scale, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || H < 1 || Tq < 0 || Tk < 0 || window < 0 || !std::isfinite(scale)) return JA_ERR_INVALID_ARG;
+    if (d != kMxD) return JA_ERR_UNSUPPORTED;
+    if (Tq > INT32_MAX || Tk > INT32_MAX) return JA_ERR_UNSUPPORTED;
+    if (B == 0 || Tq == 0) return JA_OK;
+    if (!q8 || !q_scales || !q_scale_offsets || !out || !q_offsets || !k_offsets || !k_scale_offsets || !workspace)
+        return JA_ERR_INVALID_ARG;
+    if (Tk > 0 && (!k8 || !v8 || !k_scales || !v_scales)) return JA_ERR_INVALID_ARG;
+    const void* p16[] = {q8, k8, v8, out, workspace};
+    for (const void* p : p16)
+        if (!aligned(p, 16)) return JA_ERR_INVALID_ARG;
+    const void* p4[] = {q_scales, k_scales, v_scales, q_scale_offsets, k_scale_offsets, q_offsets, k_offsets, lse};
+    for (const void* p : p4)
+        if (!aligned(p, 4)) return JA_ERR_INVALID_ARG;
+    const size_t need = ja_fwd_mxfp8_workspace_size(B, H, d, Tq, Tk);
+    if (need == 0) return JA_ERR_UNSUPPORTED;
+    if (workspace_bytes < need) return JA_ERR_WORKSPACE;
+    const int64_t max_pairs = (Tq + kMxBM - 1) / kMxBM + B;
+    char* ws = static_cast<char*>(workspace);
+    SchedArgs sa;
+    sa.row_off = q_offsets;
+    sa.col_off = k_offsets;
+    sa.B = B;
+    sa.H = H;
+    sa.bm = kMxBM;
+    sa.bn = kMxKT;
+    sa.causal = causal ? 1 : 0;
+    sa.window = window;
+    sa.transposed = 0;
+    sa.bsh = kNoBlock;
+    sa.max_pairs = max_pairs;
+    sa.counters = reinterpret_cast<int32_t*>(ws);
+    sa.tbase = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int32_t) * kCtrCount));
+    sa.items = reinterpret_cast<int32_t*>(ws + align_up(align_up(sizeof(int32_t) * kCtrCount) +
+                                                        sizeof(int32_t) * ((size_t)B + 1)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_sched(sa, s) != hipSuccess) return JA_ERR_HIP;
+    MxFwdArgs a;
+    a.q8 = static_cast<const uint8_t*>(q8);
+    a.k8 = static_cast<const uint8_t*>(k8);
+    a.v8 = static_cast<const uint8_t*>(v8);
+    a.qs = static_cast<const uint8_t*>(q_scales);
+    a.ks = static_cast<const uint8_t*>(k_scales);
+    a.vs = static_cast<const uint8_t*>(v_scales);
+    a.q_soff = q_scale_offsets;
+    a.k_soff = k_scale_offsets;
+    a.out = out;
+    a.lse = lse;
+    a.q_off = q_offsets;
+    a.k_off = k_offsets;
+    a.items = sa.items;
+    a.counters = sa.counters;
+    a.H = H;
+    a.Tq = (int32_t)Tq;
+    a.Tk = (int32_t)Tk;
+    a.causal = causal ? 1 : 0;
+    a.window = window;
+    a.scale = scale;
+    static std::atomic<int> occ{0};
+    int n = occ.load(std::memory_order_relaxed);
+    if (n <= 0) {
+        n = mx_fwd_blocks_per_cu();
+        occ.store(n, std::memory_order_relaxed);
+    }
+    int64_t grid = (int64_t)device_cus() * n;
+    if (grid > max_pairs * H) grid = max_pairs * H;
+    if (grid < 1) grid = 1;
+    if (g_prof_before && hipEventRecord(g_prof_before, s) != hipSuccess) return JA_ERR_HIP;
+    if (launch_mx_fwd(a, (int)grid, s) != hipSuccess) return JA_ERR_HIP;
     if (g_prof_after && hipEventRecord(g_prof_after, s) != hipSuccess) return JA_ERR_HIP;
     return JA_OK;
 }

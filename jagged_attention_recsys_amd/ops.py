@@ -207,6 +207,63 @@ def jagged_block_attn_bwd(q, k, v, out, dout, lse, offsets, block, causal=False,
     return dq, dk, dv
 
 
+def mxfp8_quantize(x, offsets, stream=None):
+    """MXFP8 quantization with [32, 32] blocks (32 tokens of one sequence x 32 channels
+    of one head). x: bf16 [T,H,d] (d a multiple of 32); offsets: int32 [B+1].
+
+    Returns (x8 uint8 [T,H,d] E4M3 codes, scales uint8 [NB,H,d/32] E8M0 exponents,
+    scale_offsets int32 [B+1]); NB = ceil(T/32) + B rows are allocated, the first
+    scale_offsets[B] are used."""
+    lib = _lib.load()
+    _check_tensor("x", x, torch.bfloat16, 3)
+    _check_tensor("offsets", offsets, torch.int32, 1)
+    T, H, d = x.shape
+    B = offsets.numel() - 1
+    nb = (T + 31) // 32 + B
+    x8 = torch.empty((T, H, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((max(nb, 1), H, max(d // 32, 1)), dtype=torch.uint8, device=x.device)
+    soff = torch.empty(B + 1, dtype=torch.int32, device=x.device)
+    ws = torch.empty(max(int(lib.ja_mxfp8_quantize_workspace_size(B, T)), 256), dtype=torch.uint8, device=x.device)
+    status = lib.ja_mxfp8_quantize(_ptr(x), DTYPE[torch.bfloat16], _ptr(offsets), B, H, d, T, _ptr(x8), _ptr(scales),
+                                   _ptr(soff), _ptr(ws), ws.numel(), _stream(x.device, stream))
+    _lib.check("ja_mxfp8_quantize", status)
+    return x8, scales, soff
+
+
+def jagged_attn_fwd_mxfp8(q8, q_scales, q_scale_offsets, k8, k_scales, k_scale_offsets, v8, v_scales, q_offsets,
+                          k_offsets, causal=False, window=0, scale=None, out=None, lse=None, workspace=None,
+                          stream=None, return_lse=True):
+    """Softmax attention forward on MXFP8 Q, K, V (from ``mxfp8_quantize``; K and V share
+    k_scale_offsets), d = 128. Returns (out bf16 [Tq,H,d], lse [Tq,H] float32 or None)."""
+    lib = _lib.load()
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _check_tensor(name, t, torch.uint8, 3)
+    for name, t in (("q_scales", q_scales), ("k_scales", k_scales), ("v_scales", v_scales)):
+        _check_tensor(name, t, torch.uint8, 3)
+    for name, t in (("q_scale_offsets", q_scale_offsets), ("k_scale_offsets", k_scale_offsets),
+                    ("q_offsets", q_offsets), ("k_offsets", k_offsets)):
+        _check_tensor(name, t, torch.int32, 1)
+    Tq, H, d = q8.shape
+    Tk = k8.shape[0]
+    B = q_offsets.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((Tq, H, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None and return_lse:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=q8.device)
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.ja_fwd_mxfp8_workspace_size(B, H, d, Tq, Tk)), 256), dtype=torch.uint8,
+                                device=q8.device)
+    status = lib.jagged_attn_fwd_mxfp8(_ptr(q8), _ptr(q_scales), _ptr(q_scale_offsets), _ptr(k8), _ptr(k_scales),
+                                       _ptr(k_scale_offsets), _ptr(v8), _ptr(v_scales), _ptr(q_offsets),
+                                       _ptr(k_offsets), B, H, d, Tq, Tk, int(bool(causal)), int(window), float(scale),
+                                       _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                       _stream(q8.device, stream))
+    _lib.check("jagged_attn_fwd_mxfp8", status)
+    return out, lse
+
+
 def fwd_tile_shape(B, d, Tq, act="softmax", dtype=torch.bfloat16):
     import ctypes
     bm, bn = ctypes.c_int32(), ctypes.c_int32()

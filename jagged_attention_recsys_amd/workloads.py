@@ -5,7 +5,7 @@ tensors, rounded to bf16 where a workload asks for it. It holds none of the
 attention arithmetic, so both the HIP path (through its tests and benchmark) and
 the fp64 oracle can be fed from the same bytes.
 
-The seven workloads follow the shapes the engineering post "GEM Training: How Meta
+The eight workloads follow the shapes the engineering post "GEM Training: How Meta
 Doubled the Efficiency of Its LLM-Scale Ads Foundation Model" describes in its
 "Challenge 1" section (jagged user histories from hundreds to tens of thousands of
 tokens; self-attention, cross-attention with long queries and short key/value,
@@ -157,7 +157,7 @@ def _build(rng, name, lq, lk, H, d, dtype, act, causal, window, with_dout, share
                     act=act, causal=causal, window=window, dout=dout)
 
 
-# --- the seven named workloads ------------------------------------------------
+# --- the eight named workloads ------------------------------------------------
 
 WORKLOADS = {
     1: "tiny jagged softmax self-attention fwd, fp32: B=4 lengths {7,33,64,129}, H=2, d=32 "
@@ -174,11 +174,13 @@ WORKLOADS = {
        "lengths lognormal (median 2048, sigma 1, cap 32768), blocks of 64 tokens, H=8, d=128",
     7: "GDPA causal self-attention with the ALU-only GELU (order-6 Taylor), QK-normed (unit-norm) "
        "queries and keys, scale 1, fwd+bwd, bf16: B=64, lengths log-uniform [128,4096], H=4, d=128",
+    8: "jagged causal softmax self-attention fwd on MXFP8 Q/K/V (E4M3, [32,32] block scales), the batch of "
+       "workload 2: B=64, lengths log-uniform [128,4096], H=4, d=128",
 }
 
 
 def workload(n: int, act: str | None = None, seed: int | None = None) -> Workload:
-    """Build workload ``n`` (1..7) from its seed (default: n)."""
+    """Build workload ``n`` (1..8) from its seed (default: n; 8 reuses workload 2's batch)."""
     rng = np.random.default_rng(n if seed is None else seed)
     if n == 1:
         lq = np.array([7, 33, 64, 129], dtype=np.int64)
@@ -201,6 +203,10 @@ def workload(n: int, act: str | None = None, seed: int | None = None) -> Workloa
         lq = lognormal_lengths(rng, 32, 2048.0, 1.0, 32768)
         w = _build(rng, "w6", lq, lq, 8, 128, BF16, act or "softmax", True, 0, True, None)
         w.block = 64
+    elif n == 8:
+        w = workload(2, act=act, seed=2 if seed is None else seed)
+        w.name = "w8"
+        w.extra["mxfp8"] = True
     elif n == 7:
         lq = log_uniform_lengths(rng, 64, 128, 4096)
         w = _build(rng, "w7", lq, lq, 4, 128, BF16, act or "gelu_taylor", True, 0, True, None, qk_norm=True)
