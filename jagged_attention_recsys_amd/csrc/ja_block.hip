@@ -117,10 +117,11 @@ __device__ __forceinline__ bool tile_item(const BlkArgs& a, int idx, TileItem& i
     const int total = a.counters[kCtrTotal];
     const int b = a.items[2 * pair], t = a.items[2 * pair + 1];
     if (idx >= total || b < 0 || b >= a.B) return false;
-    it.o0 = a.off[b];
+    const int o0 = a.off[b], o1 = a.off[b + 1];  // independent loads
+    it.o0 = o0;
     // Rows are clamped to the tensors, so inconsistent offsets cannot reach
     // outside them.
-    it.L = it.o0 < 0 ? 0 : min(a.off[b + 1], a.T) - (int)it.o0;
+    it.L = o0 < 0 ? 0 : min(o1, a.T) - o0;
     it.r0 = t * kBlkTile;
     it.n = min(it.L - it.r0, kBlkTile);
     return it.n > 0;

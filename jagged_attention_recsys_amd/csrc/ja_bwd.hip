@@ -92,10 +92,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
         const int idx = __builtin_amdgcn_readfirstlane(s_item);
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
-        const int b = a.q_items[2 * pair], qt = a.q_items[2 * pair + 1];
-        const int64_t qo = a.q_off[b], ko = a.k_off[b];
-        const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
-        const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
+        const ItemSeq is = load_item(a.q_items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const int qt = is.t;
+        const int64_t qo = is.qo, ko = is.ko;
+        const int Lq = is.Lq, Lk = is.Lk;
         const int q0 = qt * kBwdRows;
         const ColRange cr = visible_cols(Lq, Lk, q0, kBwdRows, causal, window, 0, bsh);
         const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
@@ -268,10 +268,10 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
         const int idx = __builtin_amdgcn_readfirstlane(s_item);
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
-        const int b = a.k_items[2 * pair], kt = a.k_items[2 * pair + 1];
-        const int64_t qo = a.q_off[b], ko = a.k_off[b];
-        const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
-        const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
+        const ItemSeq is = load_item(a.k_items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const int kt = is.t;
+        const int64_t qo = is.qo, ko = is.ko;
+        const int Lq = is.Lq, Lk = is.Lk;
         const int k0 = kt * kBwdRows;
         const ColRange cr = visible_cols(Lk, Lq, k0, kBwdRows, causal, window, 1, bsh);
         const int qs_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;

@@ -145,12 +145,10 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
         lds_barrier();  // s_item is read by every wave before it is rewritten
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
-        const int b = a.items[2 * pair], qt = a.items[2 * pair + 1];
-        const int64_t qo = a.q_off[b], ko = a.k_off[b];
-        // Rows are clamped to the tensors, so inconsistent offsets cannot reach
-        // outside them (the header leaves such offsets undefined otherwise).
-        const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
-        const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
+        const ItemSeq is = load_item(a.items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const int qt = is.t;
+        const int64_t qo = is.qo, ko = is.ko;
+        const int Lq = is.Lq, Lk = is.Lk;
         const int q0 = qt * C::BM;
         const ColRange cr = visible_cols(Lq, Lk, q0, C::BM, causal, window, 0, bsh);
         const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / C::KT) : 0;

@@ -147,6 +147,32 @@ struct TileLoader {
     }
 };
 
+// A work item's sequence: the (sequence, tile) pair, then the sequence's four
+// offsets as independent loads (one round trip after the pair's, not four).
+// Rows are clamped to the tensors, so inconsistent offsets cannot reach outside
+// them (the C ABI leaves such offsets undefined otherwise).
+struct ItemSeq {
+    int b, t;        // sequence, tile
+    int64_t qo, ko;  // first query / key row of the sequence
+    int Lq, Lk;      // its query / key counts
+};
+
+__device__ __forceinline__ ItemSeq load_item(const int32_t* items, int pair, const int32_t* q_off,
+                                             const int32_t* k_off, int Tq, int Tk) {
+    typedef int int2v __attribute__((ext_vector_type(2)));
+    const int2v it = *(const int2v*)(items + 2 * pair);
+    const int q0 = q_off[it[0]], q1 = q_off[it[0] + 1];
+    const int k0 = k_off[it[0]], k1 = k_off[it[0] + 1];
+    ItemSeq s;
+    s.b = it[0];
+    s.t = it[1];
+    s.qo = q0;
+    s.ko = k0;
+    s.Lq = q0 < 0 ? 0 : min(q1, Tq) - q0;
+    s.Lk = k0 < 0 ? 0 : min(k1, Tk) - k0;
+    return s;
+}
+
 // Wave-uniform mask decisions for a block [x0, x0 + n) of the other index, from
 // every lane's visible range; lanes with lane_ok false (rows past the sequence
 // end, never written) take no part.

@@ -248,10 +248,10 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
         lds_barrier();
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
-        const int b = a.items[2 * pair], qt = a.items[2 * pair + 1];
-        const int64_t qo = a.q_off[b], ko = a.k_off[b];
-        const int Lq = qo < 0 ? 0 : min(a.q_off[b + 1], a.Tq) - (int)qo;
-        const int Lk = ko < 0 ? 0 : min(a.k_off[b + 1], a.Tk) - (int)ko;
+        const ItemSeq is = load_item(a.items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const int b = is.b, qt = is.t;
+        const int64_t qo = is.qo, ko = is.ko;
+        const int Lq = is.Lq, Lk = is.Lk;
         const int q0 = qt * kMxBM;
         const ColRange cr = visible_cols(Lq, Lk, q0, kMxBM, causal, window, 0, kNoBlock);
         const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / kMxKT) : 0;
