@@ -9,7 +9,7 @@ namespace ja {
 constexpr int kMxBlock = 32;   // tokens (and channels) per scale block
 constexpr int kMxD = 128;      // head dim of the MXFP8 attention forward
 constexpr int kMxBM = 128;     // query rows per work item
-constexpr int kMxKT = 64;      // keys per stage (scheduler cost unit)
+constexpr int kMxKT = 128;     // keys per stage (scheduler cost unit)
 
 struct MxQuantArgs {
     const void* x;             // bf16 [T, H, d]

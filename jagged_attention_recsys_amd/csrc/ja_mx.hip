@@ -47,7 +47,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMxWaves = 4;
 constexpr int kMxThreads = 64 * kMxWaves;
 constexpr int kMxRowB = kMxD;              // bytes per FP8 row of one head
-[[maybe_unused]] constexpr int kMxTile = kMxKT * kMxRowB;  // one K or V stage: 8 KB
+[[maybe_unused]] constexpr int kMxTile = kMxKT * kMxRowB;  // one K or V stage
+[[maybe_unused]] constexpr int kMxNKB = kMxKT / 32;          // 32-key blocks per stage
+[[maybe_unused]] constexpr int kMxNKH = kMxKT / 64;          // 64-key halves per stage (one P V product each)
+[[maybe_unused]] constexpr int kMxLPW = kMxTile / 1024 / kMxWaves;  // 64-lane loads per wave per tile
 [[maybe_unused]] constexpr int kPScale = 127 - 8;          // E8M0 scale 2^-8 of the quantized softmax weights
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -204,9 +207,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
     const float c_exp = prescale ? 1.0f : a.scale * kLog2e;
 
     // Stage loads: slot (wave + 4j) * 64 + lane of a tile is chunk p of row r.
-    uint32_t voff[2];
+    uint32_t voff[kMxLPW];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kMxLPW; ++j) {
         const int slot = (wave + j * kMxWaves) * 64 + lane;
         const int r = slot >> 3, p = slot & 7;
         voff[j] = (uint32_t)r * rsb + (uint32_t)((p ^ swz8(r)) << 4);
@@ -290,9 +293,10 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
         const char* Vseq = (const char*)a.v8 + ko * rs + (int64_t)h * kMxD;
         const int64_t kblk0 = a.k_soff[b];
 
-        // Stage kt: K and V rows [64kt, 64kt + 64) into LDS; the K scale words of
-        // its two key blocks and the V scale word of this lane's key block.
-        auto issue = [&](int kt, char* kdst, char* vdst, uint32_t (&ksw)[2], uint32_t& vsw) {
+        // Stage kt: K and V rows [KT kt, KT kt + KT) into LDS; the K scale words of
+        // its key blocks and the V scale words of this lane's key block in each
+        // 64-key half.
+        auto issue = [&](int kt, char* kdst, char* vdst, uint32_t (&ksw)[kMxNKB], uint32_t (&vsw)[kMxNKH]) {
             const int kbase = kt * kMxKT;
             const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)min(max(Lk - kbase, 0), kMxKT) * rsb);
             const __amdgpu_buffer_rsrc_t rk =
@@ -300,29 +304,33 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
             const __amdgpu_buffer_rsrc_t rv =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(Vseq + (int64_t)kbase * rsb), (short)0, (int)nrec, 0x00020000);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < kMxLPW; ++j) {
                 const int inst = wave + j * kMxWaves;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_char*)kdst + inst * 1024, 16, voff[j], 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_char*)vdst + inst * 1024, 16, voff[j], 0, 0, 0);
             }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int kb = 2 * kt + nb;
+            for (int nb = 0; nb < kMxNKB; ++nb) {
+                const int kb = kMxNKB * kt + nb;
                 ksw[nb] = kb < nkblk ? *(const uint32_t*)(a.ks + ((kblk0 + kb) * a.H + h) * 4) : 0x7f7f7f7fu;
             }
-            const int vb = 2 * kt + g;
-            vsw = vb < nkblk ? *(const uint32_t*)(a.vs + ((kblk0 + vb) * a.H + h) * 4) : 0x7f7f7f7fu;
+#pragma unroll
+            for (int kh = 0; kh < kMxNKH; ++kh) {
+                const int vb = kMxNKB * kt + 2 * kh + g;
+                vsw[kh] = vb < nkblk ? *(const uint32_t*)(a.vs + ((kblk0 + vb) * a.H + h) * 4) : 0x7f7f7f7fu;
+            }
         };
 
-        auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn, const uint32_t (&ksc)[2],
-                         uint32_t vsc, uint32_t (&ksn)[2], uint32_t& vsn) {
+        auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn,
+                         const uint32_t (&ksc)[kMxNKB], const uint32_t (&vsc)[kMxNKH], uint32_t (&ksn)[kMxNKB],
+                         uint32_t (&vsn)[kMxNKH]) {
             if (kt + 1 < kt_hi) issue(kt + 1, kn, vn, ksn, vsn);
             const int kw0 = kt * kMxKT;
             const bool skip = wave_skips(vis, row_ok, kw0, kMxKT);
             if (!skip) {
-                floatx16 sacc[2];
+                floatx16 sacc[kMxNKB];
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
+                for (int nb = 0; nb < kMxNKB; ++nb) {
                     sacc[nb] = floatx16{};
                     const char* kblk = kl + nb * 32 * kMxRowB;
 #pragma unroll
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                 }
                 const bool need_mask = wave_needs_mask(vis, row_ok, kw0, kMxKT);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < kMxNKB; ++nb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float x = prescale ? sacc[nb][r] * (a.scale * kLog2e) : sacc[nb][r];
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                     }
                 float mx = -INFINITY;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < kMxNKB; ++nb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
                 mx = halves_max(mx) * c_exp;
@@ -358,9 +366,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                 }
                 const float msub = m_run == -INFINITY ? 0.0f : m_run;
                 float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                v8i pf;
+                v8i pf[kMxNKH];
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < kMxNKB; ++nb)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         float p4[4];
@@ -370,26 +378,33 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                             lsum[e] += p;
                             p4[e] = p * 256.0f;
                         }
-                        pf[4 * nb + q] = (int)pack4(p4[0], p4[1], p4[2], p4[3]);
+                        pf[nb >> 1][4 * (nb & 1) + q] = (int)pack4(p4[0], p4[1], p4[2], p4[3]);
                     }
                 l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 #pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const v2i t0 = read_tr8(vl + toff[db][0]);
-                    const v2i t1 = read_tr8(vl + toff[db][1]);
-                    const v2i t2 = read_tr8(vl + toff[db][2]);
-                    const v2i t3 = read_tr8(vl + toff[db][3]);
-                    const v8i va = v8i{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
-                    const int vsb = (int)((vsc >> (8 * db)) & 0xff);
-                    oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf, oacc[db], 0, 0, 0, vsb, 0,
-                                                                                kPScale);
+                for (int kh = 0; kh < kMxNKH; ++kh) {
+                    const char* vh = vl + kh * 64 * kMxRowB;
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        const v2i t0 = read_tr8(vh + toff[db][0]);
+                        const v2i t1 = read_tr8(vh + toff[db][1]);
+                        const v2i t2 = read_tr8(vh + toff[db][2]);
+                        const v2i t3 = read_tr8(vh + toff[db][3]);
+                        const v8i va = v8i{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+                        const int vsb = (int)((vsc[kh] >> (8 * db)) & 0xff);
+                        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[kh], oacc[db], 0, 0, 0, vsb,
+                                                                                    0, kPScale);
+                    }
                 }
             }
             __syncthreads();
         };
 
-        uint32_t ks0[2], ks1[2], vs0 = 0, vs1 = 0;
-        ks0[0] = ks0[1] = ks1[0] = ks1[1] = 0;
+        uint32_t ks0[kMxNKB], ks1[kMxNKB], vs0[kMxNKH], vs1[kMxNKH];
+#pragma unroll
+        for (int i = 0; i < kMxNKB; ++i) ks0[i] = ks1[i] = 0;
+#pragma unroll
+        for (int i = 0; i < kMxNKH; ++i) vs0[i] = vs1[i] = 0;
         if (kt_hi > kt_lo) {
             issue(kt_lo, lds_k0, lds_v0, ks0, vs0);
             __syncthreads();
