@@ -25,8 +25,8 @@
  *     count of the sequence;
  *   - GELU is the tanh form (the pages name GELU's tanh);
  *   - the ALU-only GELU of the same section (ORA_GELU_TAYLOR) is the Taylor
- *     polynomial of that tanh form about 0 through x^6 (the pages' "6th-order
- *     Taylor expansion"), used where QK-norm keeps |scale q.k| small: it is
+ *     polynomial of that tanh form about 0 through x^6 (the pages' Taylor
+ *     expansion of order 6), used where QK-norm keeps |scale q.k| small: it is
  *     within 1.2e-3 of the tanh form for |x| <= 1;
  *   - causal is top-left aligned: key j is visible to query i iff j <= i;
  *   - a window W > 0 keeps W keys including the query's own position:
