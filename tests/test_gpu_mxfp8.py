@@ -156,3 +156,24 @@ def test_rejects_unsupported_head_dim():
     q, k, v = _quantized(w)
     with pytest.raises(RuntimeError):
         run_mx(w, q, k, v, False, 0)
+
+
+def test_quantizer_many_sequences():
+    # more sequences than the prefix kernel's threads: each thread takes several
+    rng = np.random.default_rng(2400)
+    lengths = rng.integers(0, 70, size=2600)
+    w = W.make_case(lengths, H=2, d=64, dtype=W.BF16, seed=2401)
+    say(f"[mx quant] B={w.B} T={w.q.shape[0]}")
+    r8, rsc, rsoff = oracle.mxfp8_quantize(w.q, w.q_offsets)
+    g8, gsc, gsoff = ja.mxfp8_quantize(to_dev(w.q), to_dev(w.q_offsets))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gsoff.cpu().numpy(), rsoff)
+    np.testing.assert_array_equal(g8.cpu().numpy(), r8)
+    np.testing.assert_array_equal(gsc.cpu().numpy()[:rsoff[-1]], rsc)
+
+
+def test_many_short_sequences_fwd():
+    rng = np.random.default_rng(2500)
+    lengths = rng.integers(0, 90, size=400)
+    w = W.make_case(lengths, H=2, d=128, dtype=W.BF16, seed=2501)
+    check(w, True, 0, what="short")
