@@ -161,20 +161,22 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
         const bool valid = f < f_hi;
         int b = 0, t = 0, bin = -1;
         if (valid) bin = bin_of(f, &b, &t);
+        // Every lane reads its bin's next free position, learns which lanes share
+        // its bin (a register-only loop over the distinct bins of the chunk), and
+        // the lowest such lane advances the bin's position by their count.
+        const int base = valid ? cnt[w * kSchedBins + bin] : 0;
         uint64_t pending = __ballot(valid);
-        int pos = 0;
+        uint64_t mine = 0;
         while (pending) {
             const int leader = __ffsll((unsigned long long)pending) - 1;
-            const int lbin = __shfl(bin, leader);
+            const int lbin = __builtin_amdgcn_readlane(bin, leader);
             const uint64_t same = __ballot(valid && bin == lbin);
-            const int base = cnt[w * kSchedBins + lbin];
-            if (valid && bin == lbin) {
-                const uint64_t below = same & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
-                pos = base + __popcll(below);
-            }
-            if (lane == leader) cnt[w * kSchedBins + lbin] = base + __popcll(same);
+            if (valid && bin == lbin) mine = same;
             pending &= ~same;
         }
+        const uint64_t below = mine & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
+        const int pos = base + __popcll(below);
+        if (valid && below == 0) cnt[w * kSchedBins + bin] = base + __popcll(mine);
         if (valid) {
             a.items[2 * pos] = b;
             a.items[2 * pos + 1] = t;
