@@ -246,6 +246,13 @@ def jagged_attn_fwd_mxfp8(q8, q_scales, q_scale_offsets, k8, k_scales, k_scale_o
     Tq, H, d = q8.shape
     Tk = k8.shape[0]
     B = q_offsets.numel() - 1
+    if k8.shape[1:] != (H, d) or v8.shape != k8.shape:
+        raise ValueError("k8 and v8 must be [Tk, H, d] with q8's H and d")
+    for name, t in (("q_scales", q_scales), ("k_scales", k_scales), ("v_scales", v_scales)):
+        if t.shape[1:] != (H, d // 32):
+            raise ValueError(f"{name} must be [blocks, H, d/32]")
+    if k_offsets.numel() != B + 1 or q_scale_offsets.numel() != B + 1 or k_scale_offsets.numel() != B + 1:
+        raise ValueError("offsets and scale offsets must all have B+1 entries")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
