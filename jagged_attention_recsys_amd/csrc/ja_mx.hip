@@ -364,7 +364,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                     for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
                     m_run = m_new;
                 }
-                const float msub = m_run == -INFINITY ? 0.0f : m_run;
+                // Weights come out of the exponential already scaled by 2^8 (the E4M3
+                // scale of P); the running sum carries the same factor.
+                const float msub = (m_run == -INFINITY ? 0.0f : m_run) - 8.0f;
                 float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                 v8i pf[kMxNKH];
 #pragma unroll
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                         for (int e = 0; e < 4; ++e) {
                             const float p = fast_exp2(fmaf(sacc[nb][4 * q + e], c_exp, -msub));
                             lsum[e] += p;
-                            p4[e] = p * 256.0f;
+                            p4[e] = p;
                         }
                         pf[nb >> 1][4 * (nb & 1) + q] = (int)pack4(p4[0], p4[1], p4[2], p4[3]);
                     }
@@ -416,8 +418,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
 
         if (tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
 
-        const float l_tot = halves_sum(l_run);
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        const float l_tot = halves_sum(l_run);  // 2^8 times the softmax normaliser
+        const float inv = l_tot > 0.0f ? 256.0f / l_tot : 0.0f;
         if (row_ok) {
             bf16* dst = (bf16*)a.out + (qo + my_row) * (int64_t)a.H * kMxD + (int64_t)h * kMxD + 4 * g;
 #pragma unroll
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                     store4<bf16>(dst + 32 * i + 8 * j, oacc[i][4 * j] * inv, oacc[i][4 * j + 1] * inv,
                                  oacc[i][4 * j + 2] * inv, oacc[i][4 * j + 3] * inv);
             if (a.lse != nullptr && g == 0)
-                a.lse[(qo + my_row) * a.H + h] = l_tot > 0.0f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+                a.lse[(qo + my_row) * a.H + h] = l_tot > 0.0f ? (m_run - 8.0f) * kLn2 + logf(l_tot) : -INFINITY;
         }
     }
 #else
