@@ -70,8 +70,10 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 }
 
 // Four floats (already scaled, within +-448) to four E4M3 codes, nearest even.
+// The first conversion writes the low half, the second the high half, so the
+// word the first one starts from is irrelevant (a's own bits: no extra move).
 __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)__float_as_uint(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -177,10 +179,12 @@ __device__ __forceinline__ int swz8(int row) { return (((row >> 1) & 3) << 1) | 
 // keys 16g..16g+15 in register order.
 __device__ __forceinline__ int key_of_slot(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ v8i read_k(const char* blk, int o0, int o1) {
-    const u32x4 lo = *(const u32x4*)(blk + o0);
-    const u32x4 hi = *(const u32x4*)(blk + o1);
-    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    const i32x4 lo = *(const i32x4*)(blk + o0);
+    const i32x4 hi = *(const i32x4*)(blk + o1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ v2i read_tr8(const char* p) {
@@ -340,15 +344,20 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                             read_k(kblk, koff[c][0], koff[c][1]), qf[c], sacc[nb], 0, 0, 0, ksb, 0, qsc[c]);
                     }
                 }
-                const bool need_mask = wave_needs_mask(vis, row_ok, kw0, kMxKT);
+                // Wave-uniform branches around whole loops (not a select per score).
+                if (prescale) {
 #pragma unroll
-                for (int nb = 0; nb < kMxNKB; ++nb)
+                    for (int nb = 0; nb < kMxNKB; ++nb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float x = prescale ? sacc[nb][r] * (a.scale * kLog2e) : sacc[nb][r];
-                        if (need_mask) x = vis.has(kw0 + nb * 32 + 16 * g + r) ? x : -INFINITY;
-                        sacc[nb][r] = x;
-                    }
+                        for (int r = 0; r < 16; ++r) sacc[nb][r] *= a.scale * kLog2e;
+                }
+                if (wave_needs_mask(vis, row_ok, kw0, kMxKT)) {
+#pragma unroll
+                    for (int nb = 0; nb < kMxNKB; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            sacc[nb][r] = vis.has(kw0 + nb * 32 + 16 * g + r) ? sacc[nb][r] : -INFINITY;
+                }
                 float mx = -INFINITY;
 #pragma unroll
                 for (int nb = 0; nb < kMxNKB; ++nb)
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                 // Weights come out of the exponential already scaled by 2^8 (the E4M3
                 // scale of P); the running sum carries the same factor.
                 const float msub = (m_run == -INFINITY ? 0.0f : m_run) - 8.0f;
-                float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                float lsum[4];
                 v8i pf[kMxNKH];
 #pragma unroll
                 for (int nb = 0; nb < kMxNKB; ++nb)
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float p = fast_exp2(fmaf(sacc[nb][4 * q + e], c_exp, -msub));
-                            lsum[e] += p;
+                            lsum[e] = (nb == 0 && q == 0) ? p : lsum[e] + p;
                             p4[e] = p;
                         }
                         pf[nb >> 1][4 * (nb & 1) + q] = (int)pack4(p4[0], p4[1], p4[2], p4[3]);
@@ -388,11 +397,11 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                     const char* vh = vl + kh * 64 * kMxRowB;
 #pragma unroll
                     for (int db = 0; db < 4; ++db) {
-                        const v2i t0 = read_tr8(vh + toff[db][0]);
-                        const v2i t1 = read_tr8(vh + toff[db][1]);
-                        const v2i t2 = read_tr8(vh + toff[db][2]);
-                        const v2i t3 = read_tr8(vh + toff[db][3]);
-                        const v8i va = v8i{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+                        const i32x4 t01 = __builtin_shufflevector(read_tr8(vh + toff[db][0]),
+                                                                  read_tr8(vh + toff[db][1]), 0, 1, 2, 3);
+                        const i32x4 t23 = __builtin_shufflevector(read_tr8(vh + toff[db][2]),
+                                                                  read_tr8(vh + toff[db][3]), 0, 1, 2, 3);
+                        const v8i va = __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
                         const int vsb = (int)((vsc[kh] >> (8 * db)) & 0xff);
                         oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[kh], oacc[db], 0, 0, 0, vsb,
                                                                                     0, kPScale);
