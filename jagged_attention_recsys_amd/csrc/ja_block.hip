@@ -71,15 +71,24 @@ __device__ __forceinline__ float tile_softmax(floatx16 (&s)[2], bool nb1, bool n
                                               int k0, int grp, float scale, float& m2) {
     const bool prescale = !(scale > 0.0f);
     const float c_exp = prescale ? 1.0f : scale * kLog2e;
+    // Wave-uniform branches around whole loops, not selects per score.
+    if (prescale) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = prescale ? s[nb][r] * (scale * kLog2e) : s[nb][r];
-            if (need_mask) x = vis.has(k0 + nb * 32 + key_of_reg<8>(grp, r)) ? x : -INFINITY;
-            if (nb == 1 && !nb1) x = -INFINITY;
-            s[nb][r] = x;
-        }
+            for (int r = 0; r < 16; ++r) s[nb][r] *= scale * kLog2e;
+    }
+    if (need_mask) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[nb][r] = vis.has(k0 + nb * 32 + key_of_reg<8>(grp, r)) ? s[nb][r] : -INFINITY;
+    }
+    if (!nb1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[1][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)

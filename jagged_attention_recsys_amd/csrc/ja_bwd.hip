@@ -178,11 +178,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
                             pointwise_grad<ACT>(sacc[r] * a.scale, act, dact);
                             g = dact * dpacc[r] * inv_lk;
                         }
-                        if (need_mask) {
-                            const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
-                            g = vis.has(key) ? g : 0.0f;
-                        }
                         sacc[r] = g;
+                    }
+                    // One wave-uniform branch per block, not a select per element.
+                    if (need_mask) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            sacc[r] = vis.has(kw0 + nb * 32 + key_of_reg<KP>(grp, r)) ? sacc[r] : 0.0f;
                     }
 #pragma unroll
                     for (int t = 0; t < C::NT; ++t) dsf[nb][t] = to_frag<T>(sacc, KP * t);
@@ -377,14 +379,17 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
                         p = act * inv_lk;
                         g = dact * dpacc[r] * inv_lk;
                     }
-                    if (need_mask) {
-                        const int q = qb0 + key_of_reg<KP>(grp, r);
-                        const bool ok = vis.has(q);
-                        p = ok ? p : 0.0f;
-                        g = ok ? g : 0.0f;
-                    }
                     sacc[r] = p;
                     dsacc[r] = g;
+                }
+                // One wave-uniform branch per block, not a select per element.
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const bool ok = vis.has(qb0 + key_of_reg<KP>(grp, r));
+                        sacc[r] = ok ? sacc[r] : 0.0f;
+                        dsacc[r] = ok ? dsacc[r] : 0.0f;
+                    }
                 }
 #pragma unroll
                 for (int t = 0; t < C::NT; ++t) {
