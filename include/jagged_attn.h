@@ -235,9 +235,13 @@ ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Tile shape the forward uses for these sizes: bm query rows per work item, bn
- * keys per scheduler cost unit. Host only; returns JA_ERR_UNSUPPORTED for
+ * keys per scheduler cost unit. The layout, and so the shape, depends only on
+ * B, d, Tq, Tk, act and dtype: short queries (Tq <= 48 B) take 32-row items;
+ * short keys with long queries (Tk <= 64 B and Tq >= 512 B, bf16) take items of
+ * four consecutive 128-row query tiles that share one resident key/value stage;
+ * everything else 128-row items. Host only; returns JA_ERR_UNSUPPORTED for
  * unsupported d / dtype / act. */
-ja_status_t ja_fwd_tile_shape(int32_t B, int32_t d, int64_t Tq, int32_t act, int32_t dtype,
+ja_status_t ja_fwd_tile_shape(int32_t B, int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t dtype,
                               int32_t* bm, int32_t* bn);
 
 /* Checks offsets on the device (non-decreasing, [0] == 0, [B] == T) and waits

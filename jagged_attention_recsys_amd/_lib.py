@@ -33,7 +33,7 @@ SIGNATURES = {
                                      _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "ja_fwd_schedule": (_i32, [_vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
                                _vp, _sz, _vp]),
-    "ja_fwd_tile_shape": (_i32, [_i32, _i32, _i64, _i32, _i32, _vp, _vp]),
+    "ja_fwd_tile_shape": (_i32, [_i32, _i32, _i64, _i64, _i32, _i32, _vp, _vp]),
     "ja_validate_offsets": (_i32, [_vp, _i32, _i64, _vp]),
     "ja_set_profile_events": (None, [_vp, _vp]),
     "ja_status_string": (ctypes.c_char_p, [_i32]),

@@ -33,16 +33,22 @@ size_t align_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 struct FwdPlan {
-    bool split;
+    int layout;  // kLayoutStandard / kLayoutSplit / kLayoutChunked
     FwdShape shape;
     int64_t max_pairs;
     size_t off_tbase, off_items, bytes;
 };
 
-// Short-query batches (mean query length <= 48, e.g. pooled attention seeds) use
-// the split layout; the choice depends only on sizes, never on device data.
-bool use_split(int32_t B, int64_t Tq, int32_t dtype) {
-    return dtype == JA_BF16 && B > 0 && Tq <= 48LL * B;
+// Forward layout from the sizes alone (never from device data): short-query batches
+// (mean query length <= 48, e.g. pooled attention seeds) use the split layout;
+// short keys and values with long queries (mean key length <= 64, one stage, and
+// mean query length >= 512, e.g. cross-attention to a few events) use the chunked
+// layout. Every layout is correct for any lengths; the choice only affects speed.
+int fwd_layout(int32_t B, int64_t Tq, int64_t Tk, int32_t dtype) {
+    if (dtype != JA_BF16 || B <= 0) return kLayoutStandard;
+    if (Tq <= 48LL * B) return kLayoutSplit;
+    if (Tk <= 64LL * B && Tq >= 512LL * B) return kLayoutChunked;
+    return kLayoutStandard;
 }
 
 ja_status_t check_common(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
@@ -54,9 +60,10 @@ ja_status_t check_common(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk
     return JA_OK;
 }
 
-ja_status_t plan_fwd(int32_t B, int32_t H, int32_t d, int64_t Tq, int32_t act, int32_t dtype, FwdPlan* p) {
-    p->split = use_split(B, Tq, dtype);
-    p->shape = fwd_shape(dtype, d, act, p->split);
+ja_status_t plan_fwd(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t dtype,
+                     FwdPlan* p) {
+    p->layout = fwd_layout(B, Tq, Tk, dtype);
+    p->shape = fwd_shape(dtype, d, act, p->layout);
     if (p->shape.bm <= 0) return JA_ERR_UNSUPPORTED;
     p->max_pairs = (Tq + p->shape.bm - 1) / p->shape.bm + B;
     if (p->max_pairs * (int64_t)H >= INT32_MAX) return JA_ERR_UNSUPPORTED;
@@ -116,13 +123,13 @@ int device_cus() {
     return n;
 }
 
-int fwd_occupancy(int dtype, int d, int act, bool split) {
-    static std::atomic<int> cache[2][3][4][2];
+int fwd_occupancy(int dtype, int d, int act, int layout) {
+    static std::atomic<int> cache[2][3][4][3];
     const int di = d == 32 ? 0 : d == 64 ? 1 : 2;
-    std::atomic<int>& slot = cache[dtype][di][act][split ? 1 : 0];
+    std::atomic<int>& slot = cache[dtype][di][act][layout];
     int n = slot.load(std::memory_order_relaxed);
     if (n > 0) return n;
-    n = fwd_blocks_per_cu(dtype, d, act, split);
+    n = fwd_blocks_per_cu(dtype, d, act, layout);
     slot.store(n, std::memory_order_relaxed);
     return n;
 }
@@ -179,7 +186,7 @@ ja_status_t fwd_impl(const void* q, const void* k, const void* v, const int32_t*
         !aligned(q_offsets, 4) || !aligned(k_offsets, 4) || !aligned(workspace, 16))
         return JA_ERR_INVALID_ARG;
     FwdPlan p;
-    st = plan_fwd(B, H, d, Tq, act, dtype, &p);
+    st = plan_fwd(B, H, d, Tq, Tk, act, dtype, &p);
     if (st != JA_OK) return st;
     if (workspace_bytes < p.bytes) return JA_ERR_WORKSPACE;
 
@@ -205,11 +212,11 @@ ja_status_t fwd_impl(const void* q, const void* k, const void* v, const int32_t*
     fa.bsh = bsh;
     fa.scale = scale;
     const int64_t max_items = p.max_pairs * H;
-    int64_t grid = (int64_t)device_cus() * fwd_occupancy(dtype, d, act, p.split);
+    int64_t grid = (int64_t)device_cus() * fwd_occupancy(dtype, d, act, p.layout);
     if (grid > max_items) grid = max_items;
     if (grid < 1) grid = 1;
     if (g_prof_before && hipEventRecord(g_prof_before, s) != hipSuccess) return JA_ERR_HIP;
-    if (launch_fwd(fa, dtype, d, act, p.split, (int)grid, s) != hipSuccess) return JA_ERR_HIP;
+    if (launch_fwd(fa, dtype, d, act, p.layout, (int)grid, s) != hipSuccess) return JA_ERR_HIP;
     if (g_prof_after && hipEventRecord(g_prof_after, s) != hipSuccess) return JA_ERR_HIP;
     return JA_OK;
 }
@@ -348,7 +355,7 @@ size_t ja_fwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_
     (void)causal;
     if (check_common(B, H, d, Tq, Tk, act, window, 1.0f, dtype) != JA_OK) return 0;
     FwdPlan p;
-    if (plan_fwd(B, H, d, Tq, act, dtype, &p) != JA_OK) return 0;
+    if (plan_fwd(B, H, d, Tq, Tk, act, dtype, &p) != JA_OK) return 0;
     return p.bytes;
 }
 
@@ -377,7 +384,7 @@ size_t ja_block_attn_workspace_size(int32_t B, int32_t H, int32_t d, int64_t T, 
     if (check_common(B, H, d, T, T, JA_ACT_SOFTMAX, 0, 1.0f, dtype) != JA_OK) return 0;
     size_t bytes = 0;
     FwdPlan fp;
-    if (plan_fwd(B, H, d, T, JA_ACT_SOFTMAX, dtype, &fp) != JA_OK) return 0;
+    if (plan_fwd(B, H, d, T, T, JA_ACT_SOFTMAX, dtype, &fp) != JA_OK) return 0;
     bytes = fp.bytes;
     if (bwd_supported(dtype, d, JA_ACT_SOFTMAX)) {
         BwdPlan bp;
@@ -577,7 +584,7 @@ ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets, 
     if (st != JA_OK) return st;
     if (!q_offsets || !k_offsets || !items || !count || !workspace) return JA_ERR_INVALID_ARG;
     FwdPlan p;
-    st = plan_fwd(B, H, d, Tq, act, dtype, &p);
+    st = plan_fwd(B, H, d, Tq, Tk, act, dtype, &p);
     if (st != JA_OK) return st;
     if (max_items < p.max_pairs) return JA_ERR_INVALID_ARG;
     if (workspace_bytes < p.bytes) return JA_ERR_WORKSPACE;
@@ -588,11 +595,11 @@ ja_status_t ja_fwd_schedule(const int32_t* q_offsets, const int32_t* k_offsets, 
     return JA_OK;
 }
 
-ja_status_t ja_fwd_tile_shape(int32_t B, int32_t d, int64_t Tq, int32_t act, int32_t dtype, int32_t* bm,
-                              int32_t* bn) {
-    if (!bm || !bn || B < 0 || Tq < 0) return JA_ERR_INVALID_ARG;
+ja_status_t ja_fwd_tile_shape(int32_t B, int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t dtype,
+                              int32_t* bm, int32_t* bn) {
+    if (!bm || !bn || B < 0 || Tq < 0 || Tk < 0) return JA_ERR_INVALID_ARG;
     if (!fwd_supported(dtype, d, act)) return JA_ERR_UNSUPPORTED;
-    FwdShape s = fwd_shape(dtype, d, act, use_split(B, Tq, dtype));
+    FwdShape s = fwd_shape(dtype, d, act, fwd_layout(B, Tq, Tk, dtype));
     *bm = s.bm;
     *bn = s.bn;
     return JA_OK;

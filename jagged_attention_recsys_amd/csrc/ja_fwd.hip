@@ -50,6 +50,15 @@
 namespace ja {
 namespace {
 
+// A lane value the compiler cannot move out of the enclosing loop. The swizzled
+// LDS addresses of the query and output turnarounds depend on it, so they are
+// computed where they are used instead of being held in registers through the
+// whole stage loop.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 template <typename T, int D, bool SPLIT>
 struct FwdCfg {
     static constexpr int NW = SPLIT ? (D == 128 ? 4 : 8) : 4;  // waves per workgroup
@@ -81,7 +90,7 @@ struct FwdCfg {
     static_assert(D % (2 * KP) == 0 && D % 32 == 0, "unsupported head dim");
 };
 
-template <typename T, int D, int ACT, bool SPLIT, int NTHREADS = FwdCfg<T, D, SPLIT>::THREADS,
+template <typename T, int D, int ACT, bool SPLIT, int CHUNK, int NTHREADS = FwdCfg<T, D, SPLIT>::THREADS,
           int MINB = FwdCfg<T, D, SPLIT>::MIN_BLOCKS>
 __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
     // The body uses gfx950-only types and builtins; the host pass only needs the
@@ -146,10 +155,55 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
         const ItemSeq is = load_item(a.items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
-        const int qt = is.t;
         const int64_t qo = is.qo, ko = is.ko;
         const int Lq = is.Lq, Lk = is.Lk;
-        const int q0 = qt * C::BM;
+        const char* Kseq = Kg + (ko * rs + (int64_t)h * D) * C::ESZ;
+        const char* Vseq = Vg + (ko * rs + (int64_t)h * D) * C::ESZ;
+
+        // Chunked layout (CHUNK > 1, short keys and values): the item is CHUNK
+        // consecutive query tiles of one sequence and head, processed one after the
+        // other. When every row of the chunk sees keys of one stage only, that stage
+        // is loaded once and stays in LDS for all of them, and each tile's queries
+        // are prefetched into registers while the previous tile computes, so the
+        // item streams queries in and outputs out with no per-tile load latency or
+        // barrier ("outer-loop pipelining" for short K/V, GDPA section).
+        const int c0 = is.t * C::BM * CHUNK;  // first query row of the item
+        const int nsub = CHUNK == 1 ? 1 : max(1, min(CHUNK, (Lq - c0 + C::BM - 1) / C::BM));
+        bool resident = false;
+        int rkt = 0;
+        if constexpr (CHUNK > 1) {
+            const ColRange ccr = visible_cols(Lq, Lk, c0, C::BM * CHUNK, causal, window, 0, bsh);
+            rkt = ccr.hi > ccr.lo ? (int)(ccr.lo / C::KT) : 0;
+            resident = ccr.hi > ccr.lo && (int)((ccr.hi + C::KT - 1) / C::KT) == rkt + 1;
+        }
+
+        // Queries of a tile's wave slice as the B operand of S^T = K Q^T.
+        auto load_q = [&](int row, frag (&dst)[C::NS]) __attribute__((always_inline)) {
+            const bool ok = row < Lq;
+            const T* src = Qg + (qo + row) * rs + (int64_t)h * D + KP * grp;
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) dst[s] = ok ? *(const frag*)(src + 2 * KP * s) : Frag<T>::zero();
+        };
+        // Chunked layout: a wave's 32 query rows are read whole (16 bytes per lane,
+        // CPR lanes per row) into registers, one tile ahead, and turned into
+        // B-operand fragments through the wave's quarter of the second stage buffer.
+        constexpr int NRAW = CHUNK > 1 ? C::CPR / 2 : 1;
+        bf16x8 qraw[NRAW];
+        auto load_raw = [&](int row0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int n = 0; n < NRAW; ++n) {
+                const int p = n * 64 + lane, r = p / C::CPR, c = p % C::CPR;
+                qraw[n] = row0 + r < Lq ? *(const bf16x8*)(Qg + (qo + row0 + r) * rs + (int64_t)h * D + c * 8)
+                                        : bf16x8{};
+            }
+        };
+        char* const wreg = (wave < 2 ? lds_k1 : lds_v1) + (wave & 1) * 32 * C::ROWB;  // wave-private
+        frag qf[C::NS];
+        if constexpr (CHUNK > 1) load_raw(c0 + 32 * wq);
+        else load_q(c0 + 32 * wq + col, qf);
+
+        for (int sub = 0; sub < nsub; ++sub) {
+        const int q0 = c0 + sub * C::BM;
         const ColRange cr = visible_cols(Lq, Lk, q0, C::BM, causal, window, 0, bsh);
         const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / C::KT) : 0;
         const int kt_hi = cr.hi > cr.lo ? (int)((cr.hi + C::KT - 1) / C::KT) : 0;
@@ -157,23 +211,27 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
         const int my_row = qw0 + col;
         const bool row_ok = my_row < Lq;
         const VisRange vis = keys_seen_by(my_row, Lk, causal, window, bsh);
-
-        // Queries as the B operand of S^T = K Q^T, kept in registers.
-        frag qf[C::NS];
-        {
-            const bool ok = row_ok;
-            const T* src = Qg + (qo + my_row) * rs + (int64_t)h * D + KP * grp;
+        if constexpr (CHUNK > 1) {
+            // The region is free: the previous tile's output turnaround finished in
+            // this wave's own order, and no stage load targets it before the next
+            // barrier.
+            const int ln = opaque(lane);
 #pragma unroll
-            for (int s = 0; s < C::NS; ++s) qf[s] = ok ? *(const frag*)(src + 2 * KP * s) : Frag<T>::zero();
+            for (int n = 0; n < NRAW; ++n) {
+                const int p = n * 64 + ln, r = p / C::CPR, c = p % C::CPR;
+                *(bf16x8*)(wreg + r * C::ROWB + ((c ^ (r & (C::CPR - 1))) * 16)) = qraw[n];
+            }
+            const int cl = ln & 31, gp = ln >> 5;
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s)
+                qf[s] = *(const frag*)(wreg + cl * C::ROWB + (((gp + 2 * s) ^ (cl & (C::CPR - 1))) * 16));
+            if (sub + 1 < nsub) load_raw(qw0 + C::BM);
         }
 
         floatx16 oacc[C::ND];
 #pragma unroll
         for (int i = 0; i < C::ND; ++i) oacc[i] = floatx16{};
         float m_run = -INFINITY, l_run = 0.0f;
-
-        const char* Kseq = Kg + (ko * rs + (int64_t)h * D) * C::ESZ;
-        const char* Vseq = Vg + (ko * rs + (int64_t)h * D) * C::ESZ;
 
         // Stage kt -> (kdst, vdst): K and V rows [kt*KT, kt*KT + KT) of this
         // sequence and head; rows at or past Lk read as zero.
@@ -187,8 +245,7 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
 
         // Consume the stage in (kl, vl) while the next one (if any) streams into
         // (kn, vn).
-        auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
-            if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
+        auto compute = [&](int kt, const char* kl, const char* vl) {
             const int kw0 = kt * C::KT + wk * 32 * C::NB;  // first key of this wave's blocks
             const bool skip = wave_skips(vis, row_ok, kw0, 32 * C::NB);
             if (!skip) {
@@ -274,19 +331,33 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
                             oacc[db] = M::run(C::KVTile::read_tr(vblk, t, voff, db), pf[nb][t], oacc[db]);
                 }
             }
+        };
+        auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
+            if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
+            compute(kt, kl, vl);
             __syncthreads();
         };
 
-        if (kt_hi > kt_lo) {
-            issue(kt_lo, lds_k0, lds_v0);
-            __syncthreads();
-        }
-        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-            stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
-            if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+        if (CHUNK > 1 && resident) {
+            // The chunk's one stage: loaded by the first tile, read by all. A tile
+            // whose rows see no key (kt_hi == kt_lo) skips it.
+            if (sub == 0) {
+                issue(rkt, lds_k0, lds_v0);
+                __syncthreads();
+            }
+            if (kt_hi > kt_lo) compute(rkt, lds_k0, lds_v0);
+        } else {
+            if (kt_hi > kt_lo) {
+                issue(kt_lo, lds_k0, lds_v0);
+                __syncthreads();
+            }
+            for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+                stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+                if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+            }
         }
 
-        if (tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
+        if (sub == nsub - 1 && tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
 
         // Split layout: merge the key slices (the loop ended on a barrier, or no
         // stage was loaded, so the stage buffers are free). Softmax first agrees on
@@ -339,79 +410,127 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
             } else {
                 inv = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
             }
+            bool staged = false;
+            if constexpr (!SPLIT && KP == 8) {
+                // The second stage buffer is free here (the stage loop ended on a
+                // barrier, resident chunks never load it): each wave turns its 32
+                // output rows around in its own quarter of it (16-byte chunks
+                // XOR-swizzled by row) and writes whole rows, 16 bytes per lane,
+                // instead of 8-byte pieces of 32 rows per instruction.
+                {
+                    staged = true;
+                    char* reg = wreg;
+                    const int ln = opaque(lane), cl = ln & 31, gp = ln >> 5;
+#pragma unroll
+                    for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            bf16x4 v4;
+                            v4[0] = (bf16)(oacc[i][4 * j] * inv);
+                            v4[1] = (bf16)(oacc[i][4 * j + 1] * inv);
+                            v4[2] = (bf16)(oacc[i][4 * j + 2] * inv);
+                            v4[3] = (bf16)(oacc[i][4 * j + 3] * inv);
+                            const int pc = (4 * i + j) ^ (cl & (C::CPR - 1));
+                            *(bf16x4*)(reg + cl * C::ROWB + pc * 16 + gp * 8) = v4;
+                        }
+#pragma unroll
+                    for (int n = 0; n < C::CPR / 2; ++n) {
+                        const int p = n * 64 + ln, r = p / C::CPR, c = p % C::CPR;
+                        const bf16x8 v8 = *(const bf16x8*)(reg + r * C::ROWB + ((c ^ (r & (C::CPR - 1))) * 16));
+                        if (qw0 + r < Lq) *(bf16x8*)(Og + (qo + qw0 + r) * rs + (int64_t)h * D + c * 8) = v8;
+                    }
+                }
+            }
             if (my_row < Lq) {
-                T* dst = Og + (qo + my_row) * rs + (int64_t)h * D + 4 * grp;
+                if (!staged) {
+                    T* dst = Og + (qo + my_row) * rs + (int64_t)h * D + 4 * grp;
 #pragma unroll
-                for (int i = 0; i < C::ND; ++i)
+                    for (int i = 0; i < C::ND; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        store4<T>(dst + 32 * i + 8 * j, oacc[i][4 * j] * inv, oacc[i][4 * j + 1] * inv,
-                                  oacc[i][4 * j + 2] * inv, oacc[i][4 * j + 3] * inv);
+                        for (int j = 0; j < 4; ++j)
+                            store4<T>(dst + 32 * i + 8 * j, oacc[i][4 * j] * inv, oacc[i][4 * j + 1] * inv,
+                                      oacc[i][4 * j + 2] * inv, oacc[i][4 * j + 3] * inv);
+                }
                 if (ACT == ACT_SOFTMAX && a.lse != nullptr && grp == 0)
                     a.lse[(qo + my_row) * a.H + h] = lse_val;
             }
         }
+        }  // sub-tiles
     }
 #else
     (void)a;
 #endif
 }
 
-template <typename T, int D, int ACT, bool SPLIT>
+// Layouts: 0 standard, 1 split (short queries), 2 chunked (short keys and values).
+constexpr int kChunk = 4;  // query tiles per item in the chunked layout
+template <int LAYOUT> struct LayoutOf {
+    static constexpr bool split = LAYOUT == 1;
+    static constexpr int chunk = LAYOUT == 2 ? kChunk : 1;
+};
+
+template <typename T, int D, int ACT, int LAYOUT>
 hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((ja_fwd_kernel<T, D, ACT, SPLIT>), dim3(grid), dim3(FwdCfg<T, D, SPLIT>::THREADS), 0,
-                       stream, a);
+    using L = LayoutOf<LAYOUT>;
+    hipLaunchKernelGGL((ja_fwd_kernel<T, D, ACT, L::split, L::chunk>), dim3(grid),
+                       dim3(FwdCfg<T, D, L::split>::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int D, int ACT, bool SPLIT>
+template <typename T, int D, int ACT, int LAYOUT>
 int occupancy_one() {
+    using L = LayoutOf<LAYOUT>;
     int n = 0;
-    const void* fn = reinterpret_cast<const void*>(&ja_fwd_kernel<T, D, ACT, SPLIT>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, FwdCfg<T, D, SPLIT>::THREADS, 0) != hipSuccess)
+    const void* fn = reinterpret_cast<const void*>(&ja_fwd_kernel<T, D, ACT, L::split, L::chunk>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, FwdCfg<T, D, L::split>::THREADS, 0) != hipSuccess)
         return 1;
     return n > 0 ? n : 1;
 }
 
-// Dispatch over (dtype, d, act, split) to a callable template F<T, D, ACT, SPLIT>.
-template <template <typename, int, int, bool> class F, typename R, typename... Args>
-R dispatch(int dtype, int d, int act, bool split, R fail, Args... args) {
-#define JA_ACTS(T, D, S)                                                 \
-    switch (act) {                                                       \
-        case ACT_SOFTMAX: return F<T, D, ACT_SOFTMAX, S>::call(args...); \
-        case ACT_SILU: return F<T, D, ACT_SILU, S>::call(args...);       \
-        case ACT_GELU: return F<T, D, ACT_GELU, S>::call(args...);       \
-        case ACT_GELU_TAYLOR: return F<T, D, ACT_GELU_TAYLOR, S>::call(args...); \
-        default: return fail;                                            \
+// Dispatch over (dtype, d, act, layout) to a callable template F<T, D, ACT, LAYOUT>.
+// The split and chunked layouts exist for bf16 only.
+template <template <typename, int, int, int> class F, typename R, typename... Args>
+R dispatch(int dtype, int d, int act, int layout, R fail, Args... args) {
+#define JA_ACTS(T, D, LY)                                                 \
+    switch (act) {                                                        \
+        case ACT_SOFTMAX: return F<T, D, ACT_SOFTMAX, LY>::call(args...); \
+        case ACT_SILU: return F<T, D, ACT_SILU, LY>::call(args...);       \
+        case ACT_GELU: return F<T, D, ACT_GELU, LY>::call(args...);       \
+        case ACT_GELU_TAYLOR: return F<T, D, ACT_GELU_TAYLOR, LY>::call(args...); \
+        default: return fail;                                             \
     }
-#define JA_DIMS(T, S)              \
-    switch (d) {                   \
-        case 32: JA_ACTS(T, 32, S)   \
-        case 64: JA_ACTS(T, 64, S)   \
-        case 128: JA_ACTS(T, 128, S) \
-        default: return fail;      \
+#define JA_DIMS(T, LY)              \
+    switch (d) {                    \
+        case 32: JA_ACTS(T, 32, LY)   \
+        case 64: JA_ACTS(T, 64, LY)   \
+        case 128: JA_ACTS(T, 128, LY) \
+        default: return fail;       \
     }
     if (dtype == 1) {
-        if (split) { JA_DIMS(bf16, true) }
-        JA_DIMS(bf16, false)
+        if (layout == 1) { JA_DIMS(bf16, 1) }
+        if (layout == 2) { JA_DIMS(bf16, 2) }
+        JA_DIMS(bf16, 0)
     }
-    if (dtype == 0) { JA_DIMS(float, false) }
+    if (dtype == 0) { JA_DIMS(float, 0) }
 #undef JA_DIMS
 #undef JA_ACTS
     return fail;
 }
 
-template <typename T, int D, int ACT, bool SPLIT>
+template <typename T, int D, int ACT, int LAYOUT>
 struct LaunchF {
-    static hipError_t call(const FwdArgs* a, int grid, hipStream_t s) { return launch_one<T, D, ACT, SPLIT>(*a, grid, s); }
+    static hipError_t call(const FwdArgs* a, int grid, hipStream_t s) { return launch_one<T, D, ACT, LAYOUT>(*a, grid, s); }
 };
-template <typename T, int D, int ACT, bool SPLIT>
+template <typename T, int D, int ACT, int LAYOUT>
 struct OccF {
-    static int call() { return occupancy_one<T, D, ACT, SPLIT>(); }
+    static int call() { return occupancy_one<T, D, ACT, LAYOUT>(); }
 };
-template <typename T, int D, int ACT, bool SPLIT>
+template <typename T, int D, int ACT, int LAYOUT>
 struct ShapeF {
-    static FwdShape call() { return FwdShape{FwdCfg<T, D, SPLIT>::BM, FwdCfg<T, D, SPLIT>::KT}; }
+    static FwdShape call() {
+        using L = LayoutOf<LAYOUT>;
+        return FwdShape{FwdCfg<T, D, L::split>::BM * L::chunk, FwdCfg<T, D, L::split>::KT};
+    }
 };
 
 }  // namespace
@@ -420,17 +539,17 @@ bool fwd_supported(int dtype, int d, int act) {
     return (dtype == 0 || dtype == 1) && (d == 32 || d == 64 || d == 128) && act >= ACT_SOFTMAX && act <= ACT_GELU_TAYLOR;
 }
 
-FwdShape fwd_shape(int dtype, int d, int act, bool split) {
-    return dispatch<ShapeF, FwdShape>(dtype, d, act, split && dtype == 1, FwdShape{0, 0});
+FwdShape fwd_shape(int dtype, int d, int act, int layout) {
+    return dispatch<ShapeF, FwdShape>(dtype, d, act, dtype == 1 ? layout : 0, FwdShape{0, 0});
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, int act, bool split, int grid, hipStream_t stream) {
-    return dispatch<LaunchF, hipError_t>(dtype, d, act, split && dtype == 1, hipErrorInvalidValue, &a, grid,
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, int act, int layout, int grid, hipStream_t stream) {
+    return dispatch<LaunchF, hipError_t>(dtype, d, act, dtype == 1 ? layout : 0, hipErrorInvalidValue, &a, grid,
                                          stream);
 }
 
-int fwd_blocks_per_cu(int dtype, int d, int act, bool split) {
-    return dispatch<OccF, int>(dtype, d, act, split && dtype == 1, 1);
+int fwd_blocks_per_cu(int dtype, int d, int act, int layout) {
+    return dispatch<OccF, int>(dtype, d, act, dtype == 1 ? layout : 0, 1);
 }
 
 }  // namespace ja

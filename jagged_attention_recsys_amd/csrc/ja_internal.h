@@ -47,19 +47,21 @@ struct FwdArgs {
     float scale;               // applied to Q K^T
 };
 
-// Forward kernel family. `split` selects the short-query layout (one 32-row query
-// tile per workgroup, the four waves splitting the keys) instead of four 32-row
-// query slices sharing each key tile.
+// Forward kernel family. `layout` selects the standard layout (0: four 32-row query
+// slices sharing each key tile), the short-query layout (1: one 32-row query tile
+// per workgroup, the waves splitting the keys) or the short-key layout (2: items of
+// several consecutive query tiles sharing one resident key/value stage).
+enum { kLayoutStandard = 0, kLayoutSplit = 1, kLayoutChunked = 2 };
 struct FwdShape {
     int bm;  // query rows per work item
     int bn;  // keys per stage (scheduler cost unit)
 };
 bool fwd_supported(int dtype, int d, int act);
-FwdShape fwd_shape(int dtype, int d, int act, bool split);
-hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, int act, bool split, int grid,
+FwdShape fwd_shape(int dtype, int d, int act, int layout);
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, int act, int layout, int grid,
                       hipStream_t stream);
 // Workgroups per CU the forward kernel reaches (from the occupancy query).
-int fwd_blocks_per_cu(int dtype, int d, int act, bool split);
+int fwd_blocks_per_cu(int dtype, int d, int act, int layout);
 
 // Softmax backward: dQ pass (query tiles) then dK/dV pass (key tiles).
 struct BwdArgs {

@@ -271,10 +271,11 @@ def jagged_attn_fwd_mxfp8(q8, q_scales, q_scale_offsets, k8, k_scales, k_scale_o
     return out, lse
 
 
-def fwd_tile_shape(B, d, Tq, act="softmax", dtype=torch.bfloat16):
+def fwd_tile_shape(B, d, Tq, Tk, act="softmax", dtype=torch.bfloat16):
     import ctypes
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
-    status = _lib.load().ja_fwd_tile_shape(B, d, Tq, _act(act), DTYPE[dtype], ctypes.byref(bm), ctypes.byref(bn))
+    status = _lib.load().ja_fwd_tile_shape(B, d, Tq, Tk, _act(act), DTYPE[dtype], ctypes.byref(bm),
+                                           ctypes.byref(bn))
     _lib.check("ja_fwd_tile_shape", status)
     return bm.value, bn.value
 
@@ -284,7 +285,7 @@ def fwd_schedule(q_offsets, k_offsets, H, d, Tq, Tk, act="softmax", causal=False
     """Run only the forward's tile scheduler; returns the (sequence, tile) pairs as an int32 [n,2] GPU tensor."""
     lib = _lib.load()
     B = q_offsets.numel() - 1
-    bm, _ = fwd_tile_shape(B, d, Tq, act, dtype)
+    bm, _ = fwd_tile_shape(B, d, Tq, Tk, act, dtype)
     max_items = (Tq + bm - 1) // bm + B
     items = torch.empty((max(max_items, 1), 2), dtype=torch.int32, device=q_offsets.device)
     count = torch.zeros(1, dtype=torch.int32, device=q_offsets.device)

@@ -104,9 +104,25 @@ def test_short_queries_split_layout(d, act, causal, window):
     lk = rng.integers(0, 700, size=B)
     lk[0], lk[1] = 0, 1
     w = W.make_case(lq, lk, H=2, d=d, dtype=W.BF16, seed=d + 1)
-    bm, bn = ja.fwd_tile_shape(w.B, d, w.q.shape[0], act)
+    bm, bn = ja.fwd_tile_shape(w.B, d, w.q.shape[0], w.k.shape[0], act)
     assert bm == 32, "short-query batch should take the split layout"
     check_against_oracle(w, act, causal, window, what="split")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("act,causal,window", [("silu", False, 0), ("gelu", False, 0), ("softmax", False, 0),
+                                               ("softmax", True, 0), ("silu", True, 30), ("softmax", False, 50)])
+def test_short_keys_chunked_layout(d, act, causal, window):
+    # Mean key length <= 64 with mean query length >= 512: items of four 128-row
+    # query tiles. Sequences whose keys fit one stage (Lk <= 64) keep it resident
+    # for the whole item; Lk = 300 crosses stages and takes the streaming path;
+    # partial chunks, single rows, empty queries and empty keys are included.
+    lq = [1100, 1, 0, 512, 513, 640, 2049, 700]
+    lk = [64, 5, 3, 0, 1, 64, 63, 300]
+    w = W.make_case(lq, lk, H=2, d=d, dtype=W.BF16, seed=5 * d + window)
+    bm, bn = ja.fwd_tile_shape(w.B, d, w.q.shape[0], w.k.shape[0], act)
+    assert (bm, bn) == (512, 64), "short-key batch should take the chunked layout"
+    check_against_oracle(w, act, causal, window, what="chunked")
 
 
 def test_workload1_fp32_softmax_and_silu():
@@ -193,7 +209,7 @@ def test_schedule_matches_reference_work_list(n):
     Tq, Tk = w.q.shape[0], w.k.shape[0]
     items = ja.fwd_schedule(to_dev(w.q_offsets), to_dev(w.k_offsets), w.H, w.d, Tq, Tk, w.act, w.causal,
                             w.window).cpu().numpy()
-    bm, bn = ja.fwd_tile_shape(w.B, w.d, Tq, w.act)
+    bm, bn = ja.fwd_tile_shape(w.B, w.d, Tq, Tk, w.act)
     ref, _ = oracle.tile_list(w.q_offsets, w.k_offsets, bm, bn, w.causal, w.window, cap=511)
     assert np.array_equal(items, ref)
 
@@ -207,7 +223,7 @@ def test_schedule_small_cases_with_cap():
         Tq = int(w.q_offsets[-1])
         items = ja.fwd_schedule(to_dev(w.q_offsets), to_dev(w.k_offsets), 1, 32, Tq, Tq, "softmax", causal,
                                 window).cpu().numpy()
-        bm, bn = ja.fwd_tile_shape(w.B, 32, Tq, "softmax")
+        bm, bn = ja.fwd_tile_shape(w.B, 32, Tq, Tq, "softmax")
         ref, _ = oracle.tile_list(w.q_offsets, w.k_offsets, bm, bn, causal, window, cap=511)
         assert np.array_equal(items, ref)
 
@@ -223,7 +239,7 @@ def test_schedule_many_sequences(B):
     Tq, Tk = int(qo[-1]), int(ko[-1])
     for causal, window in [(True, 0), (False, 90)]:
         items = ja.fwd_schedule(to_dev(qo), to_dev(ko), 2, 64, Tq, Tk, "softmax", causal, window).cpu().numpy()
-        bm, bn = ja.fwd_tile_shape(B, 64, Tq, "softmax")
+        bm, bn = ja.fwd_tile_shape(B, 64, Tq, Tk, "softmax")
         ref, _ = oracle.tile_list(qo, ko, bm, bn, causal, window, cap=511)
         assert np.array_equal(items, ref)
 

@@ -91,18 +91,28 @@ def test_workspace_size_grows_with_tiles(lib):
 def test_tile_shape_query(lib):
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
     # standard layout: 4 waves x 32 query rows, 64-key stages
-    assert lib.ja_fwd_tile_shape(64, 128, 70000, 0, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert lib.ja_fwd_tile_shape(64, 128, 70000, 70000, 0, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
     assert (bm.value, bn.value) == (128, 64)
     # short queries (mean <= 48 rows) use the split layout: one 32-row tile, the
     # waves splitting each key stage (8 x 32 keys for d <= 64, 4 x 32 for d = 128)
-    assert lib.ja_fwd_tile_shape(256, 64, 256 * 32, 2, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert lib.ja_fwd_tile_shape(256, 64, 256 * 32, 10 ** 6, 2, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
     assert (bm.value, bn.value) == (32, 256)
-    assert lib.ja_fwd_tile_shape(256, 128, 256 * 32, 0, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert lib.ja_fwd_tile_shape(256, 128, 256 * 32, 10 ** 6, 0, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
     assert (bm.value, bn.value) == (32, 128)
-    # fp32 never splits
-    assert lib.ja_fwd_tile_shape(4, 32, 233, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    # short keys (mean <= 64) with long queries (mean >= 512): items of four
+    # 128-row query tiles sharing one resident 64-key stage
+    assert lib.ja_fwd_tile_shape(128, 128, 128 * 2772, 128 * 64, 1, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert (bm.value, bn.value) == (512, 64)
+    assert lib.ja_fwd_tile_shape(128, 128, 128 * 511, 128 * 64, 1, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
     assert (bm.value, bn.value) == (128, 64)
-    assert lib.ja_fwd_tile_shape(4, 40, 233, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == UNSUPPORTED
+    assert lib.ja_fwd_tile_shape(128, 128, 128 * 2772, 128 * 65, 1, 1, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert (bm.value, bn.value) == (128, 64)
+    # fp32 never splits or chunks
+    assert lib.ja_fwd_tile_shape(4, 32, 233, 233, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert (bm.value, bn.value) == (128, 64)
+    assert lib.ja_fwd_tile_shape(4, 32, 4 * 1024, 4 * 8, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert (bm.value, bn.value) == (128, 64)
+    assert lib.ja_fwd_tile_shape(4, 40, 233, 233, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == UNSUPPORTED
 
 
 def test_schedule_rejects_short_item_buffer(lib):
