@@ -110,7 +110,31 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
         // layout.
         frag qf[C::NS], dof[C::NS];
         float di = 0.0f;
-        {
+        // The wave's quarter of the second stage buffer: free until this item's
+        // first barrier, and again after its last.
+        using RT = RowTurn<D>;
+        char* const wreg = (wave < 2 ? lds_k1 : lds_v1) + (wave & 1) * RT::BYTES;
+        if constexpr (KP == 8) {
+            // Whole rows in (16 bytes per lane), fragments out of LDS.
+            const int64_t wrow = (qo + qw0) * rs + (int64_t)h * D;
+            bf16x8 rq[RT::N], rd[RT::N], ro[ACT == ACT_SOFTMAX ? RT::N : 1];
+            RT::load(rq, (const bf16*)a.q + wrow, rs, Lq - qw0, lane);
+            RT::load(rd, (const bf16*)a.dout + wrow, rs, Lq - qw0, lane);
+            if constexpr (ACT == ACT_SOFTMAX) RT::load(ro, (const bf16*)a.out + wrow, rs, Lq - qw0, lane);
+            RT::put(wreg, rq, lane);
+            RT::frags(qf, wreg, lane);
+            RT::put(wreg, rd, lane);
+            RT::frags(dof, wreg, lane);
+            if constexpr (ACT == ACT_SOFTMAX) {
+                frag of[C::NS];
+                RT::put(wreg, ro, lane);
+                RT::frags(of, wreg, lane);
+#pragma unroll
+                for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) di = fmaf((float)dof[s][e], (float)of[s][e], di);
+            }
+        } else {
             const T* qs = (const T*)a.q + qrow;
             const T* ds = (const T*)a.dout + qrow;
             const T* os = (const T*)a.out + qrow;
@@ -120,12 +144,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
                 dof[s] = row_ok ? *(const frag*)(ds + 2 * KP * s) : Frag<T>::zero();
                 if constexpr (ACT == ACT_SOFTMAX) {
                     const frag of = row_ok ? *(const frag*)(os + 2 * KP * s) : Frag<T>::zero();
-                    if constexpr (KP == 8) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) di = fmaf((float)dof[s][e], (float)of[e], di);
-                    } else {
-                        di = fmaf(dof[s], of, di);
-                    }
+                    di = fmaf(dof[s], of, di);
                 }
             }
         }
@@ -211,7 +230,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
             if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
         }
 
-        if (row_ok) {
+        if constexpr (KP == 8) {
+            // Whole rows out through the wave's region (the stage loop ended on a
+            // barrier, or loaded nothing).
+            RT::put_acc(wreg, dqacc, a.scale, lane);
+            RT::store((bf16*)a.dq + (qo + qw0) * rs + (int64_t)h * D, rs, Lq - qw0, wreg, lane);
+        } else if (row_ok) {
             T* dst = (T*)a.dq + (qo + my_row) * rs + (int64_t)h * D + 4 * grp;
             const float sc = a.scale;
 #pragma unroll
@@ -286,7 +310,20 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
 
         const float inv_lk = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
         frag kf[C::NS], vf[C::NS];
-        {
+        // The wave's quarter of the second stage buffer: free until this item's
+        // first barrier, and again after its last.
+        using RT = RowTurn<D>;
+        char* const wreg = (wave < 2 ? lds_q1 : lds_o1) + (wave & 1) * RT::BYTES;
+        if constexpr (KP == 8) {
+            const int64_t wrow = (ko + kw0) * rs + (int64_t)h * D;
+            bf16x8 rk[RT::N], rv[RT::N];
+            RT::load(rk, (const bf16*)a.k + wrow, rs, Lk - kw0, lane);
+            RT::load(rv, (const bf16*)a.v + wrow, rs, Lk - kw0, lane);
+            RT::put(wreg, rk, lane);
+            RT::frags(kf, wreg, lane);
+            RT::put(wreg, rv, lane);
+            RT::frags(vf, wreg, lane);
+        } else {
             const T* ks = (const T*)a.k + krow;
             const T* vs = (const T*)a.v + krow;
 #pragma unroll
@@ -414,7 +451,15 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
             if (qs + 1 < qs_hi) stage(qs + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
         }
 
-        if (key_ok) {
+        if constexpr (KP == 8) {
+            // Whole rows out through the wave's region (the stage loop ended on a
+            // barrier, or loaded nothing): dK, then dV.
+            const int64_t wrow = (ko + kw0) * rs + (int64_t)h * D;
+            RT::put_acc(wreg, dkacc, a.scale, lane);
+            RT::store((bf16*)a.dk + wrow, rs, Lk - kw0, wreg, lane);
+            RT::put_acc(wreg, dvacc, 1.0f, lane);
+            RT::store((bf16*)a.dv + wrow, rs, Lk - kw0, wreg, lane);
+        } else if (key_ok) {
             const int64_t base = (ko + my_key) * rs + (int64_t)h * D + 4 * grp;
             T* dk = (T*)a.dk + base;
             T* dv = (T*)a.dv + base;

@@ -50,15 +50,6 @@
 namespace ja {
 namespace {
 
-// A lane value the compiler cannot move out of the enclosing loop. The swizzled
-// LDS addresses of the query and output turnarounds depend on it, so they are
-// computed where they are used instead of being held in registers through the
-// whole stage loop.
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 template <typename T, int D, bool SPLIT>
 struct FwdCfg {
     static constexpr int NW = SPLIT ? (D == 128 ? 4 : 8) : 4;  // waves per workgroup
@@ -187,17 +178,13 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
         // Chunked layout: a wave's 32 query rows are read whole (16 bytes per lane,
         // CPR lanes per row) into registers, one tile ahead, and turned into
         // B-operand fragments through the wave's quarter of the second stage buffer.
-        constexpr int NRAW = CHUNK > 1 ? C::CPR / 2 : 1;
-        bf16x8 qraw[NRAW];
+        using RT = RowTurn<D>;
+        bf16x8 qraw[CHUNK > 1 ? RT::N : 1];
         auto load_raw = [&](int row0) __attribute__((always_inline)) {
-#pragma unroll
-            for (int n = 0; n < NRAW; ++n) {
-                const int p = n * 64 + lane, r = p / C::CPR, c = p % C::CPR;
-                qraw[n] = row0 + r < Lq ? *(const bf16x8*)(Qg + (qo + row0 + r) * rs + (int64_t)h * D + c * 8)
-                                        : bf16x8{};
-            }
+            if constexpr (CHUNK > 1)
+                RT::load(qraw, (const bf16*)Qg + (qo + row0) * rs + (int64_t)h * D, rs, Lq - row0, lane);
         };
-        char* const wreg = (wave < 2 ? lds_k1 : lds_v1) + (wave & 1) * 32 * C::ROWB;  // wave-private
+        char* const wreg = (wave < 2 ? lds_k1 : lds_v1) + (wave & 1) * RT::BYTES;  // wave-private
         frag qf[C::NS];
         if constexpr (CHUNK > 1) load_raw(c0 + 32 * wq);
         else load_q(c0 + 32 * wq + col, qf);
@@ -215,16 +202,8 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
             // The region is free: the previous tile's output turnaround finished in
             // this wave's own order, and no stage load targets it before the next
             // barrier.
-            const int ln = opaque(lane);
-#pragma unroll
-            for (int n = 0; n < NRAW; ++n) {
-                const int p = n * 64 + ln, r = p / C::CPR, c = p % C::CPR;
-                *(bf16x8*)(wreg + r * C::ROWB + ((c ^ (r & (C::CPR - 1))) * 16)) = qraw[n];
-            }
-            const int cl = ln & 31, gp = ln >> 5;
-#pragma unroll
-            for (int s = 0; s < C::NS; ++s)
-                qf[s] = *(const frag*)(wreg + cl * C::ROWB + (((gp + 2 * s) ^ (cl & (C::CPR - 1))) * 16));
+            RT::put(wreg, qraw, lane);
+            RT::frags(qf, wreg, lane);
             if (sub + 1 < nsub) load_raw(qw0 + C::BM);
         }
 
@@ -417,29 +396,9 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
                 // output rows around in its own quarter of it (16-byte chunks
                 // XOR-swizzled by row) and writes whole rows, 16 bytes per lane,
                 // instead of 8-byte pieces of 32 rows per instruction.
-                {
-                    staged = true;
-                    char* reg = wreg;
-                    const int ln = opaque(lane), cl = ln & 31, gp = ln >> 5;
-#pragma unroll
-                    for (int i = 0; i < C::ND; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            bf16x4 v4;
-                            v4[0] = (bf16)(oacc[i][4 * j] * inv);
-                            v4[1] = (bf16)(oacc[i][4 * j + 1] * inv);
-                            v4[2] = (bf16)(oacc[i][4 * j + 2] * inv);
-                            v4[3] = (bf16)(oacc[i][4 * j + 3] * inv);
-                            const int pc = (4 * i + j) ^ (cl & (C::CPR - 1));
-                            *(bf16x4*)(reg + cl * C::ROWB + pc * 16 + gp * 8) = v4;
-                        }
-#pragma unroll
-                    for (int n = 0; n < C::CPR / 2; ++n) {
-                        const int p = n * 64 + ln, r = p / C::CPR, c = p % C::CPR;
-                        const bf16x8 v8 = *(const bf16x8*)(reg + r * C::ROWB + ((c ^ (r & (C::CPR - 1))) * 16));
-                        if (qw0 + r < Lq) *(bf16x8*)(Og + (qo + qw0 + r) * rs + (int64_t)h * D + c * 8) = v8;
-                    }
-                }
+                staged = true;
+                RT::put_acc(wreg, oacc, inv, lane);
+                RT::store((bf16*)Og + (qo + qw0) * rs + (int64_t)h * D, rs, Lq - qw0, wreg, lane);
             }
             if (my_row < Lq) {
                 if (!staged) {

@@ -225,4 +225,79 @@ __device__ __forceinline__ typename Frag<T>::type to_frag(const floatx16& c, int
     }
 }
 
+// A lane value the compiler cannot move out of the enclosing loop. The swizzled
+// LDS addresses of the row turnarounds below depend on it, so they are computed
+// where they are used instead of being held in registers through a stage loop.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Whole-row turnaround of a wave's 32 rows of one head through a wave-private LDS
+// region of 32 x ROWB bytes. Global memory sees only whole rows, 16 bytes per lane
+// (CPR lanes per row), instead of the 8- or 16-byte pieces of 32 rows that the
+// matrix-core layouts (lane = row) would give one instruction. 16-byte chunks are
+// XOR-swizzled by row, so the row-major pieces and the per-lane fragments and
+// accumulator quads both hit distinct banks.
+template <int D>
+struct RowTurn {
+    static constexpr int ROWB = D * 2;       // bf16 row
+    static constexpr int CPR = ROWB / 16;    // 16-byte chunks per row
+    static constexpr int N = CPR / 2;        // pieces per lane for 32 rows
+    static constexpr int BYTES = 32 * ROWB;  // region size
+    static __device__ __forceinline__ int at(int r, int c) { return r * ROWB + ((c ^ (r & (CPR - 1))) << 4); }
+
+    // Rows [0, 32) from base (row 0, this head), row stride rs elements; rows at
+    // or past nrows read as zero.
+    static __device__ __forceinline__ void load(bf16x8 (&raw)[N], const bf16* base, int64_t rs, int nrows,
+                                                int lane) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const int p = n * 64 + lane, r = p / CPR, c = p % CPR;
+            raw[n] = r < nrows ? *(const bf16x8*)(base + r * rs + c * 8) : bf16x8{};
+        }
+    }
+    static __device__ __forceinline__ void put(char* reg, const bf16x8 (&raw)[N], int lane) {
+        const int ln = opaque(lane);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const int p = n * 64 + ln;
+            *(bf16x8*)(reg + at(p / CPR, p % CPR)) = raw[n];
+        }
+    }
+    // B-operand fragments: fragment s of lane (col, grp) holds elements
+    // [8 grp + 16 s, 8 grp + 16 s + 8) of row col.
+    static __device__ __forceinline__ void frags(bf16x8 (&f)[D / 16], const char* reg, int lane) {
+        const int ln = opaque(lane), cl = ln & 31, gp = ln >> 5;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) f[s] = *(const bf16x8*)(reg + at(cl, gp + 2 * s));
+    }
+    // C-layout accumulators of O^T-like products (lane = row col, register r of
+    // block i = element 32 i + 8 (r / 4) + 4 grp + r % 4), times sc, as bf16 rows.
+    static __device__ __forceinline__ void put_acc(char* reg, const floatx16 (&acc)[D / 32], float sc, int lane) {
+        const int ln = opaque(lane), cl = ln & 31, gp = ln >> 5;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 v;
+                v[0] = (bf16)(acc[i][4 * j] * sc);
+                v[1] = (bf16)(acc[i][4 * j + 1] * sc);
+                v[2] = (bf16)(acc[i][4 * j + 2] * sc);
+                v[3] = (bf16)(acc[i][4 * j + 3] * sc);
+                *(bf16x4*)(reg + at(cl, 4 * i + j) + gp * 8) = v;
+            }
+    }
+    // Region rows [0, nrows) to global rows at base (row 0, this head).
+    static __device__ __forceinline__ void store(bf16* base, int64_t rs, int nrows, const char* reg, int lane) {
+        const int ln = opaque(lane);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const int p = n * 64 + ln, r = p / CPR, c = p % CPR;
+            const bf16x8 v = *(const bf16x8*)(reg + at(r, c));
+            if (r < nrows) *(bf16x8*)(base + r * rs + c * 8) = v;
+        }
+    }
+};
+
 }  // namespace ja
