@@ -187,8 +187,12 @@ __global__ __launch_bounds__(kBlkThreads) void ja_blk_bwd_kernel(BlkArgs a) {
     const bool wave_rows = 32 * wave < it.n;  // this wave has query rows
     __syncthreads();
 
-    // Query-stationary phase: S^T, dP^T, softmax, dS, dQ.
+    // Query-stationary phase: S^T, dP^T, softmax, dS, dQ (kept in registers until
+    // the end of the item).
     floatx16 sacc[2], dpacc[2];
+    floatx16 dqacc[C::ND];
+#pragma unroll
+    for (int i = 0; i < C::ND; ++i) dqacc[i] = floatx16{};
     if (wave_rows) {
         frag qf[C::NS], dof[C::NS];
 #pragma unroll
@@ -241,9 +245,6 @@ __global__ __launch_bounds__(kBlkThreads) void ja_blk_bwd_kernel(BlkArgs a) {
             }
 
         // dQ^T = K^T dS^T
-        floatx16 dqacc[C::ND];
-#pragma unroll
-        for (int i = 0; i < C::ND; ++i) dqacc[i] = floatx16{};
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             if (nb == 1 && !nb1) continue;
@@ -254,16 +255,6 @@ __global__ __launch_bounds__(kBlkThreads) void ja_blk_bwd_kernel(BlkArgs a) {
                 for (int db = 0; db < C::ND; ++db)
                     dqacc[db] = M::run(C::RTile::read_tr(lds_k + nb * 32 * C::ROWB, t, toff, db), dsf, dqacc[db]);
             }
-        }
-        if (row_ok) {
-            bf16* dst = (bf16*)a.dq + tile0 + (int64_t)qloc * rs + 4 * grp;
-            const float sc = a.scale;
-#pragma unroll
-            for (int i = 0; i < C::ND; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    store4<bf16>(dst + 32 * i + 8 * j, dqacc[i][4 * j] * sc, dqacc[i][4 * j + 1] * sc,
-                                 dqacc[i][4 * j + 2] * sc, dqacc[i][4 * j + 3] * sc);
         }
     } else {
         // No query rows: P and dS rows of this wave are zero.
@@ -279,9 +270,8 @@ __global__ __launch_bounds__(kBlkThreads) void ja_blk_bwd_kernel(BlkArgs a) {
     }
     __syncthreads();
 
-    // Key-stationary phase: wave w owns keys [32w, 32w + 32) of the tile.
-    if (!wave_rows) continue;  // its keys are past the end too
-    const int my_key = it.r0 + qloc;
+    // Key-stationary phase: wave w owns keys [32w, 32w + 32) of the tile (a wave
+    // with no query rows has no keys either).
     floatx16 dkacc[C::ND], dvacc[C::ND];
 #pragma unroll
     for (int i = 0; i < C::ND; ++i) {
@@ -291,6 +281,7 @@ __global__ __launch_bounds__(kBlkThreads) void ja_blk_bwd_kernel(BlkArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         if (nb == 1 && !nb1) continue;
+        if (!wave_rows) continue;
 #pragma unroll
         for (int t = 0; t < C::NT; ++t) {
             const frag pf = C::PTile::read_tr(lds_p + nb * 32 * C::PTile::ROWB, t, poff, wave);
@@ -302,20 +293,21 @@ __global__ __launch_bounds__(kBlkThreads) void ja_blk_bwd_kernel(BlkArgs a) {
             }
         }
     }
-    if (my_key < it.L) {
-        const int64_t base = tile0 + (int64_t)qloc * rs + 4 * grp;
-        bf16* dk = (bf16*)a.dk + base;
-        bf16* dv = (bf16*)a.dv + base;
-        const float sc = a.scale;
-#pragma unroll
-        for (int i = 0; i < C::ND; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                store4<bf16>(dk + 32 * i + 8 * j, dkacc[i][4 * j] * sc, dkacc[i][4 * j + 1] * sc,
-                             dkacc[i][4 * j + 2] * sc, dkacc[i][4 * j + 3] * sc);
-                store4<bf16>(dv + 32 * i + 8 * j, dvacc[i][4 * j], dvacc[i][4 * j + 1], dvacc[i][4 * j + 2],
-                             dvacc[i][4 * j + 3]);
-            }
+    // Every wave is done reading the tiles: each turns its 32 rows of dQ, dK and
+    // dV around in its half of the K tile and writes whole rows (16 bytes per
+    // lane) instead of 8-byte pieces of 32 rows per instruction.
+    __syncthreads();
+    if (wave_rows) {
+        using RT = RowTurn<D>;
+        char* const wreg = lds_k + wave * RT::BYTES;
+        const int nrows = it.L - it.r0 - 32 * wave;
+        const int64_t wrow = tile0 + (int64_t)(32 * wave) * rs;
+        RT::put_acc(wreg, dqacc, a.scale, lane);
+        RT::store((bf16*)a.dq + wrow, rs, nrows, wreg, lane);
+        RT::put_acc(wreg, dkacc, a.scale, lane);
+        RT::store((bf16*)a.dk + wrow, rs, nrows, wreg, lane);
+        RT::put_acc(wreg, dvacc, 1.0f, lane);
+        RT::store((bf16*)a.dv + wrow, rs, nrows, wreg, lane);
     }
     }
 #else
