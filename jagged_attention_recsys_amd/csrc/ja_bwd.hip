@@ -302,7 +302,14 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
         const ColRange cr = visible_cols(Lk, Lq, k0, kBwdRows, causal, window, 1, bsh);
         const int qs_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
         const int qs_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
-        const int kw0 = k0 + 32 * wave;
+        // A tile of at most 64 keys (short K/V, or a sequence's last tile) would
+        // leave two waves without keys: then, if it visits at least two query
+        // stages (both pairs get work), waves w and w + 2 share keys [32 (w % 2),
+        // +32) and split each stage's queries (wave pair p takes the stage's
+        // 32-query block p); the pairs add their partial dK, dV at the end.
+        const bool pair_split = Lk - k0 <= 64 && qs_hi - qs_lo >= 2;  // uniform over the workgroup
+        const int kwave = pair_split ? (wave & 1) : wave;
+        const int kw0 = k0 + 32 * kwave;
         const int my_key = kw0 + col;
         const bool key_ok = my_key < Lk;
         const VisRange vis = queries_seeing(my_key, Lq, Lk, causal, window, bsh);
@@ -366,6 +373,7 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
             const int qbase = qs * kBwdStage;
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
+                if (pair_split && nb != (wave >> 1)) continue;  // the other pair's block
                 const int qb0 = qbase + nb * 32;  // first query of this block
                 // Wave-uniform: lanes past the sequence end still feed the shared
                 // matrix operands (their K/V rows are zero and masked below).
@@ -451,7 +459,37 @@ __global__ __launch_bounds__(kBwdThreads) void ja_bwd_dkdv_kernel(BwdArgs a) {
             if (qs + 1 < qs_hi) stage(qs + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
         }
 
-        if constexpr (KP == 8) {
+        if (pair_split) {
+            // Waves 2 and 3 hand their partial sums to waves 0 and 1 through the
+            // stage buffers (free: the stage loop ended on a barrier, or loaded
+            // nothing); each array holds one accumulator set of one wave.
+            static_assert(C::ND * 16 * 64 * 4 <= C::STile::BYTES, "partial sums must fit a stage array");
+            float* pk = (float*)((wave & 1) ? lds_q1 : lds_q0);
+            float* pv = (float*)((wave & 1) ? lds_o1 : lds_o0);
+            if (wave >= 2) {
+#pragma unroll
+                for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        pk[(i * 16 + r) * 64 + lane] = dkacc[i][r];
+                        pv[(i * 16 + r) * 64 + lane] = dvacc[i][r];
+                    }
+            }
+            __syncthreads();
+            if (wave < 2) {
+#pragma unroll
+                for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        dkacc[i][r] += pk[(i * 16 + r) * 64 + lane];
+                        dvacc[i][r] += pv[(i * 16 + r) * 64 + lane];
+                    }
+            }
+            __syncthreads();  // the partial sums are read before the row turnarounds reuse the buffers
+        }
+        const bool owner = !pair_split || wave < 2;  // writes its keys' dK, dV
+        if (!owner) {
+        } else if constexpr (KP == 8) {
             // Whole rows out through the wave's region (the stage loop ended on a
             // barrier, or loaded nothing): dK, then dV.
             const int64_t wrow = (ko + kw0) * rs + (int64_t)h * D;
