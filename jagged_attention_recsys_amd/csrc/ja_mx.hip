@@ -429,14 +429,16 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
 
         const float l_tot = halves_sum(l_run);  // 2^8 times the softmax normaliser
         const float inv = l_tot > 0.0f ? 256.0f / l_tot : 0.0f;
+        {
+            // Output rows written whole (16 bytes per lane) through the wave's half
+            // of a second stage buffer, free after the stage loop's last barrier.
+            using RT = RowTurn<kMxD>;
+            static_assert(2 * RT::BYTES <= kMxTile, "two wave regions per stage array");
+            char* const wreg = (wave < 2 ? lds_k1 : lds_v1) + (wave & 1) * RT::BYTES;
+            RT::put_acc(wreg, oacc, inv, lane);
+            RT::store((bf16*)a.out + (qo + qw0) * rs + (int64_t)h * kMxD, rs, Lq - qw0, wreg, lane);
+        }
         if (row_ok) {
-            bf16* dst = (bf16*)a.out + (qo + my_row) * (int64_t)a.H * kMxD + (int64_t)h * kMxD + 4 * g;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    store4<bf16>(dst + 32 * i + 8 * j, oacc[i][4 * j] * inv, oacc[i][4 * j + 1] * inv,
-                                 oacc[i][4 * j + 2] * inv, oacc[i][4 * j + 3] * inv);
             if (a.lse != nullptr && g == 0)
                 a.lse[(qo + my_row) * a.H + h] = l_tot > 0.0f ? (m_run - 8.0f) * kLn2 + logf(l_tot) : -INFINITY;
         }
