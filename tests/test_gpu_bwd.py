@@ -174,6 +174,18 @@ def test_pointwise_cross_lengths(act, d):
     check(case(lq, lk, H=3, d=d, seed=500 + d), False, 0, what="cross", act=act)
 
 
+@pytest.mark.parametrize("act,causal,window", [("softmax", False, 0), ("softmax", True, 0), ("softmax", True, 30),
+                                               ("silu", False, 0), ("gelu", True, 0)])
+def test_short_key_tiles_split_queries(act, causal, window):
+    # Key tiles of at most 64 keys that visit two or more 64-query stages split the
+    # stages' queries between two wave pairs and add their partial dK, dV: keys of
+    # 64, 63, 1 and the last tiles of 129 and 192 keys, against 300-700 queries;
+    # 65 and 128 keys (no split) and a one-stage tile (33 queries) beside them.
+    lq = [700, 300, 450, 500, 640, 300, 512, 33]
+    lk = [64, 63, 1, 129, 192, 65, 128, 40]
+    check(case(lq, lk, H=2, d=128, seed=77 + window), causal, window, what="split-keys", act=act)
+
+
 def _sample_pairs(w, n, seed):
     rng = np.random.default_rng(seed)
     mask = np.zeros((w.B, w.H), dtype=bool)
