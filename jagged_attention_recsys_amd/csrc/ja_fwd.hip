@@ -190,230 +190,230 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
         else load_q(c0 + 32 * wq + col, qf);
 
         for (int sub = 0; sub < nsub; ++sub) {
-        const int q0 = c0 + sub * C::BM;
-        const ColRange cr = visible_cols(Lq, Lk, q0, C::BM, causal, window, 0, bsh);
-        const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / C::KT) : 0;
-        const int kt_hi = cr.hi > cr.lo ? (int)((cr.hi + C::KT - 1) / C::KT) : 0;
-        const int qw0 = q0 + 32 * wq;  // first query row of this wave
-        const int my_row = qw0 + col;
-        const bool row_ok = my_row < Lq;
-        const VisRange vis = keys_seen_by(my_row, Lk, causal, window, bsh);
-        if constexpr (CHUNK > 1) {
-            // The region is free: the previous tile's output turnaround finished in
-            // this wave's own order, and no stage load targets it before the next
-            // barrier.
-            RT::put(wreg, qraw, lane);
-            RT::frags(qf, wreg, lane);
-            if (sub + 1 < nsub) load_raw(qw0 + C::BM);
-        }
+            const int q0 = c0 + sub * C::BM;
+            const ColRange cr = visible_cols(Lq, Lk, q0, C::BM, causal, window, 0, bsh);
+            const int kt_lo = cr.hi > cr.lo ? (int)(cr.lo / C::KT) : 0;
+            const int kt_hi = cr.hi > cr.lo ? (int)((cr.hi + C::KT - 1) / C::KT) : 0;
+            const int qw0 = q0 + 32 * wq;  // first query row of this wave
+            const int my_row = qw0 + col;
+            const bool row_ok = my_row < Lq;
+            const VisRange vis = keys_seen_by(my_row, Lk, causal, window, bsh);
+            if constexpr (CHUNK > 1) {
+                // The region is free: the previous tile's output turnaround finished in
+                // this wave's own order, and no stage load targets it before the next
+                // barrier.
+                RT::put(wreg, qraw, lane);
+                RT::frags(qf, wreg, lane);
+                if (sub + 1 < nsub) load_raw(qw0 + C::BM);
+            }
 
-        floatx16 oacc[C::ND];
+            floatx16 oacc[C::ND];
 #pragma unroll
-        for (int i = 0; i < C::ND; ++i) oacc[i] = floatx16{};
-        float m_run = -INFINITY, l_run = 0.0f;
+            for (int i = 0; i < C::ND; ++i) oacc[i] = floatx16{};
+            float m_run = -INFINITY, l_run = 0.0f;
 
-        // Stage kt -> (kdst, vdst): K and V rows [kt*KT, kt*KT + KT) of this
-        // sequence and head; rows at or past Lk read as zero.
-        auto issue = [&](int kt, char* kdst, char* vdst) {
-            const int kbase = kt * C::KT;
-            const uint32_t nrec =
-                __builtin_amdgcn_readfirstlane((uint32_t)min(max(Lk - kbase, 0), C::KT) * rsb);
-            ld.issue(Kseq + (int64_t)kbase * rsb, nrec, kdst, wave);
-            ld.issue(Vseq + (int64_t)kbase * rsb, nrec, vdst, wave);
-        };
+            // Stage kt -> (kdst, vdst): K and V rows [kt*KT, kt*KT + KT) of this
+            // sequence and head; rows at or past Lk read as zero.
+            auto issue = [&](int kt, char* kdst, char* vdst) {
+                const int kbase = kt * C::KT;
+                const uint32_t nrec =
+                    __builtin_amdgcn_readfirstlane((uint32_t)min(max(Lk - kbase, 0), C::KT) * rsb);
+                ld.issue(Kseq + (int64_t)kbase * rsb, nrec, kdst, wave);
+                ld.issue(Vseq + (int64_t)kbase * rsb, nrec, vdst, wave);
+            };
 
-        // Consume the stage in (kl, vl) while the next one (if any) streams into
-        // (kn, vn).
-        auto compute = [&](int kt, const char* kl, const char* vl) {
-            const int kw0 = kt * C::KT + wk * 32 * C::NB;  // first key of this wave's blocks
-            const bool skip = wave_skips(vis, row_ok, kw0, 32 * C::NB);
-            if (!skip) {
-                floatx16 sacc[C::NB];
+            // Consume the stage in (kl, vl) while the next one (if any) streams into
+            // (kn, vn).
+            auto compute = [&](int kt, const char* kl, const char* vl) {
+                const int kw0 = kt * C::KT + wk * 32 * C::NB;  // first key of this wave's blocks
+                const bool skip = wave_skips(vis, row_ok, kw0, 32 * C::NB);
+                if (!skip) {
+                    floatx16 sacc[C::NB];
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb) {
-                    sacc[nb] = floatx16{};
-                    const char* kblk = kl + (wk * C::NB + nb) * 32 * C::ROWB;
+                    for (int nb = 0; nb < C::NB; ++nb) {
+                        sacc[nb] = floatx16{};
+                        const char* kblk = kl + (wk * C::NB + nb) * 32 * C::ROWB;
 #pragma unroll
-                    for (int s = 0; s < C::NS; ++s)
-                        sacc[nb] = M::run(C::KVTile::read_rows(kblk, koff[s]), qf[s], sacc[nb]);
-                }
+                        for (int s = 0; s < C::NS; ++s)
+                            sacc[nb] = M::run(C::KVTile::read_rows(kblk, koff[s]), qf[s], sacc[nb]);
+                    }
 
-                const bool need_mask = wave_needs_mask(vis, row_ok, kw0, 32 * C::NB);
-                if (ACT == ACT_SOFTMAX) {
-                    if (prescale) {
+                    const bool need_mask = wave_needs_mask(vis, row_ok, kw0, 32 * C::NB);
+                    if (ACT == ACT_SOFTMAX) {
+                        if (prescale) {
+#pragma unroll
+                            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) sacc[nb][r] *= a.scale * kLog2e;
+                        }
+                        if (need_mask) {
+#pragma unroll
+                            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
+                                    sacc[nb][r] = vis.has(key) ? sacc[nb][r] : -INFINITY;
+                                }
+                        }
+                        float mx = -INFINITY;
 #pragma unroll
                         for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) sacc[nb][r] *= a.scale * kLog2e;
-                    }
-                    if (need_mask) {
+                            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
+                        mx = halves_max(mx) * c_exp;
+                        if (__any(mx > m_run + 8.0f)) {
+                            const float m_new = fmaxf(m_run, mx);
+                            const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run - m_new);
+                            l_run *= alpha;
+#pragma unroll
+                            for (int i = 0; i < C::ND; ++i) oacc[i] *= alpha;
+                            m_run = m_new;
+                        }
+                        const float msub = m_run == -INFINITY ? 0.0f : m_run;
+                        float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                         for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
-                                const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
-                                sacc[nb][r] = vis.has(key) ? sacc[nb][r] : -INFINITY;
+                                const float p = fast_exp2(fmaf(sacc[nb][r], c_exp, -msub));
+                                lsum[r & 3] += p;
+                                sacc[nb][r] = p;
+                            }
+                        l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+                    } else {
+#pragma unroll
+                        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                float p = pointwise<ACT>(sacc[nb][r] * a.scale);
+                                if (need_mask) {
+                                    const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
+                                    p = vis.has(key) ? p : 0.0f;
+                                }
+                                sacc[nb][r] = p;
                             }
                     }
-                    float mx = -INFINITY;
+
+                    // P^T in the B-operand layout, then O^T += V^T P^T.
+                    frag pf[C::NB][C::NT];
 #pragma unroll
                     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-                    mx = halves_max(mx) * c_exp;
-                    if (__any(mx > m_run + 8.0f)) {
-                        const float m_new = fmaxf(m_run, mx);
-                        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run - m_new);
-                        l_run *= alpha;
+                        for (int t = 0; t < C::NT; ++t) pf[nb][t] = to_frag<T>(sacc[nb], KP * t);
 #pragma unroll
-                        for (int i = 0; i < C::ND; ++i) oacc[i] *= alpha;
-                        m_run = m_new;
+                    for (int nb = 0; nb < C::NB; ++nb) {
+                        const char* vblk = vl + (wk * C::NB + nb) * 32 * C::ROWB;
+#pragma unroll
+                        for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+                            for (int db = 0; db < C::ND; ++db)
+                                oacc[db] = M::run(C::KVTile::read_tr(vblk, t, voff, db), pf[nb][t], oacc[db]);
                     }
-                    const float msub = m_run == -INFINITY ? 0.0f : m_run;
-                    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float p = fast_exp2(fmaf(sacc[nb][r], c_exp, -msub));
-                            lsum[r & 3] += p;
-                            sacc[nb][r] = p;
-                        }
-                    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-                } else {
-#pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            float p = pointwise<ACT>(sacc[nb][r] * a.scale);
-                            if (need_mask) {
-                                const int key = kw0 + nb * 32 + key_of_reg<KP>(grp, r);
-                                p = vis.has(key) ? p : 0.0f;
-                            }
-                            sacc[nb][r] = p;
-                        }
                 }
+            };
+            auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
+                if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
+                compute(kt, kl, vl);
+                __syncthreads();
+            };
 
-                // P^T in the B-operand layout, then O^T += V^T P^T.
-                frag pf[C::NB][C::NT];
-#pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                    for (int t = 0; t < C::NT; ++t) pf[nb][t] = to_frag<T>(sacc[nb], KP * t);
-#pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb) {
-                    const char* vblk = vl + (wk * C::NB + nb) * 32 * C::ROWB;
-#pragma unroll
-                    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-                        for (int db = 0; db < C::ND; ++db)
-                            oacc[db] = M::run(C::KVTile::read_tr(vblk, t, voff, db), pf[nb][t], oacc[db]);
+            if (CHUNK > 1 && resident) {
+                // The chunk's one stage: loaded by the first tile, read by all. A tile
+                // whose rows see no key (kt_hi == kt_lo) skips it.
+                if (sub == 0) {
+                    issue(rkt, lds_k0, lds_v0);
+                    __syncthreads();
                 }
-            }
-        };
-        auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
-            if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
-            compute(kt, kl, vl);
-            __syncthreads();
-        };
-
-        if (CHUNK > 1 && resident) {
-            // The chunk's one stage: loaded by the first tile, read by all. A tile
-            // whose rows see no key (kt_hi == kt_lo) skips it.
-            if (sub == 0) {
-                issue(rkt, lds_k0, lds_v0);
-                __syncthreads();
-            }
-            if (kt_hi > kt_lo) compute(rkt, lds_k0, lds_v0);
-        } else {
-            if (kt_hi > kt_lo) {
-                issue(kt_lo, lds_k0, lds_v0);
-                __syncthreads();
-            }
-            for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-                stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
-                if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
-            }
-        }
-
-        if (sub == nsub - 1 && tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
-
-        // Split layout: merge the key slices (the loop ended on a barrier, or no
-        // stage was loaded, so the stage buffers are free). Softmax first agrees on
-        // the row max, then partial sums and accumulators are added pairwise.
-        if constexpr (SPLIT) {
-            if (ACT == ACT_SOFTMAX) {
-                s_max[wave * 64 + lane] = m_run;
-                __syncthreads();
-                float mg = -INFINITY;
-#pragma unroll
-                for (int w = 0; w < C::WK; ++w) mg = fmaxf(mg, s_max[w * 64 + lane]);
-                const float sc = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mg);
-                l_run *= sc;
-#pragma unroll
-                for (int i = 0; i < C::ND; ++i) oacc[i] *= sc;
-                m_run = mg;
-            }
-            // slot j: [D/2 + 2][64] floats at (j/2) * SLICE of lds_k0 (j even) or lds_v0 (j odd)
-            auto slot = [&](int j) { return (float*)((j & 1) ? lds_v0 : lds_k0) + (j >> 1) * C::SLICE; };
-#pragma unroll
-            for (int half = C::WK / 2; half >= 1; half /= 2) {
-                if (wave >= half && wave < 2 * half) {
-                    float* dst = slot(wave - half);
-#pragma unroll
-                    for (int i = 0; i < C::ND; ++i)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) dst[(i * 16 + r) * 64 + lane] = oacc[i][r];
-                    dst[(D / 2) * 64 + lane] = l_run;
-                }
-                __syncthreads();
-                if (wave < half) {
-                    const float* src = slot(wave);
-#pragma unroll
-                    for (int i = 0; i < C::ND; ++i)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[i][r] += src[(i * 16 + r) * 64 + lane];
-                    l_run += src[(D / 2) * 64 + lane];
-                }
-                __syncthreads();
-            }
-        }
-
-        if (!SPLIT || wave == 0) {
-            float inv;
-            float lse_val = 0.0f;
-            if (ACT == ACT_SOFTMAX) {
-                const float l_tot = halves_sum(l_run);
-                inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-                lse_val = l_tot > 0.0f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+                if (kt_hi > kt_lo) compute(rkt, lds_k0, lds_v0);
             } else {
-                inv = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
-            }
-            bool staged = false;
-            if constexpr (!SPLIT && KP == 8) {
-                // The second stage buffer is free here (the stage loop ended on a
-                // barrier, resident chunks never load it): each wave turns its 32
-                // output rows around in its own quarter of it (16-byte chunks
-                // XOR-swizzled by row) and writes whole rows, 16 bytes per lane,
-                // instead of 8-byte pieces of 32 rows per instruction.
-                staged = true;
-                RT::put_acc(wreg, oacc, inv, lane);
-                RT::store((bf16*)Og + (qo + qw0) * rs + (int64_t)h * D, rs, Lq - qw0, wreg, lane);
-            }
-            if (my_row < Lq) {
-                if (!staged) {
-                    T* dst = Og + (qo + my_row) * rs + (int64_t)h * D + 4 * grp;
-#pragma unroll
-                    for (int i = 0; i < C::ND; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            store4<T>(dst + 32 * i + 8 * j, oacc[i][4 * j] * inv, oacc[i][4 * j + 1] * inv,
-                                      oacc[i][4 * j + 2] * inv, oacc[i][4 * j + 3] * inv);
+                if (kt_hi > kt_lo) {
+                    issue(kt_lo, lds_k0, lds_v0);
+                    __syncthreads();
                 }
-                if (ACT == ACT_SOFTMAX && a.lse != nullptr && grp == 0)
-                    a.lse[(qo + my_row) * a.H + h] = lse_val;
+                for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+                    stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+                    if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+                }
             }
-        }
+
+            if (sub == nsub - 1 && tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
+
+            // Split layout: merge the key slices (the loop ended on a barrier, or no
+            // stage was loaded, so the stage buffers are free). Softmax first agrees on
+            // the row max, then partial sums and accumulators are added pairwise.
+            if constexpr (SPLIT) {
+                if (ACT == ACT_SOFTMAX) {
+                    s_max[wave * 64 + lane] = m_run;
+                    __syncthreads();
+                    float mg = -INFINITY;
+#pragma unroll
+                    for (int w = 0; w < C::WK; ++w) mg = fmaxf(mg, s_max[w * 64 + lane]);
+                    const float sc = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mg);
+                    l_run *= sc;
+#pragma unroll
+                    for (int i = 0; i < C::ND; ++i) oacc[i] *= sc;
+                    m_run = mg;
+                }
+                // slot j: [D/2 + 2][64] floats at (j/2) * SLICE of lds_k0 (j even) or lds_v0 (j odd)
+                auto slot = [&](int j) { return (float*)((j & 1) ? lds_v0 : lds_k0) + (j >> 1) * C::SLICE; };
+#pragma unroll
+                for (int half = C::WK / 2; half >= 1; half /= 2) {
+                    if (wave >= half && wave < 2 * half) {
+                        float* dst = slot(wave - half);
+#pragma unroll
+                        for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) dst[(i * 16 + r) * 64 + lane] = oacc[i][r];
+                        dst[(D / 2) * 64 + lane] = l_run;
+                    }
+                    __syncthreads();
+                    if (wave < half) {
+                        const float* src = slot(wave);
+#pragma unroll
+                        for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) oacc[i][r] += src[(i * 16 + r) * 64 + lane];
+                        l_run += src[(D / 2) * 64 + lane];
+                    }
+                    __syncthreads();
+                }
+            }
+
+            if (!SPLIT || wave == 0) {
+                float inv;
+                float lse_val = 0.0f;
+                if (ACT == ACT_SOFTMAX) {
+                    const float l_tot = halves_sum(l_run);
+                    inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                    lse_val = l_tot > 0.0f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+                } else {
+                    inv = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
+                }
+                bool staged = false;
+                if constexpr (!SPLIT && KP == 8) {
+                    // The second stage buffer is free here (the stage loop ended on a
+                    // barrier, resident chunks never load it): each wave turns its 32
+                    // output rows around in its own quarter of it (16-byte chunks
+                    // XOR-swizzled by row) and writes whole rows, 16 bytes per lane,
+                    // instead of 8-byte pieces of 32 rows per instruction.
+                    staged = true;
+                    RT::put_acc(wreg, oacc, inv, lane);
+                    RT::store((bf16*)Og + (qo + qw0) * rs + (int64_t)h * D, rs, Lq - qw0, wreg, lane);
+                }
+                if (my_row < Lq) {
+                    if (!staged) {
+                        T* dst = Og + (qo + my_row) * rs + (int64_t)h * D + 4 * grp;
+#pragma unroll
+                        for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                store4<T>(dst + 32 * i + 8 * j, oacc[i][4 * j] * inv, oacc[i][4 * j + 1] * inv,
+                                          oacc[i][4 * j + 2] * inv, oacc[i][4 * j + 3] * inv);
+                    }
+                    if (ACT == ACT_SOFTMAX && a.lse != nullptr && grp == 0)
+                        a.lse[(qo + my_row) * a.H + h] = lse_val;
+                }
+            }
         }  // sub-tiles
     }
 #else
