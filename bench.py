@@ -140,9 +140,9 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build runs the attention path on a single MI355X and has "
-              "no multi-GPU path (each sequence and head is independent; sharding is by sequence, see the "
-              "design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the attention path on a single MI355X and has "
+              "no multi-GPU path (each sequence and head is independent, so a batch would be sharded by "
+              "sequence). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
