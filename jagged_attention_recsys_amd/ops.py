@@ -272,6 +272,9 @@ def jagged_attn_fwd_mxfp8(q8, q_scales, q_scale_offsets, k8, k_scales, k_scale_o
 
 
 def fwd_tile_shape(B, d, Tq, Tk, act="softmax", dtype=torch.bfloat16):
+    """(query rows per work item, keys per stage) of the forward for these sizes; the
+    layout (standard, split for short queries, chunked for short keys) follows from B,
+    Tq and Tk alone."""
     import ctypes
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
     status = _lib.load().ja_fwd_tile_shape(B, d, Tq, Tk, _act(act), DTYPE[dtype], ctypes.byref(bm),
