@@ -274,8 +274,10 @@ def main() -> int:
         # (and the fp32 lse where the backward needs it) once.
         min_bytes = 2 * w.H * w.d * (2 * Tq + 2 * Tk) + (4 * w.H * Tq if need_lse else 0)
         gbs = min_bytes / (fwd_kernel_ms * 1e-3) / 1e9
+        copy = measure_copy_gbs(1024)  # what a plain streaming kernel sustains on this GPU, same run
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": min_bytes,
+                    "copy_gbs": round(copy, 1), "frac_of_copy": round(gbs / copy, 4),
                     "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
     else:
         peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
@@ -382,8 +384,33 @@ def record_traffic(workload: int, fetch_dir: str, write_dir: str, copy_fetch_dir
     return 0
 
 
+def measure_copy_gbs(mib: int, x=None, y=None) -> float:
+    """Bytes read + written per second by a plain streaming kernel (y = x * 1 over mib MiB),
+    20 event-timed launches after a 200 ms spin-up."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    if x is None:
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+    t_end = time.perf_counter() + 0.2
+    while time.perf_counter() < t_end:
+        torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * n * 4 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
+
 def copy_calibration(mib: int) -> int:
-    """A plain streaming kernel of known traffic: reads and writes mib MiB per launch."""
+    """A plain streaming kernel of known traffic: reads and writes mib MiB per launch.
+    Five launches serve as the counter calibration; the copy bandwidth the GPU
+    sustains is then timed on the same buffers."""
     import torch
 
     n = mib * (1 << 20) // 4
@@ -392,8 +419,9 @@ def copy_calibration(mib: int) -> int:
     for _ in range(5):
         torch.mul(x, 1.0, out=y)
     torch.cuda.synchronize()
+    gbs = measure_copy_gbs(mib, x, y)
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
-                      "launches": 5}), flush=True)
+                      "launches": 5, "copy_gbs": round(gbs, 1)}), flush=True)
     return 0
 
 
