@@ -237,8 +237,10 @@ __device__ __forceinline__ int opaque(int x) {
 // region of 32 x ROWB bytes. Global memory sees only whole rows, 16 bytes per lane
 // (CPR lanes per row), instead of the 8- or 16-byte pieces of 32 rows that the
 // matrix-core layouts (lane = row) would give one instruction. 16-byte chunks are
-// XOR-swizzled by row, so the row-major pieces and the per-lane fragments and
-// accumulator quads both hit distinct banks.
+// XOR-swizzled by row: at d = 128 the 16-byte row pieces and per-lane fragments hit
+// distinct banks (a model of the 64-bank LDS), while the 8-byte accumulator writes
+// can pair rows r and r + 16 on one bank (a layout that separates them measured the
+// same LDS bank-conflict count and time).
 template <int D>
 struct RowTurn {
     static constexpr int ROWB = D * 2;       // bf16 row
