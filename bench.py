@@ -1,30 +1,37 @@
 #!/usr/bin/env python3
 """Throughput of the jagged attention hot path on one MI355X; prints ONE JSON line.
 
-A step is one full ``jagged_attn_fwd`` call (device tile scheduler + fused attention
-kernel) over the whole synthetic batch, inputs already resident in HBM. The default
-workload is the jagged causal softmax self-attention batch (B=64, lengths
-log-uniform in [128, 4096], H=4, d=128, bf16). ``--workload 3|4|5|6`` measures the
-other named batches (6: 64-token block-diagonal attention through
-``jagged_block_attn_fwd``; 7: QK-normed self-attention with the ALU-only GELU);
-``--bwd`` adds the backward (softmax for 2, 5 and 6, the pointwise SiLU / GELU
-backward for 3, 4 and 7); ``--act`` swaps the activation.
+A step is one pass of the whole hot path over one resident synthetic batch: by
+default the long sliding-window causal softmax self-attention batch (B=32, lengths
+lognormal with median 2048 capped at 32768, window 1024, H=8, d=128, bf16), forward
+AND backward, i.e. ``jagged_attn_fwd`` (device tile scheduler + fused forward) then
+``jagged_attn_bwd`` (two schedulers, the dQ pass with its Di prologue, the dK/dV
+pass). ``--workload 2|3|4|6|7|8`` measures the other batches (forward only unless
+``--bwd``; 6 and 7 include their backward like 5; ``--fwd-only`` drops it);
+``--act`` swaps the activation.
 
 Before the warm-up steps the step runs untimed for --spinup-ms (default 200 ms): an
-idle GPU takes tens of milliseconds of load to reach its working clock, which five
-warm-up steps of a fraction of a millisecond do not give it.
+idle GPU takes tens of milliseconds of load to reach its working clock.
 
 Reported:
-  value        useful (unpadded) TFLOP/s of the whole step: 4 d H sum_b pairs_b per
-               forward (10 d H pairs for the backward), pairs_b = visible (query,
-               key) pairs of sequence b, over the measured step time;
-  roofline     the forward attention kernel alone, timed with HIP events recorded on
-               its own stream right before and after its launch (library profiling
-               hook): useful TFLOP/s against the published dense bf16 MFMA peak, or,
-               for the HBM-bound batches (3, 4, 6), algorithmic bytes (Q, K, V read
-               and O written once) per second against the published 8 TB/s;
-               `traffic` is HBM bytes per launch from committed rocprofv3 counter
-               runs, or null when the kernel source changed since they were taken;
+  value        useful (unpadded) TFLOP/s of the whole step: 4 d H sum_b pairs_b for
+               the forward plus 10 d H pairs for the backward (the FlashAttention
+               convention), pairs_b = visible (query, key) pairs of sequence b, over
+               the wall-clock step time (K steps between two synchronisations);
+  step_ms      median / min / max of the per-step HIP-event durations;
+  fwd, bwd     each phase's kernels alone (HIP events the library records on its
+               stream right around them): forward TFLOP/s (the metric's own phase)
+               and its fraction of the dense bf16 peak; the dQ and dK/dV passes;
+  roofline     the dominant kernel of the step (longest median duration): its
+               algorithmic flop (forward 4 d, dQ pass 6 d, dK/dV pass 8 d per
+               visible pair and head: the products each kernel must form from its
+               inputs) or algorithmic bytes (inputs read and outputs written once)
+               per launch over its median duration, against the published peak its
+               arithmetic intensity makes binding (dense bf16 2.5 PFLOP/s, HBM 8
+               TB/s); `traffic` is HBM bytes per launch from committed rocprofv3
+               counter runs, or null when the kernel source changed since;
+  machine      the bf16 matrix rate a plain stream of products sustains on every
+               SIMD and the shader clock meanwhile (library probe, same run);
   cpu_baseline the fp64 oracle on a bounded sample of the same batch, on every host
                core (a reported baseline, not a target); its outputs double as a
                parity spot-check of the GPU result on the sampled pairs.
@@ -46,14 +53,17 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte where the two peaks meet
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-HBM_BOUND = (3, 4, 6)         # workloads whose forward is bound by HBM traffic, not the matrix cores
 KERNEL_SOURCES = {
     "ja_fwd_kernel": ["ja_fwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
     "ja_mx_fwd_kernel": ["ja_mx.hip", "ja_mx.h", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
-    "ja_bwd_kernels": ["ja_bwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
+    "ja_bwd_dq_kernel": ["ja_bwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
+    "ja_bwd_dkdv_kernel": ["ja_bwd.hip", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
+    "ja_blk_bwd_kernel": ["ja_block.hip", "ja_block.h", "ja_common.h", "ja_lds.h", "ja_tiles.h", "ja_internal.h"],
 }
 METRIC = "useful (unpadded) bf16 TFLOP/s of jagged attn fwd; % of MI355X MFMA peak"
+FWD_BWD_WORKLOADS = (5, 6, 7)  # batches whose configuration is forward + backward
 
 
 def log(msg: str) -> None:
@@ -84,11 +94,34 @@ def visible_pairs(lq: np.ndarray, lk: np.ndarray, causal: bool, window: int, blo
     return total
 
 
-def roofline_kernel(workload: int) -> str:
-    """The kernel the roofline is taken on: the forward attention kernel (the MXFP8
-    forward for workload 8; every other workload, the block one included, runs the
-    general forward)."""
-    return "ja_mx_fwd_kernel" if workload == 8 else "ja_fwd_kernel"
+def kernel_work(name: str, w, pairs: int, Tq: int, Tk: int, need_lse: bool):
+    """(algorithmic flop, algorithmic bytes) of one launch of kernel `name` on batch w:
+    the matrix products the kernel must form from its inputs, and its inputs read
+    and outputs written once."""
+    e = 2 if w.dtype == "bf16" else 4
+    row = w.H * w.d * e  # bytes of one token row of one tensor
+    softmax = w.act == "softmax"
+    if name in ("ja_fwd_kernel", "ja_mx_fwd_kernel"):
+        if name == "ja_mx_fwd_kernel":
+            row = w.H * w.d  # one byte per element (plus block scales, 1/32 of that, left out)
+        flop = 4.0 * w.d * w.H * pairs
+        byts = row * (Tq + 2 * Tk) + 2 * w.H * w.d * Tq + (4 * w.H * Tq if need_lse else 0)
+    elif name == "ja_bwd_dq_kernel":
+        flop = 6.0 * w.d * w.H * pairs                      # S, dP, dQ
+        byts = row * (2 * Tq + 2 * Tk) + row * Tq           # Q, dO, K, V in; dQ out
+        if softmax:
+            byts += row * Tq + 4 * w.H * Tq + 4 * w.H * Tq  # O, lse in; Di out
+    elif name == "ja_bwd_dkdv_kernel":
+        flop = 8.0 * w.d * w.H * pairs                      # S, dP, dV, dK
+        byts = row * (2 * Tk + 2 * Tq) + 2 * row * Tk       # K, V, Q, dO in; dK, dV out
+        if softmax:
+            byts += 8 * w.H * Tq                            # lse, Di in
+    elif name == "ja_blk_bwd_kernel":
+        flop = 10.0 * w.d * w.H * pairs                     # S, dP, dV, dK, dQ in one pass
+        byts = row * 4 * Tq + row * 3 * Tq                  # Q, K, V, dO in; dQ, dK, dV out
+    else:
+        raise ValueError(name)
+    return flop, float(byts)
 
 
 def kernel_sha(name: str) -> str:
@@ -112,26 +145,34 @@ def recorded_traffic(name: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _stats(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(xs)), 4), "min": round(float(xs.min()), 4),
+            "max": round(float(xs.max()), 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8])
-    ap.add_argument("--bwd", action="store_true",
-                    help="time forward + backward (softmax for 2, 5 and 6, SiLU / GELU for 3, 4 and 7)")
+    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--bwd", action="store_true", help="add the backward to a forward-only batch (2, 3, 4)")
+    ap.add_argument("--fwd-only", action="store_true", help="drop the backward of batches 5, 6, 7")
     ap.add_argument("--act", choices=["softmax", "silu", "gelu", "gelu_taylor"], default=None,
                     help="run the workload with another activation (e.g. 7 with the tanh GELU)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget for the CPU baseline")
     ap.add_argument("--spinup-ms", type=float, default=200.0,
                     help="untimed load before the warm-up steps, so the GPU has left its idle clock state")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the machine probe (sustained MFMA rate, clock)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy (y = x * 1) of MIB MiB, 5 times: the reference "
                          "for scaling HBM byte counters")
-    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --workload (and of "
-                         "--copy-calibration 1024) into HBM bytes per forward launch in profiles/traffic.json")
+                         "--copy-calibration 1024) into HBM bytes per launch of KERNEL in profiles/traffic.json")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
@@ -158,9 +199,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    do_bwd = (args.workload in FWD_BWD_WORKLOADS or args.bwd) and not args.fwd_only
     log(f"[bench] generating workload {args.workload}")
     w = W.workload(args.workload, act=args.act)
-    if args.bwd and w.dout is None:
+    if do_bwd and w.dout is None:
         W.with_upstream_gradient(w, 1000 + args.workload)  # seeded dO for the batches that draw none
 
     def up(a):
@@ -171,10 +213,10 @@ def main() -> int:
 
     q, k, v = up(w.q), up(w.k), up(w.v)
     qo, ko = up(w.q_offsets), up(w.k_offsets)
-    dout = up(w.dout) if args.bwd else None
+    dout = up(w.dout) if do_bwd else None
     mx = bool(w.extra.get("mxfp8"))
     if mx:
-        if args.bwd:
+        if do_bwd:
             print("the MXFP8 path has no backward", file=sys.stderr)
             return 2
         # Quantized once, outside the timed steps (upstream kernels emit MXFP8).
@@ -185,7 +227,8 @@ def main() -> int:
     out = torch.empty_like(q)
     # The block path (blocks of at most 64 tokens) keeps no log-sum-exp: its
     # backward recomputes each block's softmax.
-    need_lse = w.act == "softmax" and not (w.block and w.block <= 64)
+    fused_block = bool(w.block and w.block <= 64)
+    need_lse = w.act == "softmax" and not fused_block
     lse = torch.empty((Tq, w.H), dtype=torch.float32, device=dev) if need_lse else None
     if mx:
         ws_fwd, ws_bwd = int(lib.ja_fwd_mxfp8_workspace_size(w.B, w.H, w.d, Tq, Tk)), 0
@@ -193,20 +236,24 @@ def main() -> int:
         ws_fwd = ws_bwd = ja.block_attn_workspace_size(w.B, w.H, w.d, Tq, w.block, w.causal)
     else:
         ws_fwd = ja.fwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window)
-        ws_bwd = ja.bwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window) if args.bwd else 0
+        ws_bwd = ja.bwd_workspace_size(w.B, w.H, w.d, Tq, Tk, w.act, w.causal, w.window) if do_bwd else 0
     ws = torch.empty(max(ws_fwd, 256), dtype=torch.uint8, device=dev)
-    if args.bwd:
+    if do_bwd:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         bws = torch.empty(max(ws_bwd, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     pairs = visible_pairs(w.lq, w.lk, w.causal, w.window, w.block)
     fwd_flop = 4.0 * w.d * w.H * pairs
-    bwd_flop = 10.0 * w.d * w.H * pairs if args.bwd else 0.0
+    bwd_flop = 10.0 * w.d * w.H * pairs if do_bwd else 0.0
+    fwd_name = "ja_mx_fwd_kernel" if mx else "ja_fwd_kernel"
+    bwd_names = (["ja_blk_bwd_kernel"] if fused_block else ["ja_bwd_dq_kernel", "ja_bwd_dkdv_kernel"]) if do_bwd \
+        else []
 
     def step(ev=None):
         if ev is not None:
-            lib.ja_set_profile_events(ev[0].cuda_event, ev[1].cuda_event)
+            ev[0].record(stream)
+            lib.ja_set_profile_events(ev[1].cuda_event, ev[2].cuda_event)
         if mx:
             ja.jagged_attn_fwd_mxfp8(qm[0], qm[1], qm[2], km[0], km[1], km[2], vm[0], vm[1], qo, ko,
                                      causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse,
@@ -217,9 +264,10 @@ def main() -> int:
         else:
             ja.jagged_attn_fwd(q, k, v, qo, ko, act=w.act, causal=w.causal, window=w.window, scale=w.scale,
                                out=out, lse=lse, workspace=ws, stream=stream)
-        if args.bwd:
+        if do_bwd:
             if ev is not None:
-                lib.ja_set_profile_events(ev[2].cuda_event, ev[3].cuda_event)
+                lib.ja_set_profile_events3(ev[3].cuda_event, ev[4].cuda_event if not fused_block else None,
+                                           ev[5].cuda_event)
             if w.block:
                 ja.jagged_block_attn_bwd(q, k, v, out, dout, lse, qo, w.block, causal=w.causal, scale=w.scale,
                                          dq=dq, dk=dk, dv=dv, workspace=bws, stream=stream)
@@ -228,10 +276,8 @@ def main() -> int:
                                    scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws, stream=stream)
         if ev is not None:
             lib.ja_set_profile_events(None, None)
+            ev[6].record(stream)
 
-    # An idle GPU needs tens of milliseconds of load to reach its working clock (on
-    # MI355X the w2 forward measures 0.205 ms after 5 warm-up steps, 0.178 ms after
-    # 200): run the same step, untimed, for spinup_ms before the warm-up steps.
     log(f"[bench] spin-up {args.spinup_ms:.0f} ms, then warmup {args.warmup} steps")
     t_end = time.perf_counter() + args.spinup_ms * 1e-3
     while time.perf_counter() < t_end:
@@ -242,51 +288,57 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    nev = 4 if args.bwd else 2
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    # per step: [step start, fwd before, fwd after, bwd before, bwd mid, bwd after, step end]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     for evs in events:  # create the underlying HIP events before handing them to the library
         for e in evs:
             e.record(stream)
-    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
 
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
-    whole0.record(stream)
     for i in range(args.steps):
         step(events[i])
-    whole1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    ms_events = whole0.elapsed_time(whole1) / args.steps
-    fwd_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    bwd_kernel_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if args.bwd else None
+    step_ms = [e[0].elapsed_time(e[6]) for e in events]
+    kms = {fwd_name: [e[1].elapsed_time(e[2]) for e in events]}
+    if do_bwd:
+        if fused_block:
+            kms["ja_blk_bwd_kernel"] = [e[3].elapsed_time(e[5]) for e in events]
+        else:
+            kms["ja_bwd_dq_kernel"] = [e[3].elapsed_time(e[4]) for e in events]
+            kms["ja_bwd_dkdv_kernel"] = [e[4].elapsed_time(e[5]) for e in events]
+    med = {n: float(np.median(x)) for n, x in kms.items()}
     total_flop = fwd_flop + bwd_flop
     value = total_flop / (ms_per_step * 1e-3) / 1e12
+    peak_mm = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
 
-    name = roofline_kernel(args.workload)
-    tflops = fwd_flop / (fwd_kernel_ms * 1e-3) / 1e12
-    if args.workload in HBM_BOUND:
-        # short key/value (3), short query (4) and 64-token block (6) batches are
-        # HBM-bound: the algorithmic traffic is reading Q, K, V once and writing O
-        # (and the fp32 lse where the backward needs it) once.
-        min_bytes = 2 * w.H * w.d * (2 * Tq + 2 * Tk) + (4 * w.H * Tq if need_lse else 0)
-        gbs = min_bytes / (fwd_kernel_ms * 1e-3) / 1e9
-        copy = measure_copy_gbs(1024)  # what a plain streaming kernel sustains on this GPU, same run
-        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": min_bytes,
-                    "copy_gbs": round(copy, 1), "frac_of_copy": round(gbs / copy, 4),
-                    "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
-    else:
-        peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
-        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(tflops / peak, 4), "flop_per_launch": fwd_flop}
-    roofline["traffic"] = recorded_traffic(name, f"w{args.workload}")
-    roofline["kernel"] = name
-    roofline["kernel_ms"] = round(fwd_kernel_ms, 4)
+    def roofline_of(name):
+        flop, byts = kernel_work(name, w, pairs, Tq, Tk, need_lse)
+        t = med[name] * 1e-3
+        intensity = flop / byts
+        r = {"kernel": name, "kernel_ms": round(med[name], 4), "flop_per_launch": flop, "bytes_per_launch": byts,
+             "intensity_flop_per_byte": round(intensity, 1)}
+        if intensity >= RIDGE:
+            a = flop / t / 1e12
+            r.update({"bound": "mfma", "achieved": round(a, 2), "peak": peak_mm, "unit": "TFLOP/s",
+                      "frac": round(a / peak_mm, 4)})
+        else:
+            a = byts / t / 1e9
+            r.update({"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(a / PEAK_HBM_GBS, 4), "tflops": round(flop / t / 1e12, 2)})
+        r["traffic"] = recorded_traffic(name, f"w{args.workload}" + ("+bwd" if name != fwd_name else ""))
+        return r
 
+    dominant = max(med, key=lambda n: med[n])
+    roofline = roofline_of(dominant)
+    fwd_t = med[fwd_name] * 1e-3
+    fwd = {"kernel": fwd_name, "kernel_ms": _stats(kms[fwd_name]),
+           "tflops": round(fwd_flop / fwd_t / 1e12, 2), "frac_of_peak": round(fwd_flop / fwd_t / 1e12 / peak_mm, 4),
+           "roofline": roofline_of(fwd_name) if dominant != fwd_name else "as roofline"}
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -296,39 +348,74 @@ def main() -> int:
         "warmup": args.warmup,
         "spinup_ms": args.spinup_ms,
         "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_events": round(ms_events, 4),
+        "step_ms": _stats(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "pct_of_peak": round(100.0 * value / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS), 2),
+        "pct_of_peak": round(100.0 * value / peak_mm, 2),
         "dtype": "fp8-e4m3 (MX, [32,32] block scales)" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": w.extra.get("description", w.name), "B": w.B, "H": w.H, "d": w.d,
                    "act": w.act, "causal": bool(w.causal), "window": int(w.window), "block": int(w.block),
-                   "scale": round(w.scale, 6),
-                   "q_tokens": int(Tq),
-                   "kv_tokens": int(Tk), "visible_pairs": int(pairs), "fwd_flop": fwd_flop,
-                   "bwd_flop": bwd_flop, "phases": "fwd+bwd" if args.bwd else "fwd"},
+                   "scale": round(w.scale, 6), "q_tokens": int(Tq), "kv_tokens": int(Tk),
+                   "visible_pairs": int(pairs), "fwd_flop": fwd_flop, "bwd_flop": bwd_flop,
+                   "phases": "fwd+bwd" if do_bwd else "fwd"},
         "roofline": roofline,
+        "fwd": fwd,
     }
-    if args.bwd:
-        result["bwd"] = {"kernel_ms": round(bwd_kernel_ms, 4),
-                         "tflops": round(bwd_flop / (bwd_kernel_ms * 1e-3) / 1e12, 2)}
-        if args.workload in (3, 4, 6):
-            # reading Q, K, V, dO once and writing dQ, dK, dV once (the two-pass
-            # softmax backward also reads O and lse)
-            min_b = 2 * w.H * w.d * (3 * Tq + 4 * Tk)
-            if need_lse:
-                min_b += 2 * w.H * w.d * Tq + 4 * w.H * Tq
-            result["bwd"]["min_hbm_bytes"] = min_b
-            result["bwd"]["hbm_gbs_at_min_bytes"] = round(min_b / (bwd_kernel_ms * 1e-3) / 1e9, 1)
+    if do_bwd:
+        bt = sum(med[n] for n in bwd_names) * 1e-3
+        bwd = {"kernels_ms": round(bt * 1e3, 4), "tflops": round(bwd_flop / bt / 1e12, 2),
+               "frac_of_peak": round(bwd_flop / bt / 1e12 / PEAK_BF16_TFLOPS, 4), "flop_convention": "10 d H pairs"}
+        for n in bwd_names:
+            bwd[n] = {"kernel_ms": _stats(kms[n])}
+            if n != dominant:
+                bwd[n]["roofline"] = roofline_of(n)
+        result["bwd"] = bwd
+    if roofline["bound"] == "hbm":
+        copy = measure_copy_gbs(1024)  # what a plain streaming kernel sustains on this GPU, same run
+        roofline["copy_gbs"] = round(copy, 1)
+        roofline["frac_of_copy"] = round(roofline["achieved"] / copy, 4)
+    if not args.no_probe:
+        result["machine"] = machine_probe(lib, torch, stream)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, out, lse, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, out, lse, (dq, dk, dv) if do_bwd and not w.block else None,
+                                              args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
     return 0
+
+
+def machine_probe(lib, torch, stream, iters: int = 20000) -> dict:
+    """Sustained dense bf16 matrix rate and shader clock (ja_probe_mfma), event-timed."""
+    import ctypes
+
+    nbytes = int(lib.ja_probe_mfma_workspace_size())
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    groups, fpg, khz = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
+
+    def run(n):
+        st = lib.ja_probe_mfma(n, ws.data_ptr(), nbytes, ctypes.byref(groups), ctypes.byref(fpg), ctypes.byref(khz),
+                               int(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"ja_probe_mfma failed: {st}")
+
+    run(iters // 4)  # warm
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run(iters)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ticks = ws[: 16 * groups.value].cpu().view(torch.int64).numpy().reshape(-1, 2).astype(np.float64)
+    mhz = np.median(ticks[:, 0] / (ticks[:, 1] / (khz.value * 1e3))) / 1e6
+    tflops = groups.value * fpg.value / (ms * 1e-3) / 1e12
+    return {"sustained_mfma_bf16_tflops": round(tflops, 1), "sustained_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "sclk_mhz_under_mfma": round(float(mhz), 0), "probe_ms": round(ms, 3), "workgroups": groups.value,
+            "method": "ja_probe_mfma: one 4-wave workgroup per CU, 4 independent 32x32x16 bf16 chains per wave, "
+                      f"{iters} rounds; clock = shader cycles / real-time ticks of the loop (median over CUs)"}
 
 
 def _counter_per_dispatch(run_dir: str, counter: str, kernel_part: str) -> list[float]:
@@ -349,15 +436,17 @@ def _counter_per_dispatch(run_dir: str, counter: str, kernel_part: str) -> list[
     return [per[k] for k in sorted(per)]
 
 
-def record_traffic(workload: int, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> int:
-    """HBM bytes per forward launch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+def record_traffic(workload: int, kernel: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                   copy_write_dir: str) -> int:
+    """HBM bytes per launch of `kernel` = FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
     scaled so that the copy kernel of known size reads and writes exactly its bytes."""
+    if kernel not in KERNEL_SOURCES:
+        raise SystemExit(f"unknown kernel {kernel}")
     copy_bytes = 1024 * (1 << 20)
     cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "elementwise")
     cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "elementwise")
-    name = roofline_kernel(workload)
-    kf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", name)
-    kw = _counter_per_dispatch(write_dir, "WRITE_SIZE", name)
+    kf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
+    kw = _counter_per_dispatch(write_dir, "WRITE_SIZE", kernel)
     if not (cf and cw and kf and kw):
         raise SystemExit("missing dispatches in the counter runs")
     f_scale = copy_bytes / (float(np.median(cf)) * 1024.0)
@@ -368,19 +457,21 @@ def record_traffic(workload: int, fetch_dir: str, write_dir: str, copy_fetch_dir
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         data = {}
-    data.setdefault(name, {})[f"w{workload}"] = {
+    fwd = kernel in ("ja_fwd_kernel", "ja_mx_fwd_kernel")
+    key = f"w{workload}" + ("" if fwd else "+bwd")
+    data.setdefault(kernel, {})[key] = {
         "hbm_bytes_per_launch": round(fetch + write),
         "fetch_bytes": round(fetch), "write_bytes": round(write),
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-        "source_sha256": kernel_sha(name),
+        "source_sha256": kernel_sha(kernel),
         "method": "rocprofv3 --pmc FETCH_SIZE then --pmc WRITE_SIZE on bench.py --workload "
-                  f"{workload} --steps 2 --warmup 1 --no-cpu-baseline; KiB per dispatch (median) x 1024 x "
+                  f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --no-probe; KiB per dispatch (median) x 1024 x "
                   "scale, scale = 1 GiB / the same counter on bench.py --copy-calibration 1024",
     }
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(data, fh, indent=1, sort_keys=True)
         fh.write("\n")
-    print(json.dumps(data[name][f"w{workload}"]))
+    print(json.dumps(data[kernel][key]))
     return 0
 
 
@@ -425,10 +516,13 @@ def copy_calibration(mib: int) -> int:
     return 0
 
 
-def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
-    """Time the fp64 oracle on a bounded sample of (sequence, head) pairs of the batch."""
+def cpu_baseline(w, out_gpu, lse_gpu, grads_gpu, budget_s: float) -> dict:
+    """Time the fp64 oracle on a bounded sample of (sequence, head) pairs of the batch:
+    the same step as the GPU's (forward, or forward + backward when grads_gpu is given),
+    counted in the same useful flop."""
     import oracle  # test infrastructure: used here for the CPU baseline only
 
+    with_bwd = grads_gpu is not None
     if w.extra.get("mxfp8"):
         # the MXFP8 forward on the oracle's quantization of the batch (bit-identical to
         # the library's, which the tests check); the quantization itself is upstream
@@ -439,20 +533,26 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
         def run_oracle(mask):
             return oracle.fwd_mxfp8(qm[0], qm[1], qm[2], km[0], km[1], km[2], vm[0], vm[1], w.q_offsets,
                                     w.k_offsets, w.causal, w.window, w.scale, pquant=True, pair_mask=mask)
+    elif with_bwd:
+        def run_oracle(mask):  # (out, lse, dq, dk, dv)
+            return oracle.bwd(w.q, w.k, w.v, w.dout, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale,
+                              pair_mask=mask, block=w.block)
     else:
         def run_oracle(mask):
             return oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, w.act, w.causal, w.window, w.scale,
                               pair_mask=mask, block=w.block)
 
+    per_pair = (4.0 + (10.0 if with_bwd else 0.0)) * w.d
     rng = np.random.default_rng(1234)
     B, H = w.B, w.H
     order = [(int(b), int(h)) for b in rng.permutation(B) for h in range(H)]
-    pair_flop = np.array([4.0 * w.d * visible_pairs(w.lq[b:b + 1], w.lk[b:b + 1], w.causal, w.window, w.block)
+    pair_flop = np.array([per_pair * visible_pairs(w.lq[b:b + 1], w.lk[b:b + 1], w.causal, w.window, w.block)
                           for b, _ in order])
     # Calibrate the oracle's rate on a growing prefix of the pair order (at least
     # ~1 s of work), then fill the budget.
+    # (at least one pair per oracle thread, so the calibration runs as parallel as the sample)
     mask = np.zeros((B, H), dtype=bool)
-    rate, n_cal = None, 1
+    rate, n_cal = None, max(1, oracle.num_threads())
     while rate is None:
         mask[:] = False
         for b, h in order[:n_cal]:
@@ -460,7 +560,7 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
         t = time.perf_counter()
         run_oracle(mask)
         dt = time.perf_counter() - t
-        if dt >= 1.0 or n_cal >= len(order):
+        if dt >= 2.0 or n_cal >= len(order):
             rate = max(pair_flop[:n_cal].sum(), 1.0) / max(dt, 1e-4)
         n_cal *= 2
     budget_flop = rate * budget_s
@@ -473,23 +573,36 @@ def cpu_baseline(w, out_gpu, lse_gpu, budget_s: float) -> dict:
         acc += pair_flop[i]
     log(f"[bench] cpu baseline: {int(mask.sum())} pairs, {acc:.3g} flop")
     t = time.perf_counter()
-    ref, ref_lse = run_oracle(mask)
+    res = run_oracle(mask)
     dt = time.perf_counter() - t
-    # parity spot-check of the GPU output on the same pairs
-    got = out_gpu.float().cpu().numpy().astype(np.float64)
-    sel = np.zeros(got.shape[:2], dtype=bool)
-    for b in range(B):
-        for h in range(H):
-            if mask[b, h]:
-                sel[w.q_offsets[b]:w.q_offsets[b + 1], h] = True
-    err = np.abs(got[sel] - ref[sel])
+
+    # parity spot-check of the GPU outputs on the same pairs
+    def rows(off):
+        sel = np.zeros((int(off[-1]), H), dtype=bool)
+        for b in range(B):
+            for h in range(H):
+                if mask[b, h]:
+                    sel[off[b]:off[b + 1], h] = True
+        return sel
+
+    def err_of(gpu, ref, sel):
+        e = np.abs(gpu.float().cpu().numpy().astype(np.float64)[sel] - ref[sel])
+        return {"max_abs": float(e.max()) if e.size else 0.0, "mean_abs": float(e.mean()) if e.size else 0.0,
+                "elements": int(e.size)}
+
+    selq = rows(w.q_offsets)
+    parity = {"out": err_of(out_gpu, res[0], selq)}
+    if with_bwd:
+        selk = rows(w.k_offsets)
+        for name, g, r, sel in (("dq", grads_gpu[0], res[2], selq), ("dk", grads_gpu[1], res[3], selk),
+                                ("dv", grads_gpu[2], res[4], selk)):
+            parity[name] = err_of(g, r, sel)
     return {"value": round(acc / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{int(mask.sum())} of {B * H} (sequence, head) pairs of the same batch, "
-                      f"{acc:.4g} useful flop, fp64 C oracle on all host cores",
-            "parity_on_sample": {"max_abs": float(err.max()) if err.size else 0.0,
-                                 "mean_abs": float(err.mean()) if err.size else 0.0,
-                                 "elements": int(err.size)}}
+                      f"{'forward + backward' if with_bwd else 'forward'}, {acc:.4g} useful flop "
+                      f"(same flop convention as value), fp64 C oracle on all host cores",
+            "parity_on_sample": parity}
 
 
 if __name__ == "__main__":

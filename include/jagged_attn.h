@@ -124,13 +124,17 @@ size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_
  *     and dS = act'(Z) * (dO V^T) / Lk; out and lse are not read and may be
  *     NULL.
  *   dout [Tq,H,d]: upstream gradient; dq [Tq,H,d], dk/dv [Tk,H,d]: outputs,
- *   every row written (rows no query sees get zeros). */
+ *   every row written (rows no query sees get zeros), of element type
+ *   grad_dtype: dtype (bf16) or JA_F32. fp32 gradients keep the fp32 accumulators
+ *   unrounded, for callers that accumulate gradients in fp32 or need results
+ *   below bf16's resolution (a gradient of magnitude 4 to 8 is otherwise stored
+ *   to within 2^-6); anything else returns JA_ERR_UNSUPPORTED. */
 ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v,
                             const void* out, const void* dout, const float* lse,
                             const int32_t* q_offsets, const int32_t* k_offsets,
                             int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
                             int32_t act, int32_t causal, int32_t window, float scale,
-                            int32_t dtype, void* dq, void* dk, void* dv,
+                            int32_t dtype, int32_t grad_dtype, void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace jagged_block_attn_fwd and jagged_block_attn_bwd
@@ -256,6 +260,25 @@ ja_status_t ja_validate_offsets(const int32_t* offsets, int32_t B, int64_t T, vo
  * the attention kernels' own duration. Pass NULL, NULL to stop. The events are
  * owned by the caller and must outlive the calls that record them. */
 void ja_set_profile_events(void* before, void* after);
+
+/* As ja_set_profile_events, and jagged_attn_bwd also records `mid` between its
+ * dQ pass and its dK/dV pass (mid may be NULL), so each pass can be timed alone. */
+void ja_set_profile_events3(void* before, void* mid, void* after);
+
+/* Machine probe, a measurement aid outside the attention path: one workgroup of
+ * four waves per compute unit (one wave per SIMD) issues `iters` rounds of four
+ * independent 32x32x16 bf16 matrix products, with no memory traffic in its loop,
+ * so its duration gives the matrix-core rate the GPU sustains, and the shader
+ * clock it sustains meanwhile. Writes, per workgroup g, the shader-clock cycles
+ * and the constant-rate real-time counter ticks of the loop as uint64 at
+ * workspace[2 g] and workspace[2 g + 1] (device memory, at least
+ * ja_probe_mfma_workspace_size() bytes, 16-byte aligned; the rest is scratch).
+ * Host outputs: *groups = workgroups launched (the compute-unit count),
+ * *flop_per_group = matrix flop each performs, *wallclock_khz = the real-time
+ * counter's rate. Enqueued on stream, no synchronisation. */
+size_t ja_probe_mfma_workspace_size(void);
+ja_status_t ja_probe_mfma(int32_t iters, void* workspace, size_t workspace_bytes, int32_t* groups,
+                          int64_t* flop_per_group, int32_t* wallclock_khz, void* stream);
 
 /* Static string for a status code. */
 const char* ja_status_string(ja_status_t status);

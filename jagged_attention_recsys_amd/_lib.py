@@ -20,7 +20,7 @@ SIGNATURES = {
                                _i32, _vp, _vp, _vp, _sz, _vp]),
     "ja_bwd_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32]),
     "jagged_attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32, _i32,
-                               _i32, _f32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+                               _i32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ja_block_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i32, _i32, _i32]),
     "jagged_block_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _f32, _i32, _vp, _vp,
                                      _vp, _sz, _vp]),
@@ -36,6 +36,9 @@ SIGNATURES = {
     "ja_fwd_tile_shape": (_i32, [_i32, _i32, _i64, _i64, _i32, _i32, _vp, _vp]),
     "ja_validate_offsets": (_i32, [_vp, _i32, _i64, _vp]),
     "ja_set_profile_events": (None, [_vp, _vp]),
+    "ja_set_profile_events3": (None, [_vp, _vp, _vp]),
+    "ja_probe_mfma_workspace_size": (_sz, []),
+    "ja_probe_mfma": (_i32, [_i32, _vp, _sz, _vp, _vp, _vp, _vp]),
     "ja_status_string": (ctypes.c_char_p, [_i32]),
     "ja_version": (_i32, []),
 }

@@ -25,6 +25,7 @@ constexpr size_t kWsAlign = 256;
 
 // Events recorded around the attention kernels (ja_set_profile_events).
 thread_local hipEvent_t g_prof_before = nullptr;
+thread_local hipEvent_t g_prof_mid = nullptr;
 thread_local hipEvent_t g_prof_after = nullptr;
 constexpr int kMaxDevices = 64;
 
@@ -224,11 +225,12 @@ ja_status_t fwd_impl(const void* q, const void* k, const void* v, const int32_t*
 ja_status_t bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout,
                      const float* lse, const int32_t* q_offsets, const int32_t* k_offsets, int32_t B, int32_t H,
                      int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t causal, int32_t window, int32_t bsh,
-                     float scale, int32_t dtype, void* dq, void* dk, void* dv, void* workspace,
+                     float scale, int32_t dtype, int32_t grad_dtype, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, void* stream) {
     ja_status_t st = check_common(B, H, d, Tq, Tk, act, window, scale, dtype);
     if (st != JA_OK) return st;
     if (!bwd_supported(dtype, d, act)) return JA_ERR_UNSUPPORTED;
+    if (grad_dtype != dtype && grad_dtype != JA_F32) return JA_ERR_UNSUPPORTED;
     if (B == 0 || (Tq == 0 && Tk == 0)) return JA_OK;
     if (!q_offsets || !k_offsets || !workspace) return JA_ERR_INVALID_ARG;
     const bool softmax = act == JA_ACT_SOFTMAX;  // only softmax reads the forward's out and lse
@@ -296,14 +298,16 @@ ja_status_t bwd_impl(const void* q, const void* k, const void* v, const void* ou
     ba.window = window;
     ba.bsh = bsh;
     ba.scale = scale;
-    const int64_t cap_q = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, false);
-    const int64_t cap_k = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, true);
+    ba.grad_f32 = grad_dtype == JA_F32 ? 1 : 0;
+    const int64_t cap_q = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, false, ba.grad_f32 != 0);
+    const int64_t cap_k = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, true, ba.grad_f32 != 0);
     int64_t gq = p.max_q_pairs * H, gk = p.max_k_pairs * H;
     gq = gq < cap_q ? gq : cap_q;
     gk = gk < cap_k ? gk : cap_k;
     if (gq < 1) gq = 1;
     if (gk < 1) gk = 1;
-    if (launch_bwd(ba, d, act, (int)gq, (int)gk, s, g_prof_before, g_prof_after) != hipSuccess) return JA_ERR_HIP;
+    if (launch_bwd(ba, d, act, (int)gq, (int)gk, s, g_prof_before, g_prof_mid, g_prof_after) != hipSuccess)
+        return JA_ERR_HIP;
     return JA_OK;
 }
 
@@ -409,10 +413,10 @@ size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_
 ja_status_t jagged_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                             const float* lse, const int32_t* q_offsets, const int32_t* k_offsets, int32_t B,
                             int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act, int32_t causal,
-                            int32_t window, float scale, int32_t dtype, void* dq, void* dk, void* dv,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            int32_t window, float scale, int32_t dtype, int32_t grad_dtype, void* dq, void* dk,
+                            void* dv, void* workspace, size_t workspace_bytes, void* stream) {
     return bwd_impl(q, k, v, out, dout, lse, q_offsets, k_offsets, B, H, d, Tq, Tk, act, causal, window, kNoBlock,
-                    scale, dtype, dq, dk, dv, workspace, workspace_bytes, stream);
+                    scale, dtype, grad_dtype, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 ja_status_t jagged_block_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -423,7 +427,7 @@ ja_status_t jagged_block_attn_bwd(const void* q, const void* k, const void* v, c
     if (bsh < 0) return JA_ERR_INVALID_ARG;
     if (!blk_supported(dtype, d, bsh))
         return bwd_impl(q, k, v, out, dout, lse, offsets, offsets, B, H, d, T, T, JA_ACT_SOFTMAX, causal, 0, bsh,
-                        scale, dtype, dq, dk, dv, workspace, workspace_bytes, stream);
+                        scale, dtype, dtype, dq, dk, dv, workspace, workspace_bytes, stream);
     ja_status_t st = check_common(B, H, d, T, T, JA_ACT_SOFTMAX, 0, scale, dtype);
     if (st != JA_OK) return st;
     if (B == 0 || T == 0) return JA_OK;
@@ -620,7 +624,40 @@ ja_status_t ja_validate_offsets(const int32_t* offsets, int32_t B, int64_t T, vo
 
 void ja_set_profile_events(void* before, void* after) {
     g_prof_before = static_cast<hipEvent_t>(before);
+    g_prof_mid = nullptr;
     g_prof_after = static_cast<hipEvent_t>(after);
+}
+
+void ja_set_profile_events3(void* before, void* mid, void* after) {
+    g_prof_before = static_cast<hipEvent_t>(before);
+    g_prof_mid = static_cast<hipEvent_t>(mid);
+    g_prof_after = static_cast<hipEvent_t>(after);
+}
+
+size_t ja_probe_mfma_workspace_size(void) {
+    const size_t groups = (size_t)device_cus();
+    return align_up(sizeof(uint64_t) * 2 * groups) + sizeof(float) * groups * (size_t)probe_threads();
+}
+
+ja_status_t ja_probe_mfma(int32_t iters, void* workspace, size_t workspace_bytes, int32_t* groups,
+                          int64_t* flop_per_group, int32_t* wallclock_khz, void* stream) {
+    if (iters < 1 || !workspace || !groups || !flop_per_group || !wallclock_khz || !aligned(workspace, 16))
+        return JA_ERR_INVALID_ARG;
+    const int g = device_cus();
+    const size_t off_sink = align_up(sizeof(uint64_t) * 2 * (size_t)g);
+    if (workspace_bytes < off_sink + sizeof(float) * (size_t)g * (size_t)probe_threads()) return JA_ERR_WORKSPACE;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+        return JA_ERR_HIP;
+    char* ws = static_cast<char*>(workspace);
+    if (launch_probe_mfma(iters, g, reinterpret_cast<uint64_t*>(ws), reinterpret_cast<float*>(ws + off_sink),
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+        return JA_ERR_HIP;
+    *groups = g;
+    *flop_per_group = (int64_t)iters * probe_flop_per_iter();
+    *wallclock_khz = khz;
+    return JA_OK;
 }
 
 const char* ja_status_string(ja_status_t status) {

@@ -55,7 +55,7 @@ struct BwdCfg {
 // dQ pass ---------------------------------------------------------------------
 // The dQ pass fits in 256 VGPRs, so two of its workgroups share a CU; the dK/dV
 // pass holds two accumulators per row and runs one workgroup per CU.
-template <typename T, int D, int ACT>
+template <typename T, int D, int ACT, typename GT>
 __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = BwdCfg<T, D>;
@@ -230,20 +230,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
             if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
         }
 
-        if constexpr (KP == 8) {
+        if constexpr (KP == 8 && sizeof(GT) == 2) {
             // Whole rows out through the wave's region (the stage loop ended on a
             // barrier, or loaded nothing).
             RT::put_acc(wreg, dqacc, a.scale, lane);
             RT::store((bf16*)a.dq + (qo + qw0) * rs + (int64_t)h * D, rs, Lq - qw0, wreg, lane);
         } else if (row_ok) {
-            T* dst = (T*)a.dq + (qo + my_row) * rs + (int64_t)h * D + 4 * grp;
+            // fp32 gradients (or fp32 inputs): 16 bytes of one row per lane and store.
+            GT* dst = (GT*)a.dq + (qo + my_row) * rs + (int64_t)h * D + 4 * grp;
             const float sc = a.scale;
 #pragma unroll
             for (int i = 0; i < C::ND; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    store4<T>(dst + 32 * i + 8 * j, dqacc[i][4 * j] * sc, dqacc[i][4 * j + 1] * sc,
-                              dqacc[i][4 * j + 2] * sc, dqacc[i][4 * j + 3] * sc);
+                    store4<GT>(dst + 32 * i + 8 * j, dqacc[i][4 * j] * sc, dqacc[i][4 * j + 1] * sc,
+                               dqacc[i][4 * j + 2] * sc, dqacc[i][4 * j + 3] * sc);
         }
     }
 #else
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
 template <int D> constexpr int kDkdvWavesMin = D == 128 ? 1 : 2;
 template <int D> constexpr int kDkdvWavesMax = D == 128 ? 8 : 2;
 
-template <typename T, int D, int ACT>
+template <typename T, int D, int ACT, typename GT>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWavesMin<D>, kDkdvWavesMax<D>))) void ja_bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = BwdCfg<T, D>;
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         }
         const bool owner = !pair_split || wave < 2;  // writes its keys' dK, dV
         if (!owner) {
-        } else if constexpr (KP == 8) {
+        } else if constexpr (KP == 8 && sizeof(GT) == 2) {
             // Whole rows out through the wave's region (the stage loop ended on a
             // barrier, or loaded nothing): dK, then dV.
             const int64_t wrow = (ko + kw0) * rs + (int64_t)h * D;
@@ -505,18 +506,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
             RT::put_acc(wreg, dvacc, 1.0f, lane);
             RT::store((bf16*)a.dv + wrow, rs, Lk - kw0, wreg, lane);
         } else if (key_ok) {
+            // fp32 gradients (or fp32 inputs): 16 bytes of one row per lane and store.
             const int64_t base = (ko + my_key) * rs + (int64_t)h * D + 4 * grp;
-            T* dk = (T*)a.dk + base;
-            T* dv = (T*)a.dv + base;
+            GT* dk = (GT*)a.dk + base;
+            GT* dv = (GT*)a.dv + base;
             const float sc = a.scale;
 #pragma unroll
             for (int i = 0; i < C::ND; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    store4<T>(dk + 32 * i + 8 * j, dkacc[i][4 * j] * sc, dkacc[i][4 * j + 1] * sc,
-                              dkacc[i][4 * j + 2] * sc, dkacc[i][4 * j + 3] * sc);
-                    store4<T>(dv + 32 * i + 8 * j, dvacc[i][4 * j], dvacc[i][4 * j + 1], dvacc[i][4 * j + 2],
-                              dvacc[i][4 * j + 3]);
+                    store4<GT>(dk + 32 * i + 8 * j, dkacc[i][4 * j] * sc, dkacc[i][4 * j + 1] * sc,
+                               dkacc[i][4 * j + 2] * sc, dkacc[i][4 * j + 3] * sc);
+                    store4<GT>(dv + 32 * i + 8 * j, dvacc[i][4 * j], dvacc[i][4 * j + 1], dvacc[i][4 * j + 2],
+                               dvacc[i][4 * j + 3]);
                 }
         }
     }
@@ -525,13 +527,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 #endif
 }
 
-template <int D, int ACT>
-hipError_t launch_d(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hipEvent_t before, hipEvent_t after) {
+template <int D, int ACT, typename GT>
+hipError_t launch_g(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hipEvent_t before, hipEvent_t mid,
+                    hipEvent_t after) {
     if (before && hipEventRecord(before, s) != hipSuccess) return hipErrorUnknown;
-    hipLaunchKernelGGL((ja_bwd_dq_kernel<bf16, D, ACT>), dim3(grid_q), dim3(kBwdThreads), 0, s, a);
+    hipLaunchKernelGGL((ja_bwd_dq_kernel<bf16, D, ACT, GT>), dim3(grid_q), dim3(kBwdThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ja_bwd_dkdv_kernel<bf16, D, ACT>), dim3(grid_k), dim3(kBwdThreads), 0, s, a);
+    if (mid && hipEventRecord(mid, s) != hipSuccess) return hipErrorUnknown;
+    hipLaunchKernelGGL((ja_bwd_dkdv_kernel<bf16, D, ACT, GT>), dim3(grid_k), dim3(kBwdThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (after && hipEventRecord(after, s) != hipSuccess) return hipErrorUnknown;
@@ -539,12 +543,24 @@ hipError_t launch_d(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hip
 }
 
 template <int D, int ACT>
-int occupancy_d(bool dkdv) {
+hipError_t launch_d(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hipEvent_t before, hipEvent_t mid,
+                    hipEvent_t after) {
+    return a.grad_f32 ? launch_g<D, ACT, float>(a, grid_q, grid_k, s, before, mid, after)
+                      : launch_g<D, ACT, bf16>(a, grid_q, grid_k, s, before, mid, after);
+}
+
+template <int D, int ACT, typename GT>
+int occupancy_g(bool dkdv) {
     int n = 0;
-    const void* fn = dkdv ? reinterpret_cast<const void*>(&ja_bwd_dkdv_kernel<bf16, D, ACT>)
-                          : reinterpret_cast<const void*>(&ja_bwd_dq_kernel<bf16, D, ACT>);
+    const void* fn = dkdv ? reinterpret_cast<const void*>(&ja_bwd_dkdv_kernel<bf16, D, ACT, GT>)
+                          : reinterpret_cast<const void*>(&ja_bwd_dq_kernel<bf16, D, ACT, GT>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBwdThreads, 0) != hipSuccess) n = 1;
     return n > 0 ? n : 1;
+}
+
+template <int D, int ACT>
+int occupancy_d(bool dkdv, bool grad_f32) {
+    return grad_f32 ? occupancy_g<D, ACT, float>(dkdv) : occupancy_g<D, ACT, bf16>(dkdv);
 }
 
 }  // namespace
@@ -558,42 +574,42 @@ int bwd_cols_per_stage() { return kBwdStage; }
 
 template <int ACT>
 hipError_t launch_a(const BwdArgs& a, int d, int grid_q, int grid_k, hipStream_t stream, hipEvent_t before,
-                    hipEvent_t after) {
+                    hipEvent_t mid, hipEvent_t after) {
     switch (d) {
-        case 32: return launch_d<32, ACT>(a, grid_q, grid_k, stream, before, after);
-        case 64: return launch_d<64, ACT>(a, grid_q, grid_k, stream, before, after);
-        case 128: return launch_d<128, ACT>(a, grid_q, grid_k, stream, before, after);
+        case 32: return launch_d<32, ACT>(a, grid_q, grid_k, stream, before, mid, after);
+        case 64: return launch_d<64, ACT>(a, grid_q, grid_k, stream, before, mid, after);
+        case 128: return launch_d<128, ACT>(a, grid_q, grid_k, stream, before, mid, after);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int ACT>
-int occupancy_a(int d, bool dkdv) {
+int occupancy_a(int d, bool dkdv, bool grad_f32) {
     switch (d) {
-        case 32: return occupancy_d<32, ACT>(dkdv);
-        case 64: return occupancy_d<64, ACT>(dkdv);
-        case 128: return occupancy_d<128, ACT>(dkdv);
+        case 32: return occupancy_d<32, ACT>(dkdv, grad_f32);
+        case 64: return occupancy_d<64, ACT>(dkdv, grad_f32);
+        case 128: return occupancy_d<128, ACT>(dkdv, grad_f32);
         default: return 1;
     }
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, hipStream_t stream,
-                      hipEvent_t before, hipEvent_t after) {
+                      hipEvent_t before, hipEvent_t mid, hipEvent_t after) {
     switch (act) {
-        case ACT_SOFTMAX: return launch_a<ACT_SOFTMAX>(a, d, grid_q, grid_k, stream, before, after);
-        case ACT_SILU: return launch_a<ACT_SILU>(a, d, grid_q, grid_k, stream, before, after);
-        case ACT_GELU: return launch_a<ACT_GELU>(a, d, grid_q, grid_k, stream, before, after);
-        case ACT_GELU_TAYLOR: return launch_a<ACT_GELU_TAYLOR>(a, d, grid_q, grid_k, stream, before, after);
+        case ACT_SOFTMAX: return launch_a<ACT_SOFTMAX>(a, d, grid_q, grid_k, stream, before, mid, after);
+        case ACT_SILU: return launch_a<ACT_SILU>(a, d, grid_q, grid_k, stream, before, mid, after);
+        case ACT_GELU: return launch_a<ACT_GELU>(a, d, grid_q, grid_k, stream, before, mid, after);
+        case ACT_GELU_TAYLOR: return launch_a<ACT_GELU_TAYLOR>(a, d, grid_q, grid_k, stream, before, mid, after);
         default: return hipErrorInvalidValue;
     }
 }
 
-int bwd_blocks_per_cu(int d, int act, bool dkdv) {
+int bwd_blocks_per_cu(int d, int act, bool dkdv, bool grad_f32) {
     switch (act) {
-        case ACT_SOFTMAX: return occupancy_a<ACT_SOFTMAX>(d, dkdv);
-        case ACT_SILU: return occupancy_a<ACT_SILU>(d, dkdv);
-        case ACT_GELU: return occupancy_a<ACT_GELU>(d, dkdv);
-        case ACT_GELU_TAYLOR: return occupancy_a<ACT_GELU_TAYLOR>(d, dkdv);
+        case ACT_SOFTMAX: return occupancy_a<ACT_SOFTMAX>(d, dkdv, grad_f32);
+        case ACT_SILU: return occupancy_a<ACT_SILU>(d, dkdv, grad_f32);
+        case ACT_GELU: return occupancy_a<ACT_GELU>(d, dkdv, grad_f32);
+        case ACT_GELU_TAYLOR: return occupancy_a<ACT_GELU_TAYLOR>(d, dkdv, grad_f32);
         default: return 1;
     }
 }

@@ -86,12 +86,23 @@ struct BwdArgs {
     int32_t causal, window;
     int32_t bsh;               // block shift of the block-diagonal mask (kNoBlock: none)
     float scale;
+    int32_t grad_f32;          // dq, dk, dv are fp32 (else the input type)
 };
 bool bwd_supported(int dtype, int d, int act);
 int bwd_rows_per_item();   // query rows (dQ pass) and key rows (dK/dV pass) per work item
 int bwd_cols_per_stage();  // keys (dQ pass) and queries (dK/dV pass) per stage: scheduler cost unit
+// Events (may be null) recorded before the dQ pass, between the passes and after
+// the dK/dV pass.
 hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, hipStream_t stream,
-                      hipEvent_t before, hipEvent_t after);
-int bwd_blocks_per_cu(int d, int act, bool dkdv);  // workgroups per CU of the dQ (false) or dK/dV pass
+                      hipEvent_t before, hipEvent_t mid, hipEvent_t after);
+// Workgroups per CU of the dQ (false) or dK/dV pass.
+int bwd_blocks_per_cu(int d, int act, bool dkdv, bool grad_f32);
+
+// Machine probe: one workgroup per compute unit streaming 32x32x16 bf16 products;
+// writes (shader cycles, real-time ticks) of each workgroup's loop to out[2 g],
+// out[2 g + 1]; sink receives probe_threads() floats per workgroup.
+int probe_threads();
+int probe_flop_per_iter();  // matrix flop one workgroup performs per iteration
+hipError_t launch_probe_mfma(int iters, int grid, uint64_t* out, float* sink, hipStream_t stream);
 
 }  // namespace ja

@@ -13,11 +13,12 @@ sequences; the full block workload on sampled (sequence, head) pairs; the
 dedicated backward ignoring out and lse; a block at least as long as every
 sequence, which must give bit for bit the result of the unmasked entry points;
 and argument errors.
-bf16 results are held to the non-strict bound (absolute 2e-2 plus 2^-8 relative,
-and the mean bound): under a causal block mask the first query of every block
-sees only its own key (P = 1), so dV of that key carries a whole dO row, and with
-one- or two-token blocks so do the outputs; values reach ~7, where the bf16
-rounding of the result alone is up to 2^-6 / 2 = 0.0156.
+bf16 results are held to the strict bound (|err| <= 2e-2 per element, mean <= 2e-3)
+except on rounding-limited elements (tests/_parity.py), which are held to their own
+bf16 rounding bound: blocks give every query few visible keys, so weights are of
+order one (under a causal block mask the first query of each block sees only its
+own key, P = 1, and dV of that key carries a whole dO row); such values reach ~7,
+where the bf16 rounding of the result alone is up to 2^-6 / 2 = 0.0156.
 """
 import numpy as np
 import pytest
@@ -26,7 +27,7 @@ import torch
 import jagged_attention_recsys_amd as ja
 import oracle
 from jagged_attention_recsys_amd import workloads as W
-from _parity import compare, rows_of_pairs, say, to_dev, to_host64
+from _parity import compare, rows_of_pairs, say, term_sums, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +65,7 @@ def run_block(w, block, causal, bwd=True):
     return out, lse, (dq, dk, dv)
 
 
-def check(w, block, causal, bwd=True, pair_mask=None, what="", strict=False):
+def check(w, block, causal, bwd=True, pair_mask=None, what="", report=False):
     say(f"[block] {what} B={w.B} H={w.H} d={w.d} T={w.q.shape[0]} block={block} causal={causal} "
         f"dtype={w.dtype} bwd={bwd}")
     out, lse, grads = run_block(w, block, causal, bwd)
@@ -76,15 +77,22 @@ def check(w, block, causal, bwd=True, pair_mask=None, what="", strict=False):
     else:
         ro, rl = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, "softmax", causal, 0, w.scale,
                             pair_mask=pair_mask, block=block)
-    stats["out"] = compare(to_host64(out), ro, w.dtype, f"out {what}", sel, strict=strict)
+    # term sums for the rounding-limited elements (module docstring)
+    t_out = tq = tk = tv = None
+    if w.dtype == "bf16":
+        if bwd:
+            t_out, tq, tk, tv = term_sums(w, "softmax", causal, 0, block=block, pair_mask=pair_mask, grads=True)
+        else:
+            t_out = term_sums(w, "softmax", causal, 0, block=block, pair_mask=pair_mask)
+    stats["out"] = compare(to_host64(out), ro, w.dtype, f"{what} out", sel, terms=t_out, report=report)
     gl = to_host64(lse)[sel]
     assert np.all(np.isfinite(gl)), "every row sees at least its own key"
     lse_err = float(np.max(np.abs(gl - rl[sel]))) if gl.size else 0.0
     lse_tol = (1e-5 if w.dtype == "f32" else 1e-3) * max(1.0, float(np.max(np.abs(rl[sel]))) if gl.size else 1.0)
     assert lse_err <= lse_tol, f"lse {what}: {lse_err} > {lse_tol}"
     if bwd:
-        for name, got, ref in (("dq", grads[0], rq), ("dk", grads[1], rk), ("dv", grads[2], rv)):
-            stats[name] = compare(to_host64(got), ref, w.dtype, f"{name} {what}", sel, strict=strict)
+        for name, got, ref, terms in (("dq", grads[0], rq, tq), ("dk", grads[1], rk, tk), ("dv", grads[2], rv, tv)):
+            stats[name] = compare(to_host64(got), ref, w.dtype, f"{what} {name}", sel, terms=terms, report=report)
     say(f"      ok lse_err={lse_err:.2e} {stats}")
 
 
@@ -131,7 +139,7 @@ def _sample_pairs(w, n, seed):
 
 def test_workload6_fwd_bwd_sampled():
     w = W.workload(6)
-    check(w, w.block, w.causal, pair_mask=_sample_pairs(w, 8, 6), what="w6")
+    check(w, w.block, w.causal, pair_mask=_sample_pairs(w, 8, 6), what="w6", report=True)
 
 
 @pytest.mark.parametrize("causal", [True, False])

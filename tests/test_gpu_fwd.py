@@ -4,7 +4,8 @@ Every case calls the HIP library through its C ABI (Python binding) and compares
 element by element with the oracle on the same seeded inputs:
   * small ragged batches spanning several tiles and ragged tails, every mask and
     activation, d in {32, 64, 128}, bf16 and fp32, both kernel layouts;
-  * the five named workloads at full size, on sampled (sequence, head) pairs;
+  * the five named workloads at full size, every (sequence, head) pair, held to
+    the strict bf16 bound (fp32 for the first);
   * closed forms (zero queries under SiLU/GELU give exactly 0; identical keys give
     the mean of the visible values), bitwise invariance to sequence order,
     bitwise run-to-run determinism, untouched guard bands around the outputs;
@@ -19,7 +20,7 @@ import torch
 import jagged_attention_recsys_amd as ja
 import oracle
 from jagged_attention_recsys_amd import workloads as W
-from _parity import compare, rows_of_pairs, sample_pairs, say, to_dev, to_host64
+from _parity import compare, rows_of_pairs, say, term_sums, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +46,10 @@ def run_fwd(w, act=None, causal=None, window=None, guard=True):
     return out, lse
 
 
-def check_against_oracle(w, act, causal, window, pair_mask=None, what="", strict=False):
+def check_against_oracle(w, act, causal, window, pair_mask=None, what="", bounds=False, report=False):
+    """Strict bf16 / fp32 bound on every compared element. bounds: the edge-case batches
+    (rows with few visible keys) pass their term sums, so that elements whose own bf16
+    rounding bound exceeds half the tolerance are held to that bound instead."""
     say(f"[fwd] {what} B={w.B} H={w.H} d={w.d} Tq={w.q.shape[0]} Tk={w.k.shape[0]} {w.dtype} act={act} "
         f"causal={causal} window={window}")
     out, lse = run_fwd(w, act, causal, window)
@@ -53,7 +57,8 @@ def check_against_oracle(w, act, causal, window, pair_mask=None, what="", strict
                                   pair_mask=pair_mask)
     sel = rows_of_pairs(w.q_offsets, w.H, pair_mask)
     got = to_host64(out)
-    stats = compare(got, ref_out, w.dtype, f"out {what}", sel, strict=strict)
+    terms = term_sums(w, act, causal, window, pair_mask=pair_mask) if bounds and w.dtype == "bf16" else None
+    stats = compare(got, ref_out, w.dtype, f"out {what}", sel, terms=terms, report=report)
     if act == "softmax":
         gl = to_host64(lse)
         fin = np.isfinite(ref_lse) & sel
@@ -73,7 +78,7 @@ MASKS = [("softmax", False, 0), ("softmax", True, 0), ("softmax", True, 37), ("s
 @pytest.mark.parametrize("act,causal,window", MASKS)
 def test_ragged_self_attention_bf16(d, act, causal, window):
     w = W.make_case(RAGGED, H=2, d=d, dtype=W.BF16, seed=d + window)
-    check_against_oracle(w, act, causal, window, what="ragged-self")
+    check_against_oracle(w, act, causal, window, what="ragged-self", bounds=True)
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
@@ -83,7 +88,7 @@ def test_ragged_cross_attention_bf16(d, act, causal, window):
     lq = [200, 1, 0, 77, 130, 129]
     lk = [64, 300, 5, 0, 1, 257]
     w = W.make_case(lq, lk, H=3, d=d, dtype=W.BF16, seed=7 * d + window)
-    check_against_oracle(w, act, causal, window, what="ragged-cross")
+    check_against_oracle(w, act, causal, window, what="ragged-cross", bounds=True)
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
@@ -106,7 +111,7 @@ def test_short_queries_split_layout(d, act, causal, window):
     w = W.make_case(lq, lk, H=2, d=d, dtype=W.BF16, seed=d + 1)
     bm, bn = ja.fwd_tile_shape(w.B, d, w.q.shape[0], w.k.shape[0], act)
     assert bm == 32, "short-query batch should take the split layout"
-    check_against_oracle(w, act, causal, window, what="split")
+    check_against_oracle(w, act, causal, window, what="split", bounds=True)
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
@@ -122,21 +127,21 @@ def test_short_keys_chunked_layout(d, act, causal, window):
     w = W.make_case(lq, lk, H=2, d=d, dtype=W.BF16, seed=5 * d + window)
     bm, bn = ja.fwd_tile_shape(w.B, d, w.q.shape[0], w.k.shape[0], act)
     assert (bm, bn) == (512, 64), "short-key batch should take the chunked layout"
-    check_against_oracle(w, act, causal, window, what="chunked")
+    check_against_oracle(w, act, causal, window, what="chunked", bounds=True)
 
 
 def test_workload1_fp32_softmax_and_silu():
     w = W.workload(1)
-    check_against_oracle(w, "softmax", False, 0, what="w1", strict=True)
-    check_against_oracle(w, "silu", False, 0, what="w1-silu", strict=True)
+    check_against_oracle(w, "softmax", False, 0, what="w1 fwd", report=True)
+    check_against_oracle(w, "silu", False, 0, what="w1 fwd silu", report=True)
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
-def test_full_workloads_sampled(n):
+def test_full_workloads_every_pair(n):
+    # The whole batch, every (sequence, head) pair, element by element, strict.
     say(f"[fwd] generating workload {n}")
     w = W.workload(n)
-    mask = sample_pairs(w, 6, seed=n)
-    check_against_oracle(w, w.act, w.causal, w.window, pair_mask=mask, what=f"w{n}", strict=True)
+    check_against_oracle(w, w.act, w.causal, w.window, what=f"w{n} fwd", report=True)
 
 
 @pytest.mark.parametrize("act", ["silu", "gelu"])

@@ -35,7 +35,7 @@ def qk_case(lq, lk=None, H=2, d=64, dtype=W.BF16, seed=0):
 def test_ragged_fwd(d, causal, window):
     for dtype in (W.F32, W.BF16):
         w = qk_case(RAGGED, d=d, dtype=dtype, seed=1100 + d + window)
-        check_against_oracle(w, "gelu_taylor", causal, window, what="ragged", strict=dtype == W.BF16)
+        check_against_oracle(w, "gelu_taylor", causal, window, what="ragged", bounds=True)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -43,14 +43,15 @@ def test_cross_fwd_bwd(d):
     lq = [200, 1, 0, 77, 130, 129, 5]
     lk = [64, 300, 5, 0, 1, 257, 140]
     w = qk_case(lq, lk, H=3, d=d, seed=1200 + d)
-    check_against_oracle(w, "gelu_taylor", False, 0, what="cross", strict=True)
-    check_bwd(w, False, 0, what="cross", act="gelu_taylor")
+    check_against_oracle(w, "gelu_taylor", False, 0, what="cross", bounds=True)
+    check_bwd(w, False, 0, what="cross", act="gelu_taylor", bounds=True)
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal,window", [(True, 0), (False, 50)])
 def test_ragged_bwd(d, causal, window):
-    check_bwd(qk_case(RAGGED, d=d, seed=1300 + d + window), causal, window, what="ragged", act="gelu_taylor")
+    check_bwd(qk_case(RAGGED, d=d, seed=1300 + d + window), causal, window, what="ragged", act="gelu_taylor",
+              bounds=True)
 
 
 def _extreme_scores(d, seed):
@@ -66,8 +67,8 @@ def _extreme_scores(d, seed):
 @pytest.mark.parametrize("d", [64, 128])
 def test_scores_at_the_ends_of_the_range(d):
     w = _extreme_scores(d, 1400 + d)
-    check_against_oracle(w, "gelu_taylor", True, 0, what="extreme", strict=True)
-    check_bwd(w, True, 0, what="extreme", act="gelu_taylor")
+    check_against_oracle(w, "gelu_taylor", True, 0, what="extreme", bounds=True)
+    check_bwd(w, True, 0, what="extreme", act="gelu_taylor", bounds=True)
 
 
 def test_close_to_tanh_gelu_on_the_qknorm_range():
@@ -104,5 +105,5 @@ def _sample(w, n, seed):
 def test_workload7_fwd_bwd_sampled():
     w = W.workload(7)
     mask = _sample(w, 6, 7)
-    check_against_oracle(w, w.act, w.causal, w.window, pair_mask=mask, what="w7", strict=True)
-    check_bwd(w, w.causal, w.window, pair_mask=mask, what="w7", strict=True, act=w.act)
+    check_against_oracle(w, w.act, w.causal, w.window, pair_mask=mask, what="w7 fwd", report=True)
+    check_bwd(w, w.causal, w.window, pair_mask=mask, what="w7 bwd", act=w.act, report=True)

@@ -13,6 +13,15 @@ bound is
 (P, l the unrounded softmax weights and their sum in fp64 on the dequantized
 tensors; 2^-8 |ref| + 2e-3 for the bf16 output and fp32 accumulation), checked
 element by element; lse (unaffected by the weight rounding) to 1e-3 relative.
+
+Where the kernel's running max is the final row max from the start (rows whose
+visible keys all lie in one 128-key stage: every row of a sequence of at most 128
+keys, the first 128 rows of a causal sequence, window rows that do not straddle a
+stage boundary), both sides round the same weights, and the tight bound applies:
+    |out - ref| <= 2^-8 |ref| + 2e-3 + sum_{j ambiguous} step_j |V_j| / l_i
+where a weight is ambiguous when 2^8 P_ij lies within 2^-12 of itself of an E4M3
+rounding midpoint (fp32 scores in the kernel, fp64 in the oracle: either code is
+a correct rounding there) and step_j is the E4M3 spacing at it, times 2^-8.
 Cases: ragged lengths that are not multiples of 32 or 64, empty sequences,
 causal, windowed, Lq != Lk, the MXFP8 workload on sampled (sequence, head)
 pairs, and argument errors.
@@ -64,16 +73,43 @@ def _quantized(w):
     return q, k, v
 
 
+def _scale_rows(sc, T, B):
+    """The oracle's scales ([NB, H, d/32], NB = the blocks used) padded with zero rows
+    to ceil(T/32) + B, the size the binding requires (what the quantizer allocates)."""
+    n = max((T + 31) // 32 + B, 1)
+    out = np.zeros((n,) + sc.shape[1:], dtype=np.uint8)
+    out[:sc.shape[0]] = sc
+    return out
+
+
 def run_mx(w, q, k, v, causal, window):
     dev = lambda t: torch.from_numpy(np.ascontiguousarray(t)).cuda()
-    out, lse = ja.jagged_attn_fwd_mxfp8(dev(q[0]), dev(q[1]), dev(q[2]), dev(k[0]), dev(k[1]), dev(k[2]),
-                                        dev(v[0]), dev(v[1]), to_dev(w.q_offsets), to_dev(w.k_offsets),
+    Tq, Tk, B = w.q.shape[0], w.k.shape[0], w.B
+    qs, ks, vs = _scale_rows(q[1], Tq, B), _scale_rows(k[1], Tk, B), _scale_rows(v[1], Tk, B)
+    out, lse = ja.jagged_attn_fwd_mxfp8(dev(q[0]), dev(qs), dev(q[2]), dev(k[0]), dev(ks), dev(k[2]),
+                                        dev(v[0]), dev(vs), to_dev(w.q_offsets), to_dev(w.k_offsets),
                                         causal=causal, window=window, scale=w.scale)
     torch.cuda.synchronize()
     return to_host64(out), to_host64(lse)
 
 
-def check(w, causal, window, pair_mask=None, what=""):
+def _e4m3_grid():
+    """Sorted non-negative finite E4M3 values (codes 0x00..0x7E)."""
+    return np.sort(oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+
+
+def _ambiguous_steps(x, grid):
+    """For values x >= 0 (fp64) to be rounded to E4M3: the E4M3 spacing where x lies
+    within 2^-12 x of a rounding midpoint, else 0."""
+    i = np.clip(np.searchsorted(grid, x, side="right") - 1, 0, grid.size - 2)
+    lo, hi = grid[i], grid[i + 1]
+    mid = 0.5 * (lo + hi)
+    return np.where(np.abs(x - mid) <= 2.0 ** -12 * x, hi - lo, 0.0)
+
+
+def check(w, causal, window, pair_mask=None, what="", tight=False):
+    """tight: rows whose visible keys lie in one 128-key stage are held to the tight
+    bound (module docstring), every other row to the derived general bound."""
     say(f"[mx fwd] {what} B={w.B} H={w.H} Tq={w.q.shape[0]} Tk={w.k.shape[0]} causal={causal} window={window}")
     q, k, v = _quantized(w)
     out, lse = run_mx(w, q, k, v, causal, window)
@@ -82,7 +118,8 @@ def check(w, causal, window, pair_mask=None, what=""):
     qd = _dequant(*q, w.q_offsets)
     kd = _dequant(*k, w.k_offsets)
     vd = _dequant(*v, w.k_offsets)
-    worst, n, esum = 0.0, 0, 0.0
+    worst, n, esum, n_amb, n_tight = 0.0, 0, 0.0, 0, 0
+    grid = _e4m3_grid()
     for b in range(w.B):
         q0, q1 = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
         k0, k1 = int(w.k_offsets[b]), int(w.k_offsets[b + 1])
@@ -108,9 +145,19 @@ def check(w, causal, window, pair_mask=None, what=""):
             l = p.sum(axis=1, keepdims=True)
             lsafe = np.where(l > 0, l, 1)
             av = np.abs(vd[k0:k1, h])
-            bound = (2.0 ** -3 * p @ av + 2.0 ** -17 * vis @ av) / lsafe
             r, g = ref[q0:q1, h], out[q0:q1, h]
+            bound = (2.0 ** -3 * p @ av + 2.0 ** -17 * vis @ av) / lsafe
             tol = bound + 2.0 ** -8 * np.abs(r) + 2e-3
+            if tight:
+                # rows whose first and last visible key share a 128-key stage
+                first = np.argmax(vis, axis=1)
+                last = vis.shape[1] - 1 - np.argmax(vis[:, ::-1], axis=1)
+                one = vis.any(axis=1) & (first // 128 == last // 128)
+                steps = _ambiguous_steps(256.0 * p, grid) * vis
+                n_amb += int(np.count_nonzero(steps[one]))
+                n_tight += int(one.sum())
+                tight_tol = 2.0 ** -8 * np.abs(r) + 2e-3 + (steps / 256.0) @ av / lsafe
+                tol = np.where(one[:, None], tight_tol, tol)
             err = np.abs(g - r)
             assert np.all(np.isfinite(g)), what
             assert np.all(err <= tol), f"{what} b={b} h={h}: max excess {np.max(err - tol):.3e}"
@@ -120,7 +167,10 @@ def check(w, causal, window, pair_mask=None, what=""):
             rows = vis.any(axis=1)
             gl, rl = lse[q0:q1, h][rows], rlse[q0:q1, h][rows]
             assert np.all(np.abs(gl - rl) <= 1e-3 * np.maximum(1.0, np.abs(rl))), f"{what} lse"
-    say(f"      ok max_abs={worst:.3e} mean_abs={esum / max(n, 1):.3e}")
+    say(f"      ok max_abs={worst:.3e} mean_abs={esum / max(n, 1):.3e} tight rows={n_tight} "
+        f"ambiguous weights={n_amb}")
+    if tight:
+        assert n_tight > 0
 
 
 RAGGED = [1, 7, 64, 65, 127, 128, 129, 300, 0, 263]
@@ -149,6 +199,26 @@ def test_workload8_sampled():
     while mask.sum() < 6:
         mask[int(rng.integers(w.B)), int(rng.integers(w.H))] = True
     check(w, w.causal, w.window, pair_mask=mask, what="w8")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_stage_keys_tight_bound(causal):
+    # Every sequence's keys fit one 128-key stage, so the running max is the row max
+    # from the start and both sides round the same weights.
+    lq = [300, 1, 77, 513, 200, 129, 64]
+    lk = [128, 1, 64, 100, 33, 127, 0]
+    w = W.make_case(lq, lk, H=2, d=128, dtype=W.BF16, seed=2600 + causal)
+    check(w, causal, 0, what="one-stage", tight=True)
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 50), (False, 60)])
+def test_single_stage_rows_tight_bound(causal, window):
+    # Sequences of several 128-key stages: the rows whose visible keys all lie in one
+    # stage (the first 128 causal rows; window rows that do not straddle a stage
+    # boundary) are held to the tight bound.
+    lengths = [700, 129, 1, 300, 257, 0, 450]
+    w = W.make_case(lengths, H=2, d=128, dtype=W.BF16, seed=2700 + causal + window)
+    check(w, causal, window, what="single-stage rows", tight=True)
 
 
 def test_rejects_unsupported_head_dim():

@@ -80,6 +80,31 @@ def test_fwd_rejects_host_visible_errors(lib):
     assert fwd(lib, Tq=0) == OK
 
 
+def bwd(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, qo=FAKE, ko=FAKE, B=2, H=2, d=64, Tq=100,
+                Tk=100, act=0, causal=0, window=0, scale=0.125, dtype=1, gdtype=1, dq=FAKE, dk=FAKE, dv=FAKE,
+                ws=FAKE, ws_bytes=0, stream=None)
+    args.update(kw)
+    a = args
+    return lib.jagged_attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["qo"], a["ko"], a["B"],
+                               a["H"], a["d"], a["Tq"], a["Tk"], a["act"], a["causal"], a["window"], a["scale"],
+                               a["dtype"], a["gdtype"], a["dq"], a["dk"], a["dv"], a["ws"], a["ws_bytes"],
+                               a["stream"])
+
+
+def test_bwd_rejects_host_visible_errors(lib):
+    assert bwd(lib, dtype=0, gdtype=0) == UNSUPPORTED     # fp32 inputs have no backward
+    assert bwd(lib, gdtype=7) == UNSUPPORTED              # gradients: the input dtype or fp32
+    assert bwd(lib, gdtype=5) == UNSUPPORTED
+    assert bwd(lib, lse=None) == INVALID                  # softmax needs the forward's lse
+    assert bwd(lib, out=None) == INVALID
+    assert bwd(lib, act=1, out=None, lse=None, ws_bytes=16) == WORKSPACE  # pointwise needs neither
+    assert bwd(lib, dq=FAKE + 8) == INVALID               # misaligned
+    assert bwd(lib, ws_bytes=16) == WORKSPACE
+    assert bwd(lib, gdtype=0, ws_bytes=16) == WORKSPACE   # fp32 gradients accepted
+    assert bwd(lib, B=0) == OK
+
+
 def test_workspace_size_grows_with_tiles(lib):
     small = lib.ja_fwd_workspace_size(4, 2, 128, 1000, 1000, 0, 1, 0, 1)
     big = lib.ja_fwd_workspace_size(4, 2, 128, 100000, 1000, 0, 1, 0, 1)
