@@ -182,11 +182,26 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
                     floatx16 sacc = floatx16{}, dpacc = floatx16{};
                     const char* kblk = kl + nb * 32 * C::ROWB;
                     const char* vblk = vl + nb * 32 * C::ROWB;
+                    // K and V rows read two k-steps ahead of their products (the
+                    // scheduling barriers keep each read from sinking next to its
+                    // product, which would expose the LDS latency per product).
+                    frag kr[2], vr[2];
+#pragma unroll
+                    for (int s = 0; s < 2 && s < C::NS; ++s) {
+                        kr[s] = C::STile::read_rows(kblk, koff[s]);
+                        vr[s] = C::STile::read_rows(vblk, koff[s]);
+                    }
 #pragma unroll
                     for (int s = 0; s < C::NS; ++s) {
-                        sacc = M::run(C::STile::read_rows(kblk, koff[s]), qf[s], sacc);
-                        dpacc = M::run(C::STile::read_rows(vblk, koff[s]), dof[s], dpacc);
+                        __builtin_amdgcn_sched_barrier(0);
+                        sacc = M::run(kr[s & 1], qf[s], sacc);
+                        dpacc = M::run(vr[s & 1], dof[s], dpacc);
+                        if (s + 2 < C::NS) {
+                            kr[s & 1] = C::STile::read_rows(kblk, koff[s + 2]);
+                            vr[s & 1] = C::STile::read_rows(vblk, koff[s + 2]);
+                        }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float g;
@@ -208,15 +223,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
                     for (int t = 0; t < C::NT; ++t) dsf[nb][t] = to_frag<T>(sacc, KP * t);
                 }
+                // dQ^T += K^T dS^T: K^T fragments read three products ahead.
+                constexpr int NQ = C::NB * C::NT * C::ND;
+                auto ktr = [&](int i) __attribute__((always_inline)) {
+                    return C::STile::read_tr(kl + (i / (C::NT * C::ND)) * 32 * C::ROWB, (i / C::ND) % C::NT, toff,
+                                             i % C::ND);
+                };
+                frag ring[3];
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb) {
-                    const char* kblk = kl + nb * 32 * C::ROWB;
+                for (int i = 0; i < 3 && i < NQ; ++i) ring[i] = ktr(i);
 #pragma unroll
-                    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-                        for (int db = 0; db < C::ND; ++db)
-                            dqacc[db] = M::run(C::STile::read_tr(kblk, t, toff, db), dsf[nb][t], dqacc[db]);
+                for (int i = 0; i < NQ; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int db = i % C::ND;
+                    dqacc[db] = M::run(ring[i % 3], dsf[i / (C::NT * C::ND)][(i / C::ND) % C::NT], dqacc[db]);
+                    if (i + 3 < NQ) ring[i % 3] = ktr(i + 3);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
         };
@@ -390,12 +413,34 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
                 const bool need_mask = wave_needs_mask(vis, key_ok, qb0, 32);
                 const char* qblk = ql + nb * 32 * C::ROWB;
                 const char* oblk = ol + nb * 32 * C::ROWB;
+                // Operands are read from LDS ahead of the products that consume them
+                // (the scheduling barriers keep the compiler from sinking each read
+                // next to its product, which would expose the LDS latency per product):
+                // Q and dO rows for S and dP first, then the transposed dO and Q blocks
+                // for dV and dK while S, dP and the softmax terms are computed.
+                frag rq[C::NS], ro[C::NS];
+#pragma unroll
+                for (int s = 0; s < C::NS; ++s) {
+                    rq[s] = C::STile::read_rows(qblk, roff[s]);
+                    ro[s] = C::STile::read_rows(oblk, roff[s]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 floatx16 sacc = floatx16{}, dpacc = floatx16{};
 #pragma unroll
                 for (int s = 0; s < C::NS; ++s) {
-                    sacc = M::run(C::STile::read_rows(qblk, roff[s]), kf[s], sacc);
-                    dpacc = M::run(C::STile::read_rows(oblk, roff[s]), vf[s], dpacc);
+                    sacc = M::run(rq[s], kf[s], sacc);
+                    dpacc = M::run(ro[s], vf[s], dpacc);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                frag tv[C::NT][C::ND], tk[C::NT][C::ND];
+#pragma unroll
+                for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+                    for (int db = 0; db < C::ND; ++db) {
+                        tv[t][db] = C::STile::read_tr(oblk, t, toff, db);
+                        tk[t][db] = C::STile::read_tr(qblk, t, toff, db);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
                 // Register r holds query qb0 + key_of_reg(grp, r): for bf16 two runs
                 // of 8 consecutive queries, read as float4s from lse / Di.
                 float lse_r[16], di_r[16];
@@ -450,8 +495,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
                     const frag dsf = to_frag<T>(dsacc, KP * t);
 #pragma unroll
                     for (int db = 0; db < C::ND; ++db) {
-                        dvacc[db] = M::run(C::STile::read_tr(oblk, t, toff, db), pf, dvacc[db]);
-                        dkacc[db] = M::run(C::STile::read_tr(qblk, t, toff, db), dsf, dkacc[db]);
+                        dvacc[db] = M::run(tv[t][db], pf, dvacc[db]);
+                        dkacc[db] = M::run(tk[t][db], dsf, dkacc[db]);
                     }
                 }
             }
