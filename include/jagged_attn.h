@@ -66,7 +66,9 @@ typedef enum {
     JA_ERR_UNSUPPORTED = 2,     /* d not in {32, 64, 128}, unknown dtype/act, bwd of fp32 */
     JA_ERR_WORKSPACE = 3,       /* workspace smaller than the matching *_workspace_size() */
     JA_ERR_INVALID_OFFSETS = 4, /* ja_validate_offsets found malformed offsets */
-    JA_ERR_HIP = 5              /* a HIP runtime call or kernel launch failed */
+    JA_ERR_HIP = 5,             /* a HIP runtime call or kernel launch failed */
+    JA_ERR_SCRATCH = 6          /* jagged_attn_fwd_noalloc: the sizes need more workspace than its
+                                   fixed device buffer holds */
 } ja_status_t;
 
 typedef enum {
@@ -108,6 +110,30 @@ ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v,
                             int32_t act, int32_t causal, int32_t window, float scale,
                             int32_t dtype, void* out, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the fixed per-GPU device buffer jagged_attn_fwd_noalloc uses as its workspace. */
+#define JA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* jagged_attn_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, results and errors as jagged_attn_fwd, without the workspace: it uses
+ * a fixed file-scope device buffer of JA_NOALLOC_SCRATCH_BYTES (8 MiB) that every
+ * GPU the library runs on holds until the process ends; its address is looked up
+ * on the first call with each device current. Calls whose
+ * ja_fwd_workspace_size() exceeds that return JA_ERR_SCRATCH before anything is
+ * enqueued (8 MiB holds a work list of about a million (sequence, tile) pairs,
+ * ceil(Tq / BM) + B of them: some 130 million query tokens at BM = 128, see
+ * ja_fwd_tile_shape). No call allocates or
+ * frees anything. All calls on one GPU share the buffer, and each call's contents
+ * last until the next one: calls that overlap on one GPU (several streams or host
+ * threads) race and must be serialised by the caller. Nothing needs clearing
+ * between calls: each call's tile scheduler writes everything its attention
+ * kernel reads. */
+ja_status_t jagged_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                    const int32_t* q_offsets, const int32_t* k_offsets,
+                                    int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                                    int32_t act, int32_t causal, int32_t window, float scale,
+                                    int32_t dtype, void* out, float* lse, void* stream);
 
 /* Bytes of device workspace jagged_attn_bwd needs. Host only. */
 size_t ja_bwd_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,

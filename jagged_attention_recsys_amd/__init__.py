@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     fwd_workspace_size,
     jagged_attn_bwd,
     jagged_attn_fwd,
+    jagged_attn_fwd_noalloc,
     jagged_block_attn_bwd,
     jagged_block_attn_fwd,
     jagged_attn_fwd_mxfp8,
@@ -21,6 +22,7 @@ from .ops import (  # noqa: F401
 
 __all__ = [
     "jagged_attn_fwd",
+    "jagged_attn_fwd_noalloc",
     "jagged_attn_bwd",
     "jagged_block_attn_fwd",
     "jagged_block_attn_bwd",

@@ -18,6 +18,8 @@ SIGNATURES = {
     "ja_fwd_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32]),
     "jagged_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _f32,
                                _i32, _vp, _vp, _vp, _sz, _vp]),
+    "jagged_attn_fwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
+                                       _f32, _i32, _vp, _vp, _vp]),
     "ja_bwd_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32]),
     "jagged_attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i32, _i32,
                                _i32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),

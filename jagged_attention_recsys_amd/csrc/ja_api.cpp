@@ -174,18 +174,39 @@ int block_shift(int32_t block) {
     return sh;
 }
 
+}  // namespace
+
+namespace ja {
+
+// Every check of the forward's arguments that needs no device access, workspace
+// aside; JA_OK also for an empty batch (the caller then has nothing to do).
+ja_status_t fwd_check_args(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                           const int32_t* k_offsets, int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                           int32_t act, int32_t window, float scale, int32_t dtype, const void* out, const float* lse) {
+    ja_status_t st = check_common(B, H, d, Tq, Tk, act, window, scale, dtype);
+    if (st != JA_OK) return st;
+    if (B == 0 || Tq == 0) return JA_OK;  // no query rows: nothing to write
+    if (!q || !out || !q_offsets || !k_offsets) return JA_ERR_INVALID_ARG;
+    if (Tk > 0 && (!k || !v)) return JA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+        !aligned(q_offsets, 4) || !aligned(k_offsets, 4))
+        return JA_ERR_INVALID_ARG;
+    return JA_OK;
+}
+
+}  // namespace ja
+
+namespace {
+
 ja_status_t fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                      const int32_t* k_offsets, int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
                      int32_t act, int32_t causal, int32_t window, int32_t bsh, float scale, int32_t dtype, void* out,
                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-    ja_status_t st = check_common(B, H, d, Tq, Tk, act, window, scale, dtype);
+    ja_status_t st = fwd_check_args(q, k, v, q_offsets, k_offsets, B, H, d, Tq, Tk, act, window, scale, dtype, out,
+                                    lse);
     if (st != JA_OK) return st;
     if (B == 0 || Tq == 0) return JA_OK;  // no query rows: nothing to write
-    if (!q || !out || !q_offsets || !k_offsets || !workspace) return JA_ERR_INVALID_ARG;
-    if (Tk > 0 && (!k || !v)) return JA_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
-        !aligned(q_offsets, 4) || !aligned(k_offsets, 4) || !aligned(workspace, 16))
-        return JA_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 16)) return JA_ERR_INVALID_ARG;
     FwdPlan p;
     st = plan_fwd(B, H, d, Tq, Tk, act, dtype, &p);
     if (st != JA_OK) return st;
@@ -668,6 +689,7 @@ const char* ja_status_string(ja_status_t status) {
         case JA_ERR_WORKSPACE: return "workspace too small";
         case JA_ERR_INVALID_OFFSETS: return "malformed offsets";
         case JA_ERR_HIP: return "HIP runtime error";
+        case JA_ERR_SCRATCH: return "sizes need more workspace than the fixed no-alloc buffer holds";
     }
     return "unknown status";
 }

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "jagged_attn.h"
+
 namespace ja {
 
 // Scheduler cost bins: costs at or above kSchedBins-1 share the last bin.
@@ -97,6 +99,12 @@ hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, 
                       hipEvent_t before, hipEvent_t mid, hipEvent_t after);
 // Workgroups per CU of the dQ (false) or dK/dV pass.
 int bwd_blocks_per_cu(int d, int act, bool dkdv, bool grad_f32);
+
+// Argument checks of jagged_attn_fwd that need no device access (workspace aside);
+// JA_OK also for an empty batch.
+ja_status_t fwd_check_args(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                           const int32_t* k_offsets, int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk,
+                           int32_t act, int32_t window, float scale, int32_t dtype, const void* out, const float* lse);
 
 // Machine probe: one workgroup per compute unit streaming 32x32x16 bf16 products;
 // writes (shader cycles, real-time ticks) of each workgroup's loop to out[2 g],

@@ -120,6 +120,43 @@ def jagged_attn_fwd(q, k, v, q_offsets, k_offsets, act="softmax", causal=False, 
     return out, (lse if a == 0 else None)
 
 
+def jagged_attn_fwd_noalloc(q, k, v, q_offsets, k_offsets, out, lse=None, act="softmax", causal=False, window=0,
+                            scale=None, stream=None):
+    """jagged_attn_fwd without a workspace: the library uses its fixed per-GPU device
+    buffer (JA_NOALLOC_SCRATCH_BYTES), so neither this call nor the C entry point
+    allocates anything. The caller passes the outputs: out [Tq,H,d] and, for softmax,
+    lse [Tq,H] float32 (or None). Calls that overlap on one GPU share the buffer and
+    race. Returns (out, lse)."""
+    lib = _lib.load()
+    if not isinstance(q, torch.Tensor) or q.dtype not in DTYPE:
+        raise ValueError(f"q must be a float32 or bfloat16 tensor")
+    _check("q", q, dim=3)
+    dtype, dev = q.dtype, q.device
+    Tq, H, d = q.shape
+    if not isinstance(k, torch.Tensor) or k.dim() != 3:
+        raise ValueError("k must be a [Tk, H, d] tensor")
+    Tk = k.shape[0]
+    _check("k", k, dtype, shape=(Tk, H, d), device=dev)
+    _check("v", v, dtype, shape=(Tk, H, d), device=dev)
+    if not isinstance(q_offsets, torch.Tensor) or q_offsets.dim() != 1 or q_offsets.numel() < 1:
+        raise ValueError("q_offsets must be an int32 [B+1] tensor")
+    B = q_offsets.numel() - 1
+    _check_offsets("q_offsets", q_offsets, B + 1, dev)
+    _check_offsets("k_offsets", k_offsets, B + 1, dev)
+    _check("out", out, dtype, shape=(Tq, H, d), device=dev)
+    a = _act(act)
+    if lse is not None:
+        _check("lse", lse, torch.float32, shape=(Tq, H), device=dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _on_gpu("q", q)
+    status = lib.jagged_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(k_offsets), B, H, d, Tq,
+                                         Tk, a, int(bool(causal)), int(window), float(scale), DTYPE[dtype],
+                                         _ptr(out), _ptr(lse) if a == 0 else None, _stream(q.device, stream))
+    _lib.check("jagged_attn_fwd_noalloc", status)
+    return out, (lse if a == 0 else None)
+
+
 def bwd_workspace_size(B, H, d, Tq, Tk, act="softmax", causal=False, window=0, dtype=torch.bfloat16) -> int:
     return int(_lib.load().ja_bwd_workspace_size(B, H, d, Tq, Tk, _act(act), int(bool(causal)), int(window),
                                                  DTYPE[dtype]))

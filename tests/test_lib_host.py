@@ -105,6 +105,21 @@ def test_bwd_rejects_host_visible_errors(lib):
     assert bwd(lib, B=0) == OK
 
 
+def test_noalloc_rejects_sizes_beyond_its_buffer(lib):
+    # the fixed 8 MiB buffer holds about a million (sequence, tile) pairs; the check is
+    # made on the host before the device is touched
+    f = lib.jagged_attn_fwd_noalloc
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE]
+    big = f(*args, 2, 2, 64, 200_000_000, 200_000_000, 0, 0, 0, 0.125, 1, FAKE, None, None)
+    assert big == 6 and "no-alloc" in _lib.status_string(big)
+    many = f(*args, 3_000_000, 1, 64, 3_000_000, 100, 0, 0, 0, 0.125, 1, FAKE, None, None)
+    assert many == 6
+    # argument errors keep their own status; nothing to do is success
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 100, 100, 0, 0, 0, 0.125, 1, FAKE, None, None) == INVALID
+    assert f(*args, 2, 2, 48, 100, 100, 0, 0, 0, 0.125, 1, FAKE, None, None) == UNSUPPORTED
+    assert f(*args, 0, 2, 64, 0, 0, 0, 0, 0, 0.125, 1, FAKE, None, None) == OK
+
+
 def test_workspace_size_grows_with_tiles(lib):
     small = lib.ja_fwd_workspace_size(4, 2, 128, 1000, 1000, 0, 1, 0, 1)
     big = lib.ja_fwd_workspace_size(4, 2, 128, 100000, 1000, 0, 1, 0, 1)
