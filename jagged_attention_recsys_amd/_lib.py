@@ -5,6 +5,7 @@ fallback: if the library is missing or fails to load, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -54,20 +55,37 @@ class JaggedAttnError(RuntimeError):
         super().__init__(f"{func} failed: {status_string(status)} (status {status})")
 
 
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` with the C signatures set."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m jagged_attention_recsys_amd.build` "
+            "(hipcc, gfx950). There is no non-HIP fallback.")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
 def load() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is not built; run `python -m jagged_attention_recsys_amd.build` "
-                "(hipcc, gfx950). There is no non-HIP fallback.")
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = lib
+        _lib = open_library(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using(lib: ctypes.CDLL):
+    """Route the binding's calls to another build of the library (tests compare builds)."""
+    global _lib
+    load()
+    saved, _lib = _lib, lib
+    try:
+        yield lib
+    finally:
+        _lib = saved
 
 
 def status_string(status: int) -> str:

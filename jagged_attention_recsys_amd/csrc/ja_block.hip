@@ -110,6 +110,9 @@ __device__ __forceinline__ float tile_softmax(floatx16 (&s)[2], bool nb1, bool n
 
 // Workgroup barrier that publishes LDS only: outstanding global loads and
 // stores are not waited for.
+// Waits for LDS operations only: at the item boundaries where it is used no global
+// load into LDS is outstanding (each tile's loads are waited for before the tile
+// is read, with a wait on vector memory operations).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct TileItem {

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
         };
 
         auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {
-            if (kt + 1 < kt_hi) issue(kt + 1, kn, vn);
+            if (!kSingleStage && kt + 1 < kt_hi) issue(kt + 1, kn, vn);
             const int kw0 = kt * kBwdStage;
             const bool skip = wave_skips(vis, row_ok, kw0, kBwdStage);
             if (!skip) {
@@ -244,13 +244,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
             __syncthreads();
         };
 
-        if (kt_hi > kt_lo) {
-            issue(kt_lo, lds_k0, lds_v0);
-            __syncthreads();
-        }
-        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-            stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
-            if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+        if constexpr (kSingleStage) {
+            for (int kt = kt_lo; kt < kt_hi; ++kt) {
+                issue(kt, lds_k0, lds_v0);
+                __syncthreads();
+                stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);  // loads nothing, ends on a barrier
+            }
+        } else {
+            if (kt_hi > kt_lo) {
+                issue(kt_lo, lds_k0, lds_v0);
+                __syncthreads();
+            }
+            for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+                stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+                if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+            }
         }
 
         if constexpr (KP == 8 && sizeof(GT) == 2) {
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 
         auto stage = [&](int qs, const char* ql, const char* ol, const float* ll, const float* dl, char* qn,
                          char* on, float* ln, float* dn) {
-            if (qs + 1 < qs_hi) issue(qs + 1, qn, on, ln, dn);
+            if (!kSingleStage && qs + 1 < qs_hi) issue(qs + 1, qn, on, ln, dn);
             const int qbase = qs * kBwdStage;
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
@@ -503,13 +511,21 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
             __syncthreads();
         };
 
-        if (qs_hi > qs_lo) {
-            issue(qs_lo, lds_q0, lds_o0, lds_l0, lds_d0);
-            __syncthreads();
-        }
-        for (int qs = qs_lo; qs < qs_hi; qs += 2) {
-            stage(qs, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
-            if (qs + 1 < qs_hi) stage(qs + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
+        if constexpr (kSingleStage) {
+            for (int qs = qs_lo; qs < qs_hi; ++qs) {
+                issue(qs, lds_q0, lds_o0, lds_l0, lds_d0);
+                __syncthreads();
+                stage(qs, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);  // ends on a barrier
+            }
+        } else {
+            if (qs_hi > qs_lo) {
+                issue(qs_lo, lds_q0, lds_o0, lds_l0, lds_d0);
+                __syncthreads();
+            }
+            for (int qs = qs_lo; qs < qs_hi; qs += 2) {
+                stage(qs, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
+                if (qs + 1 < qs_hi) stage(qs + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
+            }
         }
 
         if (pair_split) {

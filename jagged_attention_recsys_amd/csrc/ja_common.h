@@ -13,7 +13,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Race-check build switch: with JA_SINGLE_STAGE=1 the forward and both backward
+// passes stream every stage (K/V, or Q/dO) through one LDS buffer, loaded and then
+// consumed between two workgroup barriers, instead of double buffering (the next
+// stage loading while the current one is consumed). The arithmetic is the same, so
+// the two builds must agree bit for bit; a missing wait or barrier in the
+// double-buffered path would show as a difference.
+#ifndef JA_SINGLE_STAGE
+#define JA_SINGLE_STAGE 0
+#endif
+
 namespace ja {
+
+constexpr bool kSingleStage = JA_SINGLE_STAGE != 0;
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -133,6 +133,12 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
     // The next item is popped before the current item's output stores, and the
     // barriers between items only publish LDS: the atomic's return does not queue
     // behind the stores, and the stores drain while the next item starts.
+    // Invariant that makes an LDS-only wait enough here: no buffer-to-LDS stage load
+    // is outstanding at an item boundary. Every stage an item loads is consumed
+    // before that item's last stage barrier (a __syncthreads, which waits for all
+    // vector memory operations), and the next item issues its first load after
+    // these barriers. The single-stage race-check build (JA_SINGLE_STAGE) exercises
+    // the same boundaries with a wait and a barrier around every load.
     auto lds_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
@@ -326,13 +332,22 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
                 }
                 if (kt_hi > kt_lo) compute(rkt, lds_k0, lds_v0);
             } else {
-                if (kt_hi > kt_lo) {
-                    issue(kt_lo, lds_k0, lds_v0);
-                    __syncthreads();
-                }
-                for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-                    stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
-                    if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+                if constexpr (kSingleStage) {
+                    for (int kt = kt_lo; kt < kt_hi; ++kt) {
+                        issue(kt, lds_k0, lds_v0);
+                        __syncthreads();
+                        compute(kt, lds_k0, lds_v0);
+                        __syncthreads();
+                    }
+                } else {
+                    if (kt_hi > kt_lo) {
+                        issue(kt_lo, lds_k0, lds_v0);
+                        __syncthreads();
+                    }
+                    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+                        stage(kt, lds_k0, lds_v0, lds_k1, lds_v1);
+                        if (kt + 1 < kt_hi) stage(kt + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+                    }
                 }
             }
 

@@ -243,6 +243,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
             }
     }
 
+    // Waits for LDS operations only: no buffer-to-LDS stage load is outstanding at
+    // an item boundary (each item's stages are consumed before its last stage
+    // barrier, a __syncthreads that waits for every vector memory operation).
     auto lds_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
