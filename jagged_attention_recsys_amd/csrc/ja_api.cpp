@@ -320,8 +320,13 @@ ja_status_t bwd_impl(const void* q, const void* k, const void* v, const void* ou
     ba.bsh = bsh;
     ba.scale = scale;
     ba.grad_f32 = grad_dtype == JA_F32 ? 1 : 0;
-    const int64_t cap_q = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, false, ba.grad_f32 != 0);
-    const int64_t cap_k = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, true, ba.grad_f32 != 0);
+    // d = 128 with keys longer than one stage on average: the role-split dK/dV pass
+    // (two waves per SIMD). Short key tiles keep the four-wave pass, whose wave
+    // pairs split the query stages of tiles of at most 64 keys.
+    ba.kv_roles = (d == 128 && Tk > 64LL * B) ? 1 : 0;
+    const int64_t cap_q = (int64_t)device_cus() * bwd_blocks_per_cu(d, act, false, ba.grad_f32 != 0, false);
+    const int64_t cap_k =
+        (int64_t)device_cus() * bwd_blocks_per_cu(d, act, true, ba.grad_f32 != 0, ba.kv_roles != 0);
     int64_t gq = p.max_q_pairs * H, gk = p.max_k_pairs * H;
     gq = gq < cap_q ? gq : cap_q;
     gk = gk < cap_k ? gk : cap_k;

@@ -588,6 +588,316 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 #endif
 }
 
+// dK/dV pass, role-split form (d = 128) --------------------------------------------
+// Eight waves per workgroup, one workgroup per CU, two waves per SIMD: waves w and
+// w + 4 (one SIMD) own the same 32 keys of the 128-key item. Wave w (the P wave)
+// holds K as the B operand and forms S = Q K^T, the weights P (softmax: exp(S -
+// lse); SiLU / GELU: act(Z) / Lk) and dV^T += dO^T P; wave w + 4 (the dS wave) holds
+// V and forms dP = dO V^T, dS and dK^T += Q^T dS. Per 64-query stage the P wave
+// hands its per-score factor for dS (softmax: P; SiLU / GELU: act'(Z) / Lk, zero
+// where masked) to its partner through LDS, between the two halves of the stage.
+// Each wave keeps one accumulator set and one operand set, so both fit the
+// registers of two waves per SIMD, and one wave's vector work (the exponentials,
+// dS) overlaps its partner's matrix products. Every product is formed as in
+// ja_bwd_dkdv_kernel, in the same order.
+constexpr int kKv2Waves = 8;
+constexpr int kKv2Threads = 64 * kKv2Waves;
+// Tag that selects the role-split form of the dK/dV kernel (same kernel name in traces).
+struct RolePair {};
+
+template <typename T, int D, int ACT, typename GT>
+__global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, RolePair) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = BwdCfg<T, D>;
+    using M = Mma<T>;
+    typedef typename Frag<T>::type frag;
+    constexpr int KP = C::KP;
+    static_assert(KP == 8 && C::NB == 2 && C::NT == 2, "bf16, 64-query stages");
+    using Loader = TileLoader<typename C::STile, kKv2Waves>;
+
+    __shared__ __attribute__((aligned(1024))) char lds_q0[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_o0[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_q1[C::STile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_o1[C::STile::BYTES];
+    __shared__ __attribute__((aligned(256))) float lds_l0[kBwdStage];
+    __shared__ __attribute__((aligned(256))) float lds_d0[kBwdStage];
+    __shared__ __attribute__((aligned(256))) float lds_l1[kBwdStage];
+    __shared__ __attribute__((aligned(256))) float lds_d1[kBwdStage];
+    // Hand-over of the dS factor: [key block][query block][register quad][lane].
+    __shared__ __attribute__((aligned(256))) floatx4 xch[4][C::NB][4][64];
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool pw = wave < 4;  // the P wave of its pair (else the dS wave)
+    const int kb = wave & 3;   // the pair's 32-key block
+    const int col = lane & 31, grp = lane >> 5;
+    const int total = a.k_counters[kCtrTotal];
+    const int64_t rs = (int64_t)a.H * D;
+    const uint32_t rsb = (uint32_t)(rs * (int)sizeof(T));
+    const uint32_t hsb = (uint32_t)(a.H * 4);
+    const int causal = a.causal, window = a.window, bsh = a.bsh;
+    const float c_exp = a.scale * kLog2e;
+
+    int roff[C::NS];
+    int toff[C::ND][2];
+    C::STile::row_offsets(col, grp, roff);
+    C::STile::tr_offsets(lane, toff);
+    Loader ld;
+    ld.init(wave, lane, rsb);
+
+    for (;;) {
+        __syncthreads();
+        if (tid == 0) s_item = atomicAdd(&a.k_counters[kCtrPop], 1);
+        __syncthreads();
+        const int idx = __builtin_amdgcn_readfirstlane(s_item);
+        if (idx >= total) break;
+        const int pair = idx / a.H, h = idx - pair * a.H;
+        const ItemSeq is = load_item(a.k_items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const int64_t qo = is.qo, ko = is.ko;
+        const int Lq = is.Lq, Lk = is.Lk;
+        const int k0 = is.t * kBwdRows;
+        const ColRange cr = visible_cols(Lk, Lq, k0, kBwdRows, causal, window, 1, bsh);
+        const int qs_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
+        const int qs_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
+        const int kw0 = k0 + 32 * kb;
+        const int my_key = kw0 + col;
+        const bool key_ok = my_key < Lk;
+        const VisRange vis = queries_seeing(my_key, Lq, Lk, causal, window, bsh);
+        const float inv_lk = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
+
+        // The wave's B operand: K rows (P wave) or V rows (dS wave) of its 32 keys.
+        frag bf[C::NS];
+        {
+            const T* src = (const T*)(pw ? a.k : a.v) + (ko + my_key) * rs + (int64_t)h * D + KP * grp;
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) bf[s] = key_ok ? *(const frag*)(src + 2 * KP * s) : Frag<T>::zero();
+        }
+        floatx16 acc[C::ND];  // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+        for (int i = 0; i < C::ND; ++i) acc[i] = floatx16{};
+
+        const char* Qseq = (const char*)a.q + (qo * rs + (int64_t)h * D) * (int)sizeof(T);
+        const char* Oseq = (const char*)a.dout + (qo * rs + (int64_t)h * D) * (int)sizeof(T);
+        const char* Lseq = (const char*)(a.lse + qo * a.H + h);
+        const char* Dseq = (const char*)(a.di + qo * a.H + h);
+        auto issue = [&](int qs, char* qdst, char* odst, float* ldst, float* ddst) {
+            const int qbase = qs * kBwdStage;
+            const int nvalid = min(max(Lq - qbase, 0), kBwdStage);
+            const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * rsb);
+            ld.issue(Qseq + (int64_t)qbase * rsb, nrec, qdst, wave);
+            ld.issue(Oseq + (int64_t)qbase * rsb, nrec, odst, wave);
+            if (ACT == ACT_SOFTMAX && wave < 2) {
+                const uint32_t nrec_s = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * hsb);
+                const char* src = (wave == 0 ? Lseq : Dseq) + (int64_t)qbase * hsb;
+                const __amdgpu_buffer_rsrc_t r =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, (int)nrec_s, 0x00020000);
+                lds_char* dst = (lds_char*)(wave == 0 ? ldst : ddst);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, (uint32_t)lane * hsb, 0, 0, 0);
+            }
+        };
+
+        // Four consecutive fp32 values of lse (or Di) for register run r of block nb.
+        auto run4 = [&](const float* base, int nb, int r) __attribute__((always_inline)) {
+            return *(const floatx4*)(base + nb * 32 + key_of_reg<KP>(grp, r));
+        };
+
+        auto stage = [&](int qs, const char* ql, const char* ol, const float* ll, const float* dl, char* qn,
+                         char* on, float* ln, float* dn) {
+            if (!kSingleStage && qs + 1 < qs_hi) issue(qs + 1, qn, on, ln, dn);
+            const int qbase = qs * kBwdStage;
+            bool active[C::NB], need_mask[C::NB];
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                active[nb] = !wave_skips(vis, key_ok, qbase + nb * 32, 32);
+                need_mask[nb] = wave_needs_mask(vis, key_ok, qbase + nb * 32, 32);
+            }
+            // Each role's body reads its LDS arrays directly (never through a pointer
+            // chosen by role), so the compiler can tell the current stage's arrays from
+            // the ones the next stage is loading into and does not wait for that load.
+            //
+            // The stage runs in three phases split by two barriers, the dS wave one
+            // query block behind the P wave, so that each wave's vector work meets
+            // matrix products of its partner:
+            //   phase 1: P: S, weights, factor of block 0      dS: dP of blocks 0 and 1
+            //   phase 2: P: S, weights, factor of block 1;     dS: dS, dK of block 0
+            //            dV of block 0
+            //   phase 3: P: dV of block 1                      dS: dS, dK of block 1
+            // Only LDS operations are waited for at the two inner barriers: the next
+            // stage's loads stay in flight through them.
+            if (pw) {
+                frag pf[C::NB][C::NT];
+                // S = Q K^T for block nb, the weights (kept as P fragments) and the dS
+                // factor handed to the partner.
+                auto weights = [&](int nb) __attribute__((always_inline)) {
+                    const int qb0 = qbase + nb * 32;
+                    frag ra[C::NS];
+#pragma unroll
+                    for (int s = 0; s < C::NS; ++s) ra[s] = C::STile::read_rows(ql + nb * 32 * C::ROWB, roff[s]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    floatx16 c = floatx16{};
+#pragma unroll
+                    for (int s = 0; s < C::NS; ++s) c = M::run(ra[s], bf[s], c);
+                    __builtin_amdgcn_sched_barrier(0);
+                    floatx4 l4[4];
+                    if constexpr (ACT == ACT_SOFTMAX) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) l4[j] = run4(ll, nb, 4 * j);
+                    }
+                    floatx16 x;  // the dS factor handed to the partner
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p, f;
+                        if constexpr (ACT == ACT_SOFTMAX) {
+                            p = fast_exp2(fmaf(c[r], c_exp, -l4[r >> 2][r & 3] * kLog2e));
+                            f = p;
+                        } else {
+                            float av, dav;
+                            pointwise_grad<ACT>(c[r] * a.scale, av, dav);
+                            p = av * inv_lk;
+                            f = dav * inv_lk;
+                        }
+                        c[r] = p;
+                        x[r] = f;
+                    }
+                    if (need_mask[nb]) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const bool ok = vis.has(qb0 + key_of_reg<KP>(grp, r));
+                            c[r] = ok ? c[r] : 0.0f;
+                            x[r] = ok ? x[r] : 0.0f;
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        xch[kb][nb][j][lane] = floatx4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+#pragma unroll
+                    for (int t = 0; t < C::NT; ++t) pf[nb][t] = to_frag<T>(c, KP * t);
+                };
+                // dV^T += dO^T P for block nb.
+                auto dv = [&](int nb) __attribute__((always_inline)) {
+                    frag tf[C::NT][C::ND];
+#pragma unroll
+                    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+                        for (int db = 0; db < C::ND; ++db)
+                            tf[t][db] = C::STile::read_tr(ol + nb * 32 * C::ROWB, t, toff, db);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+                        for (int db = 0; db < C::ND; ++db) acc[db] = M::run(tf[t][db], pf[nb][t], acc[db]);
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                if (active[0]) weights(0);
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (active[1]) weights(1);
+                if (active[0]) dv(0);
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (active[1]) dv(1);
+            } else {
+                floatx16 dpacc[C::NB];
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb) {
+                    if (!active[nb]) continue;
+                    frag ra[C::NS];
+#pragma unroll
+                    for (int s = 0; s < C::NS; ++s) ra[s] = C::STile::read_rows(ol + nb * 32 * C::ROWB, roff[s]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    floatx16 c = floatx16{};
+#pragma unroll
+                    for (int s = 0; s < C::NS; ++s) c = M::run(ra[s], bf[s], c);
+                    __builtin_amdgcn_sched_barrier(0);
+                    dpacc[nb] = c;
+                }
+                // dS = factor o (dP - Di) (softmax) or factor o dP, then dK^T += Q^T dS,
+                // for block nb once its factor is in LDS.
+                auto dk = [&](int nb) __attribute__((always_inline)) {
+                    floatx4 xf[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) xf[j] = xch[kb][nb][j][lane];
+                    floatx4 d4[4];
+                    if constexpr (ACT == ACT_SOFTMAX) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) d4[j] = run4(dl, nb, 4 * j);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    floatx16 g;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        if constexpr (ACT == ACT_SOFTMAX)
+                            g[r] = xf[r >> 2][r & 3] * (dpacc[nb][r] - d4[r >> 2][r & 3]);
+                        else
+                            g[r] = xf[r >> 2][r & 3] * dpacc[nb][r];
+                    }
+                    frag gf[C::NT];
+#pragma unroll
+                    for (int t = 0; t < C::NT; ++t) gf[t] = to_frag<T>(g, KP * t);
+                    frag tf[C::NT][C::ND];
+#pragma unroll
+                    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+                        for (int db = 0; db < C::ND; ++db)
+                            tf[t][db] = C::STile::read_tr(ql + nb * 32 * C::ROWB, t, toff, db);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+                        for (int db = 0; db < C::ND; ++db) acc[db] = M::run(tf[t][db], gf[t], acc[db]);
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (active[0]) dk(0);
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (active[1]) dk(1);
+            }
+            __syncthreads();
+        };
+
+        if constexpr (kSingleStage) {
+            for (int qs = qs_lo; qs < qs_hi; ++qs) {
+                issue(qs, lds_q0, lds_o0, lds_l0, lds_d0);
+                __syncthreads();
+                stage(qs, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
+            }
+        } else {
+            if (qs_hi > qs_lo) {
+                issue(qs_lo, lds_q0, lds_o0, lds_l0, lds_d0);
+                __syncthreads();
+            }
+            for (int qs = qs_lo; qs < qs_hi; qs += 2) {
+                stage(qs, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
+                if (qs + 1 < qs_hi) stage(qs + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
+            }
+        }
+
+        // Whole rows out through a wave-private region of the stage buffers (free: the
+        // stage loop ended on a barrier, or loaded nothing): dV from the P waves, dK
+        // (times scale) from the dS waves.
+        const float sc = pw ? 1.0f : a.scale;
+        GT* const dst = (GT*)(pw ? a.dv : a.dk);
+        if constexpr (sizeof(GT) == 2) {
+            using RT = RowTurn<D>;
+            static_assert(2 * RT::BYTES == C::STile::BYTES, "two regions per stage array");
+            char* const buf = wave < 2 ? lds_q0 : wave < 4 ? lds_o0 : wave < 6 ? lds_q1 : lds_o1;
+            char* const wreg = buf + (wave & 1) * RT::BYTES;
+            RT::put_acc(wreg, acc, sc, lane);
+            RT::store((bf16*)dst + (ko + kw0) * rs + (int64_t)h * D, rs, Lk - kw0, wreg, lane);
+        } else if (key_ok) {
+            GT* d = dst + (ko + my_key) * rs + (int64_t)h * D + 4 * grp;
+#pragma unroll
+            for (int i = 0; i < C::ND; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    store4<GT>(d + 32 * i + 8 * j, acc[i][4 * j] * sc, acc[i][4 * j + 1] * sc,
+                               acc[i][4 * j + 2] * sc, acc[i][4 * j + 3] * sc);
+        }
+    }
+#else
+    (void)a;
+#endif
+}
+
 template <int D, int ACT, typename GT>
 hipError_t launch_g(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hipEvent_t before, hipEvent_t mid,
                     hipEvent_t after) {
@@ -596,7 +906,12 @@ hipError_t launch_g(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hip
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (mid && hipEventRecord(mid, s) != hipSuccess) return hipErrorUnknown;
-    hipLaunchKernelGGL((ja_bwd_dkdv_kernel<bf16, D, ACT, GT>), dim3(grid_k), dim3(kBwdThreads), 0, s, a);
+    void (*const plain)(BwdArgs) = &ja_bwd_dkdv_kernel<bf16, D, ACT, GT>;
+    void (*const pairs)(BwdArgs, RolePair) = &ja_bwd_dkdv_kernel<bf16, 128, ACT, GT>;
+    if (D == 128 && a.kv_roles)
+        hipLaunchKernelGGL(pairs, dim3(grid_k), dim3(kKv2Threads), 0, s, a, RolePair{});
+    else
+        hipLaunchKernelGGL(plain, dim3(grid_k), dim3(kBwdThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (after && hipEventRecord(after, s) != hipSuccess) return hipErrorUnknown;
@@ -611,17 +926,22 @@ hipError_t launch_d(const BwdArgs& a, int grid_q, int grid_k, hipStream_t s, hip
 }
 
 template <int D, int ACT, typename GT>
-int occupancy_g(bool dkdv) {
+int occupancy_g(bool dkdv, bool roles) {
     int n = 0;
-    const void* fn = dkdv ? reinterpret_cast<const void*>(&ja_bwd_dkdv_kernel<bf16, D, ACT, GT>)
-                          : reinterpret_cast<const void*>(&ja_bwd_dq_kernel<bf16, D, ACT, GT>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBwdThreads, 0) != hipSuccess) n = 1;
+    void (*const dq)(BwdArgs) = &ja_bwd_dq_kernel<bf16, D, ACT, GT>;
+    void (*const plain)(BwdArgs) = &ja_bwd_dkdv_kernel<bf16, D, ACT, GT>;
+    void (*const pairs)(BwdArgs, RolePair) = &ja_bwd_dkdv_kernel<bf16, 128, ACT, GT>;
+    const void* fn = !dkdv                 ? reinterpret_cast<const void*>(dq)
+                     : (D == 128 && roles) ? reinterpret_cast<const void*>(pairs)
+                                           : reinterpret_cast<const void*>(plain);
+    const int threads = (dkdv && D == 128 && roles) ? kKv2Threads : kBwdThreads;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess) n = 1;
     return n > 0 ? n : 1;
 }
 
 template <int D, int ACT>
-int occupancy_d(bool dkdv, bool grad_f32) {
-    return grad_f32 ? occupancy_g<D, ACT, float>(dkdv) : occupancy_g<D, ACT, bf16>(dkdv);
+int occupancy_d(bool dkdv, bool grad_f32, bool roles) {
+    return grad_f32 ? occupancy_g<D, ACT, float>(dkdv, roles) : occupancy_g<D, ACT, bf16>(dkdv, roles);
 }
 
 }  // namespace
@@ -645,11 +965,11 @@ hipError_t launch_a(const BwdArgs& a, int d, int grid_q, int grid_k, hipStream_t
 }
 
 template <int ACT>
-int occupancy_a(int d, bool dkdv, bool grad_f32) {
+int occupancy_a(int d, bool dkdv, bool grad_f32, bool roles) {
     switch (d) {
-        case 32: return occupancy_d<32, ACT>(dkdv, grad_f32);
-        case 64: return occupancy_d<64, ACT>(dkdv, grad_f32);
-        case 128: return occupancy_d<128, ACT>(dkdv, grad_f32);
+        case 32: return occupancy_d<32, ACT>(dkdv, grad_f32, false);
+        case 64: return occupancy_d<64, ACT>(dkdv, grad_f32, false);
+        case 128: return occupancy_d<128, ACT>(dkdv, grad_f32, roles);
         default: return 1;
     }
 }
@@ -665,12 +985,12 @@ hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, 
     }
 }
 
-int bwd_blocks_per_cu(int d, int act, bool dkdv, bool grad_f32) {
+int bwd_blocks_per_cu(int d, int act, bool dkdv, bool grad_f32, bool roles) {
     switch (act) {
-        case ACT_SOFTMAX: return occupancy_a<ACT_SOFTMAX>(d, dkdv, grad_f32);
-        case ACT_SILU: return occupancy_a<ACT_SILU>(d, dkdv, grad_f32);
-        case ACT_GELU: return occupancy_a<ACT_GELU>(d, dkdv, grad_f32);
-        case ACT_GELU_TAYLOR: return occupancy_a<ACT_GELU_TAYLOR>(d, dkdv, grad_f32);
+        case ACT_SOFTMAX: return occupancy_a<ACT_SOFTMAX>(d, dkdv, grad_f32, roles);
+        case ACT_SILU: return occupancy_a<ACT_SILU>(d, dkdv, grad_f32, roles);
+        case ACT_GELU: return occupancy_a<ACT_GELU>(d, dkdv, grad_f32, roles);
+        case ACT_GELU_TAYLOR: return occupancy_a<ACT_GELU_TAYLOR>(d, dkdv, grad_f32, roles);
         default: return 1;
     }
 }

@@ -89,6 +89,7 @@ struct BwdArgs {
     int32_t bsh;               // block shift of the block-diagonal mask (kNoBlock: none)
     float scale;
     int32_t grad_f32;          // dq, dk, dv are fp32 (else the input type)
+    int32_t kv_roles;          // d = 128: the dK/dV pass in its role-split form (8 waves, 2 per SIMD)
 };
 bool bwd_supported(int dtype, int d, int act);
 int bwd_rows_per_item();   // query rows (dQ pass) and key rows (dK/dV pass) per work item
@@ -97,8 +98,8 @@ int bwd_cols_per_stage();  // keys (dQ pass) and queries (dK/dV pass) per stage:
 // the dK/dV pass.
 hipError_t launch_bwd(const BwdArgs& a, int d, int act, int grid_q, int grid_k, hipStream_t stream,
                       hipEvent_t before, hipEvent_t mid, hipEvent_t after);
-// Workgroups per CU of the dQ (false) or dK/dV pass.
-int bwd_blocks_per_cu(int d, int act, bool dkdv, bool grad_f32);
+// Workgroups per CU of the dQ (false) or dK/dV pass (roles: its role-split form).
+int bwd_blocks_per_cu(int d, int act, bool dkdv, bool grad_f32, bool roles);
 
 // Argument checks of jagged_attn_fwd that need no device access (workspace aside);
 // JA_OK also for an empty batch.

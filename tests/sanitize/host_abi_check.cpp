@@ -87,7 +87,7 @@ hipError_t launch_bwd(const BwdArgs& a, int, int, int gq, int gk, hipStream_t, h
     if (gq < 1 || gk < 1) fail("backward launch shape");
     return hipSuccess;
 }
-int bwd_blocks_per_cu(int, int, bool, bool) { return 1; }
+int bwd_blocks_per_cu(int, int, bool, bool, bool) { return 1; }
 bool blk_supported(int dtype, int d, int bsh) { return dtype == 1 && (d == 32 || d == 64 || d == 128) && bsh <= 6; }
 int blk_blocks_per_cu(int) { return 2; }
 hipError_t launch_blk_bwd(const BlkArgs& a, int, int grid, hipStream_t) {
