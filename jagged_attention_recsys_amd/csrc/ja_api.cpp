@@ -70,7 +70,7 @@ ja_status_t plan_fwd(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, in
     if (p->max_pairs * (int64_t)H >= INT32_MAX) return JA_ERR_UNSUPPORTED;
     p->off_tbase = align_up(sizeof(int32_t) * kCtrCount);
     p->off_items = align_up(p->off_tbase + sizeof(int32_t) * ((size_t)B + 1));
-    p->bytes = align_up(p->off_items + sizeof(int32_t) * 2 * (size_t)p->max_pairs);
+    p->bytes = align_up(p->off_items + sizeof(int32_t) * kItemInts * (size_t)p->max_pairs);
     return JA_OK;
 }
 
@@ -92,8 +92,8 @@ ja_status_t plan_bwd(int32_t B, int32_t H, int64_t Tq, int64_t Tk, BwdPlan* p) {
     p->off_kctr = o; o = align_up(o + sizeof(int32_t) * kCtrCount);
     p->off_qtbase = o; o = align_up(o + sizeof(int32_t) * ((size_t)B + 1));
     p->off_ktbase = o; o = align_up(o + sizeof(int32_t) * ((size_t)B + 1));
-    p->off_qitems = o; o = align_up(o + sizeof(int32_t) * 2 * (size_t)p->max_q_pairs);
-    p->off_kitems = o; o = align_up(o + sizeof(int32_t) * 2 * (size_t)p->max_k_pairs);
+    p->off_qitems = o; o = align_up(o + sizeof(int32_t) * kItemInts * (size_t)p->max_q_pairs);
+    p->off_kitems = o; o = align_up(o + sizeof(int32_t) * kItemInts * (size_t)p->max_k_pairs);
     p->off_di = o; o = align_up(o + sizeof(float) * (size_t)Tq * (size_t)H);
     p->bytes = o;
     return JA_OK;
@@ -109,7 +109,7 @@ ja_status_t plan_blk(int32_t B, int32_t H, int64_t T, BlkPlan* p) {
     if (p->max_pairs * (int64_t)H >= INT32_MAX) return JA_ERR_UNSUPPORTED;
     p->off_tbase = align_up(sizeof(int32_t) * kCtrCount);
     p->off_items = align_up(p->off_tbase + sizeof(int32_t) * ((size_t)B + 1));
-    p->bytes = align_up(p->off_items + sizeof(int32_t) * 2 * (size_t)p->max_pairs);
+    p->bytes = align_up(p->off_items + sizeof(int32_t) * kItemInts * (size_t)p->max_pairs);
     return JA_OK;
 }
 
@@ -525,7 +525,7 @@ size_t ja_fwd_mxfp8_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, 
     if (max_pairs * (int64_t)H >= INT32_MAX) return 0;
     const size_t off_tbase = align_up(sizeof(int32_t) * kCtrCount);
     const size_t off_items = align_up(off_tbase + sizeof(int32_t) * ((size_t)B + 1));
-    return align_up(off_items + sizeof(int32_t) * 2 * (size_t)max_pairs);
+    return align_up(off_items + sizeof(int32_t) * kItemInts * (size_t)max_pairs);
 }
 
 ja_status_t jagged_attn_fwd_mxfp8(const void* q8, const void* q_scales, const int32_t* q_scale_offsets,

@@ -127,9 +127,11 @@ __device__ __forceinline__ bool tile_item(const BlkArgs& a, int idx, TileItem& i
     // Within the capacity the item is read before the count is known (one
     // dependent load fewer); entries past the count are stale and rejected.
     const int total = a.counters[kCtrTotal];
-    const int b = a.items[2 * pair], t = a.items[2 * pair + 1];
+    typedef int int4v __attribute__((ext_vector_type(4)));
+    const int4v rec = *(const int4v*)(a.items + kItemInts * (int64_t)pair);  // b, t, off[b], off[b+1]
+    const int b = rec[0], t = rec[1];
     if (idx >= total || b < 0 || b >= a.B) return false;
-    const int o0 = a.off[b], o1 = a.off[b + 1];  // independent loads
+    const int o0 = rec[2], o1 = rec[3];
     it.o0 = o0;
     // Rows are clamped to the tensors, so inconsistent offsets cannot reach
     // outside them.

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
         const int idx = __builtin_amdgcn_readfirstlane(s_item);
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
-        const ItemSeq is = load_item(a.q_items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const ItemSeq is = load_item(a.q_items, pair, false, a.Tq, a.Tk);
         const int qt = is.t;
         const int64_t qo = is.qo, ko = is.ko;
         const int Lq = is.Lq, Lk = is.Lk;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         const int idx = __builtin_amdgcn_readfirstlane(s_item);
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
-        const ItemSeq is = load_item(a.k_items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const ItemSeq is = load_item(a.k_items, pair, true, a.Tq, a.Tk);
         const int kt = is.t;
         const int64_t qo = is.qo, ko = is.ko;
         const int Lq = is.Lq, Lk = is.Lk;
@@ -625,7 +625,6 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
     __shared__ __attribute__((aligned(256))) float lds_d1[kBwdStage];
     // Hand-over of the dS factor: [key block][query block][register quad][lane].
     __shared__ __attribute__((aligned(256))) floatx4 xch[4][C::NB][4][64];
-    __shared__ int s_item;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -639,72 +638,110 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
     const int causal = a.causal, window = a.window, bsh = a.bsh;
     const float c_exp = a.scale * kLog2e;
 
-    int roff[C::NS];
     int toff[C::ND][2];
-    C::STile::row_offsets(col, grp, roff);
+    const int rx = C::STile::row_offset_base(col, grp);  // one register for the row-operand offsets
     C::STile::tr_offsets(lane, toff);
     Loader ld;
     ld.init(wave, lane, rsb);
 
-    for (;;) {
-        __syncthreads();
-        if (tid == 0) s_item = atomicAdd(&a.k_counters[kCtrPop], 1);
-        __syncthreads();
-        const int idx = __builtin_amdgcn_readfirstlane(s_item);
-        if (idx >= total) break;
-        const int pair = idx / a.H, h = idx - pair * a.H;
-        const ItemSeq is = load_item(a.k_items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
-        const int64_t qo = is.qo, ko = is.ko;
-        const int Lq = is.Lq, Lk = is.Lk;
-        const int k0 = is.t * kBwdRows;
-        const ColRange cr = visible_cols(Lk, Lq, k0, kBwdRows, causal, window, 1, bsh);
-        const int qs_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
-        const int qs_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
-        const int kw0 = k0 + 32 * kb;
+    // One work item: a (sequence, head, 128-key tile) and the query stages its keys see.
+    struct Item {
+        int h, Lq, Lk, k0, qs_lo, qs_hi;
+        int qo, ko;  // first query / key row of the sequence (row indices fit 32 bits)
+    };
+    auto geometry = [&](int idx, const ItemSeq& is) {
+        Item it;
+        it.h = idx - (idx / a.H) * a.H;
+        it.qo = (int)is.qo;
+        it.ko = (int)is.ko;
+        it.Lq = is.Lq;
+        it.Lk = is.Lk;
+        it.k0 = is.t * kBwdRows;
+        const ColRange cr = visible_cols(it.Lk, it.Lq, it.k0, kBwdRows, causal, window, 1, bsh);
+        it.qs_lo = cr.hi > cr.lo ? (int)(cr.lo / kBwdStage) : 0;
+        it.qs_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
+        return it;
+    };
+    // Query stage qs of an item (Q, dO rows; lse, Di for softmax) into one set of stage arrays.
+    auto issue = [&](const Item& it, int qs, char* qdst, char* odst, float* ldst, float* ddst) {
+        const int qbase = qs * kBwdStage;
+        const int nvalid = min(max(it.Lq - qbase, 0), kBwdStage);
+        const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * rsb);
+        const int64_t row0 = (int64_t)(it.qo + qbase) * rs + (int64_t)it.h * D;
+        ld.issue((const char*)a.q + row0 * (int)sizeof(T), nrec, qdst, wave);
+        ld.issue((const char*)a.dout + row0 * (int)sizeof(T), nrec, odst, wave);
+        if (ACT == ACT_SOFTMAX && wave < 2) {
+            const uint32_t nrec_s = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * hsb);
+            const float* src = (wave == 0 ? a.lse : a.di) + (int64_t)(it.qo + qbase) * a.H + it.h;
+            const __amdgpu_buffer_rsrc_t r =
+                __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, (int)nrec_s, 0x00020000);
+            lds_char* dst = (lds_char*)(wave == 0 ? ldst : ddst);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, (uint32_t)lane * hsb, 0, 0, 0);
+        }
+    };
+    // The wave's B operand: K rows (P wave) or V rows (dS wave) of its 32 keys.
+    frag bf[C::NS];
+    auto load_bf = [&](const Item& it, int ln) __attribute__((always_inline)) {
+        const int key = it.k0 + 32 * kb + (ln & 31);
+        const bool ok = key < it.Lk;
+        const T* src = (const T*)(pw ? a.k : a.v) + (int64_t)(it.ko + key) * rs + (int64_t)it.h * D + KP * (ln >> 5);
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) bf[s] = ok ? *(const frag*)(src + 2 * KP * s) : Frag<T>::zero();
+    };
+    // (Double-buffered) an item's first query stage, into the first set of stage arrays.
+    auto first_stage = [&](const Item& it) __attribute__((always_inline)) {
+        if (!kSingleStage && it.qs_hi > it.qs_lo) issue(it, it.qs_lo, lds_q0, lds_o0, lds_l0, lds_d0);
+    };
+    // Four consecutive fp32 values of lse (or Di) for register run r of block nb.
+    auto run4 = [&](const float* base, int nb, int r) __attribute__((always_inline)) {
+        return *(const floatx4*)(base + nb * 32 + key_of_reg<KP>(grp, r));
+    };
+
+    // Items are popped one ahead and the next item's record is copied into LDS while
+    // the current item runs, so that after its last stage the next item's K / V rows
+    // and first query stage are requested before the current item's output is written
+    // (their latency overlaps the output turnaround instead of following it).
+    __shared__ int s_pop[2];
+    __shared__ __attribute__((aligned(32))) int s_rec[kItemInts];
+    if (tid == 0) {
+        s_pop[0] = atomicAdd(&a.k_counters[kCtrPop], 1);
+        s_pop[1] = atomicAdd(&a.k_counters[kCtrPop], 1);
+    }
+    __syncthreads();
+    int cur_idx = __builtin_amdgcn_readfirstlane(s_pop[0]);
+    int nxt_idx = __builtin_amdgcn_readfirstlane(s_pop[1]);
+    Item cur{};
+    if (cur_idx < total) {
+        cur = geometry(cur_idx, load_item(a.k_items, cur_idx / a.H, true, a.Tq, a.Tk));
+        load_bf(cur, lane);
+        first_stage(cur);
+    }
+
+    for (int it_n = 0; cur_idx < total; ++it_n) {
+        __syncthreads();  // the item's first stage and K / V rows are in
+        const bool nx_ok = nxt_idx < total;
+        if (wave == 0 && lane < kItemInts && nx_ok) {
+            // The next item's record, straight into LDS. It lands before the first
+            // stage's closing barrier, which waits for vector memory.
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(a.k_items + kItemInts * (int64_t)(nxt_idx / a.H)), (short)0, 4 * kItemInts, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char*)s_rec, 4, (uint32_t)lane * 4, 0, 0, 0);
+        }
+        const int h = cur.h, Lq = cur.Lq, Lk = cur.Lk, qs_lo = cur.qs_lo, qs_hi = cur.qs_hi;
+        const int64_t ko = cur.ko;  // widened for the output addresses
+        const int kw0 = cur.k0 + 32 * kb;
         const int my_key = kw0 + col;
         const bool key_ok = my_key < Lk;
         const VisRange vis = queries_seeing(my_key, Lq, Lk, causal, window, bsh);
         const float inv_lk = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
 
-        // The wave's B operand: K rows (P wave) or V rows (dS wave) of its 32 keys.
-        frag bf[C::NS];
-        {
-            const T* src = (const T*)(pw ? a.k : a.v) + (ko + my_key) * rs + (int64_t)h * D + KP * grp;
-#pragma unroll
-            for (int s = 0; s < C::NS; ++s) bf[s] = key_ok ? *(const frag*)(src + 2 * KP * s) : Frag<T>::zero();
-        }
         floatx16 acc[C::ND];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
         for (int i = 0; i < C::ND; ++i) acc[i] = floatx16{};
 
-        const char* Qseq = (const char*)a.q + (qo * rs + (int64_t)h * D) * (int)sizeof(T);
-        const char* Oseq = (const char*)a.dout + (qo * rs + (int64_t)h * D) * (int)sizeof(T);
-        const char* Lseq = (const char*)(a.lse + qo * a.H + h);
-        const char* Dseq = (const char*)(a.di + qo * a.H + h);
-        auto issue = [&](int qs, char* qdst, char* odst, float* ldst, float* ddst) {
-            const int qbase = qs * kBwdStage;
-            const int nvalid = min(max(Lq - qbase, 0), kBwdStage);
-            const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * rsb);
-            ld.issue(Qseq + (int64_t)qbase * rsb, nrec, qdst, wave);
-            ld.issue(Oseq + (int64_t)qbase * rsb, nrec, odst, wave);
-            if (ACT == ACT_SOFTMAX && wave < 2) {
-                const uint32_t nrec_s = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * hsb);
-                const char* src = (wave == 0 ? Lseq : Dseq) + (int64_t)qbase * hsb;
-                const __amdgpu_buffer_rsrc_t r =
-                    __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, (int)nrec_s, 0x00020000);
-                lds_char* dst = (lds_char*)(wave == 0 ? ldst : ddst);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, (uint32_t)lane * hsb, 0, 0, 0);
-            }
-        };
-
-        // Four consecutive fp32 values of lse (or Di) for register run r of block nb.
-        auto run4 = [&](const float* base, int nb, int r) __attribute__((always_inline)) {
-            return *(const floatx4*)(base + nb * 32 + key_of_reg<KP>(grp, r));
-        };
-
         auto stage = [&](int qs, const char* ql, const char* ol, const float* ll, const float* dl, char* qn,
                          char* on, float* ln, float* dn) {
-            if (!kSingleStage && qs + 1 < qs_hi) issue(qs + 1, qn, on, ln, dn);
+            if (!kSingleStage && qs + 1 < qs_hi) issue(cur, qs + 1, qn, on, ln, dn);
             const int qbase = qs * kBwdStage;
             bool active[C::NB], need_mask[C::NB];
 #pragma unroll
@@ -733,7 +770,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
                     const int qb0 = qbase + nb * 32;
                     frag ra[C::NS];
 #pragma unroll
-                    for (int s = 0; s < C::NS; ++s) ra[s] = C::STile::read_rows(ql + nb * 32 * C::ROWB, roff[s]);
+                    for (int s = 0; s < C::NS; ++s) ra[s] = C::STile::read_rows(ql + nb * 32 * C::ROWB, C::STile::row_offset(rx, s));
                     __builtin_amdgcn_sched_barrier(0);
                     floatx16 c = floatx16{};
 #pragma unroll
@@ -802,7 +839,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
                     if (!active[nb]) continue;
                     frag ra[C::NS];
 #pragma unroll
-                    for (int s = 0; s < C::NS; ++s) ra[s] = C::STile::read_rows(ol + nb * 32 * C::ROWB, roff[s]);
+                    for (int s = 0; s < C::NS; ++s) ra[s] = C::STile::read_rows(ol + nb * 32 * C::ROWB, C::STile::row_offset(rx, s));
                     __builtin_amdgcn_sched_barrier(0);
                     floatx16 c = floatx16{};
 #pragma unroll
@@ -856,42 +893,70 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
 
         if constexpr (kSingleStage) {
             for (int qs = qs_lo; qs < qs_hi; ++qs) {
-                issue(qs, lds_q0, lds_o0, lds_l0, lds_d0);
+                issue(cur, qs, lds_q0, lds_o0, lds_l0, lds_d0);
                 __syncthreads();
                 stage(qs, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
             }
         } else {
-            if (qs_hi > qs_lo) {
-                issue(qs_lo, lds_q0, lds_o0, lds_l0, lds_d0);
-                __syncthreads();
-            }
             for (int qs = qs_lo; qs < qs_hi; qs += 2) {
                 stage(qs, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
                 if (qs + 1 < qs_hi) stage(qs + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
             }
         }
+        if (qs_hi <= qs_lo) __syncthreads();  // no stage ran: the record has landed after this
 
-        // Whole rows out through a wave-private region of the stage buffers (free: the
-        // stage loop ended on a barrier, or loaded nothing): dV from the P waves, dK
-        // (times scale) from the dS waves.
+        // The lane index as a value the compiler cannot see through: what the epilogue
+        // derives from it is computed here, not kept in registers across the stages.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        // Every stage array is free (the last stage ended on a barrier). The next item's
+        // first query stage goes out first, into the first set of stage arrays; its K / V
+        // rows follow once the accumulators are in LDS (their registers are then free).
+        Item nxt{};
+        if (nx_ok) {
+            // The record as wave-uniform scalars (LDS reads land in vector registers).
+            int rec[kItemInts];
+#pragma unroll
+            for (int i = 0; i < kItemInts; ++i) rec[i] = __builtin_amdgcn_readfirstlane(s_rec[i]);
+            nxt = geometry(nxt_idx, item_from_record(rec, true, a.Tq, a.Tk));
+        }
+        if (nx_ok) first_stage(nxt);
+        int popped = 0;  // the item after the next one (returns during the turnaround)
+        if (tid == 0) popped = atomicAdd(&a.k_counters[kCtrPop], 1);
+
+        // Whole rows out through a wave-private region of the second set of stage
+        // arrays (P waves) or of the dS hand-over array (dS waves): dV from the P waves,
+        // dK (times scale) from the dS waves.
         const float sc = pw ? 1.0f : a.scale;
         GT* const dst = (GT*)(pw ? a.dv : a.dk);
         if constexpr (sizeof(GT) == 2) {
             using RT = RowTurn<D>;
             static_assert(2 * RT::BYTES == C::STile::BYTES, "two regions per stage array");
-            char* const buf = wave < 2 ? lds_q0 : wave < 4 ? lds_o0 : wave < 6 ? lds_q1 : lds_o1;
-            char* const wreg = buf + (wave & 1) * RT::BYTES;
-            RT::put_acc(wreg, acc, sc, lane);
-            RT::store((bf16*)dst + (ko + kw0) * rs + (int64_t)h * D, rs, Lk - kw0, wreg, lane);
-        } else if (key_ok) {
-            GT* d = dst + (ko + my_key) * rs + (int64_t)h * D + 4 * grp;
+            static_assert(4 * RT::BYTES == sizeof(xch), "four regions in the hand-over array");
+            char* const wreg = pw ? (wave < 2 ? lds_q1 : lds_o1) + (wave & 1) * RT::BYTES
+                                  : (char*)&xch[0][0][0][0] + (wave - 4) * RT::BYTES;
+            RT::put_acc(wreg, acc, sc, ln);
+            if (nx_ok) load_bf(nxt, ln);
+            RT::store((bf16*)dst + (ko + kw0) * rs + (int64_t)h * D, rs, Lk - kw0, wreg, ln);
+        } else {
+            if (key_ok) {
+                GT* d = dst + (ko + my_key) * rs + (int64_t)h * D + 4 * grp;
 #pragma unroll
-            for (int i = 0; i < C::ND; ++i)
+                for (int i = 0; i < C::ND; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    store4<GT>(d + 32 * i + 8 * j, acc[i][4 * j] * sc, acc[i][4 * j + 1] * sc,
-                               acc[i][4 * j + 2] * sc, acc[i][4 * j + 3] * sc);
+                    for (int j = 0; j < 4; ++j)
+                        store4<GT>(d + 32 * i + 8 * j, acc[i][4 * j] * sc, acc[i][4 * j + 1] * sc,
+                                   acc[i][4 * j + 2] * sc, acc[i][4 * j + 3] * sc);
+            }
+            if (nx_ok) load_bf(nxt, ln);
         }
+        if (tid == 0) s_pop[it_n & 1] = popped;
+        // The turnaround regions are read back and the pop is in LDS before any wave
+        // moves on (the next item's first barrier then waits for its loads).
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        cur_idx = nxt_idx;
+        nxt_idx = __builtin_amdgcn_readfirstlane(s_pop[it_n & 1]);
+        cur = nxt;
     }
 #else
     (void)a;

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
         lds_barrier();  // s_item is read by every wave before it is rewritten
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
-        const ItemSeq is = load_item(a.items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const ItemSeq is = load_item(a.items, pair, false, a.Tq, a.Tk);
         const int64_t qo = is.qo, ko = is.ko;
         const int Lq = is.Lq, Lk = is.Lk;
         const char* Kseq = Kg + (ko * rs + (int64_t)h * D) * C::ESZ;

@@ -15,6 +15,11 @@ constexpr int kSchedBins = 512;
 // Slots of the counter block at the start of every workspace.
 enum { kCtrTotal = 0, kCtrPop = 1, kCtrPairs = 2, kCtrCount = 16 };
 
+// One work item of a scheduled list: {sequence b, tile t, row_off[b], row_off[b+1],
+// col_off[b], col_off[b+1], 0, 0}. Carrying the sequence's offsets lets a kernel
+// read everything it needs about an item in one 32-byte load.
+constexpr int kItemInts = 8;
+
 struct SchedArgs {
     const int32_t* row_off;  // [B+1] offsets of the tiled dimension
     const int32_t* col_off;  // [B+1] offsets of the visited dimension
@@ -24,7 +29,7 @@ struct SchedArgs {
     int32_t bsh;             // block shift of the block-diagonal mask (kNoBlock: none)
     int64_t max_pairs;       // capacity of items; a larger enumeration schedules nothing
     int32_t* tbase;          // [B+1] scratch: first flat tile of each sequence
-    int32_t* items;          // [2 * max_pairs] (sequence, tile) pairs
+    int32_t* items;          // [kItemInts * max_pairs] item records
     int32_t* counters;       // kCtrCount ints
 };
 

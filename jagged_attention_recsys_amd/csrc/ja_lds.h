@@ -13,6 +13,7 @@
 #pragma once
 
 #include "ja_common.h"
+#include "ja_internal.h"
 #include "ja_tiles.h"
 
 namespace ja {
@@ -71,6 +72,16 @@ struct Tile {
             }
         }
     }
+
+    // Row-operand offsets in one register (bf16, 256-byte rows): the lane's offset
+    // for k-step s is rx ^ (s << 5). The swizzle only permutes chunk bits 5-7 of the
+    // row, which the row base leaves clear, so the XOR form equals row_offsets.
+    static __device__ __forceinline__ int row_offset_base(int col, int grp) {
+        static_assert(KP == 8 && CPR == 16, "bf16 rows of 256 bytes");
+        const int r = key_of_arow<KP>(col);
+        return r * ROWB + ((grp ^ swz<CPR, ESZ>(r)) << 4);
+    }
+    static __device__ __forceinline__ int row_offset(int rx, int s) { return rx ^ (s << 5); }
 
     // Transpose-read offsets (bf16) of lane l inside a 16-row step, per 32-dim
     // block and row quad; fp32 tiles read single elements instead.
@@ -147,22 +158,21 @@ struct TileLoader {
     }
 };
 
-// A work item's sequence: the (sequence, tile) pair, then the sequence's four
-// offsets as independent loads (one round trip after the pair's, not four).
-// Rows are clamped to the tensors, so inconsistent offsets cannot reach outside
-// them (the C ABI leaves such offsets undefined otherwise).
+// A work item's sequence, from its record (read with one 32-byte load): for a list
+// tiled over queries the record's row offsets are the query offsets; for a list
+// tiled over keys (transposed) they are the key offsets. Rows are clamped to the
+// tensors, so inconsistent offsets cannot reach outside them (the C ABI leaves
+// such offsets undefined otherwise).
 struct ItemSeq {
     int b, t;        // sequence, tile
     int64_t qo, ko;  // first query / key row of the sequence
     int Lq, Lk;      // its query / key counts
 };
 
-__device__ __forceinline__ ItemSeq load_item(const int32_t* items, int pair, const int32_t* q_off,
-                                             const int32_t* k_off, int Tq, int Tk) {
-    typedef int int2v __attribute__((ext_vector_type(2)));
-    const int2v it = *(const int2v*)(items + 2 * pair);
-    const int q0 = q_off[it[0]], q1 = q_off[it[0] + 1];
-    const int k0 = k_off[it[0]], k1 = k_off[it[0] + 1];
+template <typename R>
+__device__ __forceinline__ ItemSeq item_from_record(const R& it, bool transposed, int Tq, int Tk) {
+    const int q0 = transposed ? it[4] : it[2], q1 = transposed ? it[5] : it[3];
+    const int k0 = transposed ? it[2] : it[4], k1 = transposed ? it[3] : it[5];
     ItemSeq s;
     s.b = it[0];
     s.t = it[1];
@@ -171,6 +181,12 @@ __device__ __forceinline__ ItemSeq load_item(const int32_t* items, int pair, con
     s.Lq = q0 < 0 ? 0 : min(q1, Tq) - q0;
     s.Lk = k0 < 0 ? 0 : min(k1, Tk) - k0;
     return s;
+}
+
+__device__ __forceinline__ ItemSeq load_item(const int32_t* items, int pair, bool transposed, int Tq, int Tk) {
+    typedef int int8v __attribute__((ext_vector_type(8)));
+    const int8v it = *(const int8v*)(items + kItemInts * (int64_t)pair);
+    return item_from_record(it, transposed, Tq, Tk);
 }
 
 // Wave-uniform mask decisions for a block [x0, x0 + n) of the other index, from

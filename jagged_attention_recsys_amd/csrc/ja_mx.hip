@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
         lds_barrier();
         if (idx >= total) break;
         const int pair = idx / a.H, h = idx - pair * a.H;
-        const ItemSeq is = load_item(a.items, pair, a.q_off, a.k_off, a.Tq, a.Tk);
+        const ItemSeq is = load_item(a.items, pair, false, a.Tq, a.Tk);
         const int b = is.b, qt = is.t;
         const int64_t qo = is.qo, ko = is.ko;
         const int Lq = is.Lq, Lk = is.Lk;

@@ -178,8 +178,10 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
         const int pos = base + __popcll(below);
         if (valid && below == 0) cnt[w * kSchedBins + bin] = base + __popcll(mine);
         if (valid) {
-            a.items[2 * pos] = b;
-            a.items[2 * pos + 1] = t;
+            typedef int int4v __attribute__((ext_vector_type(4)));
+            int4v* rec = (int4v*)(a.items + kItemInts * (int64_t)pos);
+            rec[0] = int4v{b, t, ro[b], ro[b + 1]};
+            rec[1] = int4v{co[b], co[b + 1], 0, 0};
         }
     }
 
@@ -195,8 +197,8 @@ __global__ void ja_copy_items_kernel(const int32_t* counters, const int32_t* ite
     const int F = counters[kCtrPairs];
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < F && i < max_items;
          i += (int64_t)gridDim.x * blockDim.x) {
-        out[2 * i] = items[2 * i];
-        out[2 * i + 1] = items[2 * i + 1];
+        out[2 * i] = items[kItemInts * i];
+        out[2 * i + 1] = items[kItemInts * i + 1];
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) *count = F;
 }
