@@ -121,8 +121,8 @@ ja_status_t jagged_attn_fwd(const void* q, const void* k, const void* v,
  * GPU the library runs on holds until the process ends; its address is looked up
  * on the first call with each device current. Calls whose
  * ja_fwd_workspace_size() exceeds that return JA_ERR_SCRATCH before anything is
- * enqueued (8 MiB holds a work list of about a million (sequence, tile) pairs,
- * ceil(Tq / BM) + B of them: some 130 million query tokens at BM = 128, see
+ * enqueued (8 MiB holds a work list of about 260,000 (sequence, tile) items of 32
+ * bytes, ceil(Tq / BM) + B of them: some 33 million query tokens at BM = 128, see
  * ja_fwd_tile_shape). No call allocates or
  * frees anything. All calls on one GPU share the buffer, and each call's contents
  * last until the next one: calls that overlap on one GPU (several streams or host

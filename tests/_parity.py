@@ -192,7 +192,8 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.nda
             lim = BF16_ULP * (t + rv)
             stats["above_2e-2_rounding_limited"] = int((lim > 0.5 * BF16_MAX).sum())
             stats["max_err_over_bound"] = float(np.max(ev / (2.0 * lim + 2e-3)))
-            _record(what, stats, report)
+            if not (np.all(lim > 0.5 * BF16_MAX) and stats["max_err_over_bound"] <= 1.0):
+                _record(what, stats, report)  # the summary shows the failing case too
             assert np.all(lim > 0.5 * BF16_MAX), f"{what}: an element above 2e-2 is not rounding-limited ({stats})"
             assert stats["max_err_over_bound"] <= 1.0, f"{what}: error exceeds the bf16 rounding bound ({stats})"
         stats["max_abs_strict"] = float(np.max(np.where(np.abs(got - ref) > BF16_MAX, 0.0, np.abs(got - ref))[sel]))

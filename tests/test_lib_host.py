@@ -106,7 +106,7 @@ def test_bwd_rejects_host_visible_errors(lib):
 
 
 def test_noalloc_rejects_sizes_beyond_its_buffer(lib):
-    # the fixed 8 MiB buffer holds about a million (sequence, tile) pairs; the check is
+    # the fixed 8 MiB buffer holds about 260,000 (sequence, tile) items; the check is
     # made on the host before the device is touched
     f = lib.jagged_attn_fwd_noalloc
     args = [FAKE, FAKE, FAKE, FAKE, FAKE]
