@@ -234,15 +234,27 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
                 const int kw0 = kt * C::KT + wk * 32 * C::NB;  // first key of this wave's blocks
                 const bool skip = wave_skips(vis, row_ok, kw0, 32 * C::NB);
                 if (!skip) {
+                    // S^T = K Q^T for the wave's blocks, the blocks' chains interleaved and
+                    // each K fragment read three products ahead of its use (the scheduling
+                    // barriers keep the reads from sinking next to their products, which
+                    // would expose the LDS latency on every product).
                     floatx16 sacc[C::NB];
 #pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb) {
-                        sacc[nb] = floatx16{};
-                        const char* kblk = kl + (wk * C::NB + nb) * 32 * C::ROWB;
+                    for (int nb = 0; nb < C::NB; ++nb) sacc[nb] = floatx16{};
+                    constexpr int NSI = C::NB * C::NS;
+                    auto kread = [&](int i) __attribute__((always_inline)) {
+                        return C::KVTile::read_rows(kl + (wk * C::NB + i % C::NB) * 32 * C::ROWB, koff[i / C::NB]);
+                    };
+                    frag kr[3];
 #pragma unroll
-                        for (int s = 0; s < C::NS; ++s)
-                            sacc[nb] = M::run(C::KVTile::read_rows(kblk, koff[s]), qf[s], sacc[nb]);
+                    for (int i = 0; i < 3 && i < NSI; ++i) kr[i] = kread(i);
+#pragma unroll
+                    for (int i = 0; i < NSI; ++i) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        sacc[i % C::NB] = M::run(kr[i % 3], qf[i / C::NB], sacc[i % C::NB]);
+                        if (i + 3 < NSI) kr[i % 3] = kread(i + 3);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
 
                     const bool need_mask = wave_needs_mask(vis, row_ok, kw0, 32 * C::NB);
                     if (ACT == ACT_SOFTMAX) {
