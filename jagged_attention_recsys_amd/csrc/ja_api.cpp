@@ -292,8 +292,7 @@ ja_status_t bwd_impl(const void* q, const void* k, const void* v, const void* ou
     sk.tbase = reinterpret_cast<int32_t*>(ws + p.off_ktbase);
     sk.items = reinterpret_cast<int32_t*>(ws + p.off_kitems);
     sk.counters = reinterpret_cast<int32_t*>(ws + p.off_kctr);
-    if (launch_sched(sq, s) != hipSuccess) return JA_ERR_HIP;
-    if (launch_sched(sk, s) != hipSuccess) return JA_ERR_HIP;
+    if (launch_sched2(sq, sk, s) != hipSuccess) return JA_ERR_HIP;
 
     BwdArgs ba;
     ba.q = q;

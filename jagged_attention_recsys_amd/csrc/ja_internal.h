@@ -34,6 +34,8 @@ struct SchedArgs {
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
+// Both lists in one launch (one workgroup each; the lists must not share memory).
+hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t stream);
 hipError_t launch_copy_items(const int32_t* counters, const int32_t* items, int32_t* out,
                              int32_t* count, int64_t max_items, hipStream_t stream);
 

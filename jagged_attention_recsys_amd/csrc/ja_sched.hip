@@ -25,6 +25,9 @@ constexpr int kWaves = kThreads / 64;
 // offsets in LDS, so the per-tile binary search and length lookups do not wait
 // on global memory; larger batches read them from the workspace and the inputs.
 constexpr int kLdsSeqs = 2048;
+// Enumerations of up to kLdsItems tiles (with the tables in LDS) keep each tile's
+// sequence and bin from the histogram pass for the scatter pass.
+constexpr int kLdsItems = 8192;
 
 // Inclusive scan of one int per thread over the whole workgroup. `tmp` holds
 // kWaves+1 ints of LDS. Returns the inclusive prefix; *total gets the sum.
@@ -65,8 +68,17 @@ __device__ int find_seq(const int32_t* tbase, int B, int f) {
     return lo;
 }
 
-__global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
+// Two lists (the backward's query-tile and key-tile lists) are built by one launch,
+// one workgroup each; a single list uses one workgroup.
+struct SchedPair {
+    SchedArgs l[2];
+};
+
+__global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedPair lists) {
+    const SchedArgs& a = lists.l[blockIdx.x];
     __shared__ int cnt[kWaves * kSchedBins];  // [wave][bin] counts, then offsets
+    __shared__ int16_t s_seq[kLdsItems];      // per tile: its sequence and bin (cached lists)
+    __shared__ int16_t s_bin[kLdsItems];
     __shared__ int tmp[kWaves + 1];
     __shared__ int32_t s_tbase[kLdsSeqs + 1];
     __shared__ int32_t s_row[kLdsSeqs + 1];
@@ -101,6 +113,11 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
     // An enumeration larger than the item buffer (offsets inconsistent with the
     // sizes the host was given) schedules nothing rather than writing past it.
     const int F = (int64_t)carry <= a.max_pairs ? carry : 0;
+    const bool cached = in_lds && F <= kLdsItems;
+    // Column tiles are a power of two wide in every list the library builds: costs then
+    // take shifts, not 64-bit divisions (the general form stays for any other width).
+    const bool pow2 = (a.bn & (a.bn - 1)) == 0;
+    const int lbn = pow2 ? __builtin_ctz(a.bn) : 0;
     for (int i = tid; i < kWaves * kSchedBins; i += kThreads) cnt[i] = 0;
     __threadfence_block();
     __syncthreads();
@@ -115,7 +132,12 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
         const int64_t Lr = (int64_t)ro[b + 1] - ro[b];
         const int64_t Lc = (int64_t)co[b + 1] - co[b];
         const ColRange cr = visible_cols(Lr, Lc, (int64_t)t * a.bm, a.bm, a.causal, a.window, a.transposed, a.bsh);
-        const int cost = tile_cost(cr, a.bn);
+        int cost;
+        if (pow2)  // 0 <= lo < hi <= Lc < 2^31: the same count as tile_cost
+            cost = cr.hi <= cr.lo ? 0
+                                  : (int)(((uint64_t)cr.hi + a.bn - 1) >> lbn) - (int)((uint64_t)cr.lo >> lbn);
+        else
+            cost = tile_cost(cr, a.bn);
         *pb = b;
         *pt = t;
         return cost < kSchedBins - 1 ? cost : kSchedBins - 1;
@@ -126,6 +148,10 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
         int b, t;
         const int bin = bin_of(f, &b, &t);
         atomicAdd(&cnt[w * kSchedBins + bin], 1);
+        if (cached) {
+            s_seq[f] = (int16_t)b;
+            s_bin[f] = (int16_t)bin;
+        }
     }
     __syncthreads();
 
@@ -160,7 +186,15 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedArgs a) {
         const int f = f0 + lane;
         const bool valid = f < f_hi;
         int b = 0, t = 0, bin = -1;
-        if (valid) bin = bin_of(f, &b, &t);
+        if (valid) {
+            if (cached) {  // written by this lane in phase 1 (same wave, same f)
+                b = s_seq[f];
+                bin = s_bin[f];
+                t = f - tb[b];
+            } else {
+                bin = bin_of(f, &b, &t);
+            }
+        }
         // Every lane reads its bin's next free position, learns which lanes share
         // its bin (a register-only loop over the distinct bins of the chunk), and
         // the lowest such lane advances the bin's position by their count.
@@ -206,7 +240,18 @@ __global__ void ja_copy_items_kernel(const int32_t* counters, const int32_t* ite
 }  // namespace
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(ja_sched_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+    SchedPair p;
+    p.l[0] = a;
+    p.l[1] = a;
+    hipLaunchKernelGGL(ja_sched_kernel, dim3(1), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t stream) {
+    SchedPair p;
+    p.l[0] = a;
+    p.l[1] = b;
+    hipLaunchKernelGGL(ja_sched_kernel, dim3(2), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -65,9 +65,14 @@ hipError_t launch_sched(const SchedArgs& a, hipStream_t) {
     ++g_launches;
     region(a.counters, sizeof(int32_t) * kCtrCount, "scheduler counters outside the workspace");
     region(a.tbase, sizeof(int32_t) * ((size_t)a.B + 1), "tile prefix outside the workspace");
-    region(a.items, sizeof(int32_t) * 2 * (size_t)a.max_pairs, "work list outside the workspace");
+    region(a.items, sizeof(int32_t) * kItemInts * (size_t)a.max_pairs, "work list outside the workspace");
     if (a.bm <= 0 || a.bn <= 0 || a.max_pairs < 0) fail("scheduler shape");
     return hipSuccess;
+}
+hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s) {
+    --g_launches;  // one launch for both lists
+    launch_sched(a, s);
+    return launch_sched(b, s);
 }
 hipError_t launch_copy_items(const int32_t*, const int32_t*, int32_t*, int32_t*, int64_t, hipStream_t) {
     ++g_launches;
