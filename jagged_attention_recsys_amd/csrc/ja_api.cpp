@@ -77,7 +77,7 @@ ja_status_t plan_fwd(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, in
 struct BwdPlan {
     int rows, cols;                     // rows per item, columns per stage
     int64_t max_q_pairs, max_k_pairs;
-    size_t off_qctr, off_kctr, off_qtbase, off_ktbase, off_qitems, off_kitems, off_di, bytes;
+    size_t off_qctr, off_kctr, off_qtbase, off_ktbase, off_qitems, off_kitems, off_di, off_nl2, bytes;
 };
 
 ja_status_t plan_bwd(int32_t B, int32_t H, int64_t Tq, int64_t Tk, BwdPlan* p) {
@@ -95,6 +95,7 @@ ja_status_t plan_bwd(int32_t B, int32_t H, int64_t Tq, int64_t Tk, BwdPlan* p) {
     p->off_qitems = o; o = align_up(o + sizeof(int32_t) * kItemInts * (size_t)p->max_q_pairs);
     p->off_kitems = o; o = align_up(o + sizeof(int32_t) * kItemInts * (size_t)p->max_k_pairs);
     p->off_di = o; o = align_up(o + sizeof(float) * (size_t)Tq * (size_t)H);
+    p->off_nl2 = o; o = align_up(o + sizeof(float) * (size_t)Tq * (size_t)H);
     p->bytes = o;
     return JA_OK;
 }
@@ -305,6 +306,7 @@ ja_status_t bwd_impl(const void* q, const void* k, const void* v, const void* ou
     ba.dk = dk;
     ba.dv = dv;
     ba.di = reinterpret_cast<float*>(ws + p.off_di);
+    ba.nl2 = reinterpret_cast<float*>(ws + p.off_nl2);
     ba.q_off = q_offsets;
     ba.k_off = k_offsets;
     ba.q_items = sq.items;

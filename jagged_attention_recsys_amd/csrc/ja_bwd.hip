@@ -21,7 +21,7 @@
 // read through LDS transpose reads.
 //
 // dK/dV pass: 4 waves, a 128-key tile, wave w owns 32 keys (K and V held as B
-// operands). For each 64-query stage (Q, dO, lse and Di streamed into LDS):
+// operands). For each 64-query stage (Q, dO, -lse log2(e) and Di streamed into LDS):
 // S = Q K^T and dP = dO V^T give lane-per-key C tiles; dV^T += dO^T P and
 // dK^T += Q^T dS use transpose reads of dO and Q. Query tiles no key of the item
 // can see (causal diagonal, window) are never loaded.
@@ -152,7 +152,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
         if constexpr (ACT == ACT_SOFTMAX) {
             di = halves_sum(di);
             nlse2 = row_ok ? -a.lse[(qo + my_row) * a.H + h] * kLog2e : 0.0f;
-            if (row_ok && grp == 0) a.di[(qo + my_row) * a.H + h] = di;
+            if (row_ok && grp == 0) {
+                a.di[(qo + my_row) * a.H + h] = di;
+                a.nl2[(qo + my_row) * a.H + h] = nlse2;  // the dK/dV pass's exponent offsets
+            }
         }
         const float inv_lk = Lk > 0 ? 1.0f / (float)Lk : 0.0f;
 
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 
         const char* Qseq = (const char*)a.q + (qo * rs + (int64_t)h * D) * (int)sizeof(T);
         const char* Oseq = (const char*)a.dout + (qo * rs + (int64_t)h * D) * (int)sizeof(T);
-        const char* Lseq = (const char*)(a.lse + qo * a.H + h);
+        const char* Lseq = (const char*)(a.nl2 + qo * a.H + h);
         const char* Dseq = (const char*)(a.di + qo * a.H + h);
         auto issue = [&](int qs, char* qdst, char* odst, float* ldst, float* ddst) {
             const int qbase = qs * kBwdStage;
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
             const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * rsb);
             ld.issue(Qseq + (int64_t)qbase * rsb, nrec, qdst, wave);
             ld.issue(Oseq + (int64_t)qbase * rsb, nrec, odst, wave);
-            // lse and Di of the stage's queries: one 64-lane dword load each.
+            // -lse log2(e) and Di of the stage's queries: one 64-lane dword load each.
             if (ACT == ACT_SOFTMAX && wave < 2) {
                 const uint32_t nrec_s = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * hsb);
                 const char* src = (wave == 0 ? Lseq : Dseq) + (int64_t)qbase * hsb;
@@ -477,7 +480,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
                 for (int r = 0; r < 16; ++r) {
                     float p, g;
                     if constexpr (ACT == ACT_SOFTMAX) {
-                        p = fast_exp2(fmaf(sacc[r], c_exp, -lse_r[r] * kLog2e));
+                        p = fast_exp2(fmaf(sacc[r], c_exp, lse_r[r]));
                         g = p * (dpacc[r] - di_r[r]);
                     } else {
                         float act, dact;
@@ -662,7 +665,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
         it.qs_hi = cr.hi > cr.lo ? (int)((cr.hi + kBwdStage - 1) / kBwdStage) : 0;
         return it;
     };
-    // Query stage qs of an item (Q, dO rows; lse, Di for softmax) into one set of stage arrays.
+    // Query stage qs of an item (Q, dO rows; -lse log2(e), Di for softmax) into one set of stage arrays.
     auto issue = [&](const Item& it, int qs, char* qdst, char* odst, float* ldst, float* ddst) {
         const int qbase = qs * kBwdStage;
         const int nvalid = min(max(it.Lq - qbase, 0), kBwdStage);
@@ -672,7 +675,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
         ld.issue((const char*)a.dout + row0 * (int)sizeof(T), nrec, odst, wave);
         if (ACT == ACT_SOFTMAX && wave < 2) {
             const uint32_t nrec_s = __builtin_amdgcn_readfirstlane((uint32_t)nvalid * hsb);
-            const float* src = (wave == 0 ? a.lse : a.di) + (int64_t)(it.qo + qbase) * a.H + it.h;
+            const float* src = (wave == 0 ? a.nl2 : a.di) + (int64_t)(it.qo + qbase) * a.H + it.h;
             const __amdgpu_buffer_rsrc_t r =
                 __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, (int)nrec_s, 0x00020000);
             lds_char* dst = (lds_char*)(wave == 0 ? ldst : ddst);
@@ -692,7 +695,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
     auto first_stage = [&](const Item& it) __attribute__((always_inline)) {
         if (!kSingleStage && it.qs_hi > it.qs_lo) issue(it, it.qs_lo, lds_q0, lds_o0, lds_l0, lds_d0);
     };
-    // Four consecutive fp32 values of lse (or Di) for register run r of block nb.
+    // Four consecutive fp32 values of -lse log2(e) (or Di) for register run r of block nb.
     auto run4 = [&](const float* base, int nb, int r) __attribute__((always_inline)) {
         return *(const floatx4*)(base + nb * 32 + key_of_reg<KP>(grp, r));
     };
@@ -786,7 +789,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
                     for (int r = 0; r < 16; ++r) {
                         float p, f;
                         if constexpr (ACT == ACT_SOFTMAX) {
-                            p = fast_exp2(fmaf(c[r], c_exp, -l4[r >> 2][r & 3] * kLog2e));
+                            p = fast_exp2(fmaf(c[r], c_exp, l4[r >> 2][r & 3]));
                             f = p;
                         } else {
                             float av, dav;

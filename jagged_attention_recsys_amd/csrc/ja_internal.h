@@ -84,6 +84,7 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* di;                 // workspace [Tq, H]: rowsum(dO * O), written by the dQ pass
+    float* nl2;                // workspace [Tq, H]: -lse * log2(e), written by the dQ pass (softmax)
     const int32_t* q_off;
     const int32_t* k_off;
     const int32_t* q_items;    // (sequence, query tile) pairs

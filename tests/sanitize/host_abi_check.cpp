@@ -89,6 +89,7 @@ int bwd_cols_per_stage() { return 64; }
 hipError_t launch_bwd(const BwdArgs& a, int, int, int gq, int gk, hipStream_t, hipEvent_t, hipEvent_t, hipEvent_t) {
     ++g_launches;
     region(a.di, sizeof(float) * (size_t)a.Tq * (size_t)a.H, "Di outside the workspace");
+    region(a.nl2, sizeof(float) * (size_t)a.Tq * (size_t)a.H, "exponent offsets outside the workspace");
     if (gq < 1 || gk < 1) fail("backward launch shape");
     return hipSuccess;
 }
