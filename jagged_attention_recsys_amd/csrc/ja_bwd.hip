@@ -85,9 +85,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
     typename C::Loader ld;
     ld.init(wave, lane, rsb);
 
+    __shared__ int s_xq[2];
+    int pend = 0;  // thread 0's pop in flight, sent before the previous item's output
+    if (tid == 0) {
+        xq_init(s_xq, a.window > 0);
+        pend = xq_issue(a.q_counters, s_xq);
+    }
     for (;;) {
         __syncthreads();
-        if (tid == 0) s_item = atomicAdd(&a.q_counters[kCtrPop], 1);
+        if (tid == 0) s_item = xq_resolve(a.q_counters, s_xq, pend, total);
         __syncthreads();
         const int idx = __builtin_amdgcn_readfirstlane(s_item);
         if (idx >= total) break;
@@ -264,6 +270,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ja_bwd_dq_kernel(BwdArgs a) {
             }
         }
 
+        if (tid == 0) pend = xq_issue(a.q_counters, s_xq);
         if constexpr (KP == 8 && sizeof(GT) == 2) {
             // Whole rows out through the wave's region (the stage loop ended on a
             // barrier, or loaded nothing).
@@ -329,9 +336,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     typename C::Loader ld;
     ld.init(wave, lane, rsb);
 
+    __shared__ int s_xq[2];
+    int pend = 0;  // thread 0's pop in flight, sent before the previous item's output
+    if (tid == 0) {
+        xq_init(s_xq, a.window > 0);
+        pend = xq_issue(a.k_counters, s_xq);
+    }
     for (;;) {
         __syncthreads();
-        if (tid == 0) s_item = atomicAdd(&a.k_counters[kCtrPop], 1);
+        if (tid == 0) s_item = xq_resolve(a.k_counters, s_xq, pend, total);
         __syncthreads();
         const int idx = __builtin_amdgcn_readfirstlane(s_item);
         if (idx >= total) break;
@@ -559,6 +572,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
             }
             __syncthreads();  // the partial sums are read before the row turnarounds reuse the buffers
         }
+        if (tid == 0) pend = xq_issue(a.k_counters, s_xq);
         const bool owner = !pair_split || wave < 2;  // writes its keys' dK, dV
         if (!owner) {
         } else if constexpr (KP == 8 && sizeof(GT) == 2) {
@@ -706,9 +720,12 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
     // (their latency overlaps the output turnaround instead of following it).
     __shared__ int s_pop[2];
     __shared__ __attribute__((aligned(32))) int s_rec[kItemInts];
+    __shared__ int s_xq[2];
+    int pend = 0;  // thread 0's pop in flight
     if (tid == 0) {
-        s_pop[0] = atomicAdd(&a.k_counters[kCtrPop], 1);
-        s_pop[1] = atomicAdd(&a.k_counters[kCtrPop], 1);
+        xq_init(s_xq, a.window > 0);
+        s_pop[0] = xq_resolve(a.k_counters, s_xq, xq_issue(a.k_counters, s_xq), total);
+        s_pop[1] = xq_resolve(a.k_counters, s_xq, xq_issue(a.k_counters, s_xq), total);
     }
     __syncthreads();
     int cur_idx = __builtin_amdgcn_readfirstlane(s_pop[0]);
@@ -924,8 +941,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
             nxt = geometry(nxt_idx, item_from_record(rec, true, a.Tq, a.Tk));
         }
         if (nx_ok) first_stage(nxt);
-        int popped = 0;  // the item after the next one (returns during the turnaround)
-        if (tid == 0) popped = atomicAdd(&a.k_counters[kCtrPop], 1);
+        if (tid == 0) pend = xq_issue(a.k_counters, s_xq);  // the item after the next one (returns during the turnaround)
 
         // Whole rows out through a wave-private region of the second set of stage
         // arrays (P waves) or of the dS hand-over array (dS waves): dV from the P waves,
@@ -953,7 +969,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
             }
             if (nx_ok) load_bf(nxt, ln);
         }
-        if (tid == 0) s_pop[it_n & 1] = popped;
+        if (tid == 0) s_pop[it_n & 1] = xq_resolve(a.k_counters, s_xq, pend, total);
         // The turnaround regions are read back and the pop is in LDS before any wave
         // moves on (the next item's first barrier then waits for its loads).
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");

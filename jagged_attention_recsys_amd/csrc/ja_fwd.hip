@@ -42,6 +42,8 @@
 // it by more than 2^8, which leaves the result unchanged in exact arithmetic.
 #include <math.h>
 
+#include <type_traits>
+
 #include "ja_common.h"
 #include "ja_internal.h"
 #include "ja_lds.h"
@@ -81,8 +83,10 @@ struct FwdCfg {
     static_assert(D % (2 * KP) == 0 && D % 32 == 0, "unsupported head dim");
 };
 
-template <typename T, int D, int ACT, bool SPLIT, int CHUNK, int NTHREADS = FwdCfg<T, D, SPLIT>::THREADS,
-          int MINB = FwdCfg<T, D, SPLIT>::MIN_BLOCKS>
+// XQ: pop from XCD-local work queues (built only for the sliding-window case they help;
+// a separate instantiation, so the other kernels keep their registers).
+template <typename T, int D, int ACT, bool SPLIT, int CHUNK, bool XQ = false,
+          int NTHREADS = FwdCfg<T, D, SPLIT>::THREADS, int MINB = FwdCfg<T, D, SPLIT>::MIN_BLOCKS>
 __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
     // The body uses gfx950-only types and builtins; the host pass only needs the
     // kernel's signature for its launch stub.
@@ -142,10 +146,14 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
     auto lds_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
-    int next = 0;
-    if (tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
+    __shared__ int s_xq[2];
+    int pend = 0;  // thread 0's pop in flight
+    if (tid == 0) {
+        if constexpr (XQ) xq_init(s_xq, true);
+        pend = XQ ? xq_issue(a.counters, s_xq) : atomicAdd(&a.counters[kCtrPop], 1);
+    }
     for (;;) {
-        if (tid == 0) s_item = next;
+        if (tid == 0) s_item = XQ ? xq_resolve(a.counters, s_xq, pend, total) : pend;
         lds_barrier();
         const int idx = __builtin_amdgcn_readfirstlane(s_item);  // same for every lane
         lds_barrier();  // s_item is read by every wave before it is rewritten
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
                 }
             }
 
-            if (sub == nsub - 1 && tid == 0) next = atomicAdd(&a.counters[kCtrPop], 1);
+            if (sub == nsub - 1 && tid == 0) pend = XQ ? xq_issue(a.counters, s_xq) : atomicAdd(&a.counters[kCtrPop], 1);
 
             // Split layout: merge the key slices (the loop ended on a barrier, or no
             // stage was loaded, so the stage buffers are free). Softmax first agrees on
@@ -458,8 +466,17 @@ template <int LAYOUT> struct LayoutOf {
 template <typename T, int D, int ACT, int LAYOUT>
 hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t stream) {
     using L = LayoutOf<LAYOUT>;
-    hipLaunchKernelGGL((ja_fwd_kernel<T, D, ACT, L::split, L::chunk>), dim3(grid),
-                       dim3(FwdCfg<T, D, L::split>::THREADS), 0, stream, a);
+    // XCD-local queues for bf16, d = 128, standard layout under a sliding window: the
+    // list then orders most tiles by sequence and tile, so an XCD's consecutive tiles
+    // share K / V stages in its L2 (under a plain causal mask the tiles of one cost come
+    // from many sequences, and the single queue measured faster).
+    constexpr bool kXqBuilt = std::is_same<T, bf16>::value && D == 128 && LAYOUT == 0;
+    if (kXqBuilt && a.window > 0)
+        hipLaunchKernelGGL((ja_fwd_kernel<T, D, ACT, L::split, L::chunk, kXqBuilt>), dim3(grid),
+                           dim3(FwdCfg<T, D, L::split>::THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((ja_fwd_kernel<T, D, ACT, L::split, L::chunk>), dim3(grid),
+                           dim3(FwdCfg<T, D, L::split>::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -13,7 +13,10 @@ namespace ja {
 constexpr int kSchedBins = 512;
 
 // Slots of the counter block at the start of every workspace.
-enum { kCtrTotal = 0, kCtrPop = 1, kCtrPairs = 2, kCtrCount = 16 };
+// Work-list counters: total items, the single pop counter, list length, and eight
+// per-XCD pop counters (64 bytes apart) for kernels that pop from XCD-local queues.
+enum { kCtrTotal = 0, kCtrPop = 1, kCtrPairs = 2, kCtrQueue = 16, kCtrQueueStride = 16, kXcds = 8,
+       kCtrCount = kCtrQueue + kXcds * kCtrQueueStride };
 
 // One work item of a scheduled list: {sequence b, tile t, row_off[b], row_off[b+1],
 // col_off[b], col_off[b+1], 0, 0}. Carrying the sequence's offsets lets a kernel

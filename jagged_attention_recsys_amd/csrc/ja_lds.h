@@ -189,6 +189,60 @@ __device__ __forceinline__ ItemSeq load_item(const int32_t* items, int pair, boo
     return item_from_record(it, transposed, Tq, Tk);
 }
 
+// Work queues over a longest-first list of `total` items, either one for the whole grid
+// or XCD-local: for XCD-local queues, queue q holds the
+// items 8k + q in order, so each queue is itself longest-first and the queues are
+// balanced. A workgroup pops from the queue of the XCD it runs on, and once that queue
+// is empty from another queue that still holds items; every item is handed out
+// exactly once. All tiles of one (sequence, head) at H = 8 (every other tile at H = 4)
+// then run on one XCD, whose L2 keeps the K / V stages they share. Thread 0 of a
+// workgroup does the popping: the queue it pops from and whether all queues are empty
+// live in two ints of LDS (`st`), and only the pending pop's return value is held in a
+// register, so a pop can be sent well before its result is needed.
+__device__ __forceinline__ int xcd_id() {
+    int x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return x & (kXcds - 1);
+}
+// local = false: one queue for the whole grid (the list's own counter).
+__device__ __forceinline__ void xq_init(int* st, bool local) {
+    st[0] = local ? xcd_id() : -1;  // current queue (-1: the single queue)
+    st[1] = 0;                      // set once every queue was found empty
+}
+// Sends a pop to the current queue; the returned value goes to xq_resolve.
+__device__ __forceinline__ int xq_issue(int32_t* counters, const int* st) {
+    const int q = st[0];
+    return atomicAdd(q < 0 ? &counters[kCtrPop] : &counters[kCtrQueue + q * kCtrQueueStride], 1);
+}
+// The popped item, or total once every queue is empty. When the current queue runs dry,
+// the other queues' counters are read together (one round trip, not one per queue) and
+// the first that still holds items is popped; a workgroup that finds them all empty is
+// done.
+__device__ __forceinline__ int xq_resolve(int32_t* counters, int* st, int pend, int total) {
+    const int cur = st[0];
+    if (cur < 0) return pend < total ? pend : total;
+    if ((int64_t)kXcds * pend + cur < total) return kXcds * pend + cur;
+    if (st[1]) return total;  // every queue was found empty before
+    int32_t* ctr = counters + kCtrQueue;
+    int seen[kXcds];
+#pragma unroll
+    for (int q = 0; q < kXcds; ++q) seen[q] = atomicAdd(&ctr[q * kCtrQueueStride], 0);
+#pragma unroll
+    for (int i = 1; i < kXcds; ++i) {
+        const int q = (cur + i) & (kXcds - 1);
+        const int len = (total - q + kXcds - 1) / kXcds;  // items 8k + q below total
+        if (seen[q] < len) {
+            const int k = atomicAdd(&ctr[q * kCtrQueueStride], 1);
+            if (k < len) {
+                st[0] = q;
+                return kXcds * k + q;
+            }
+        }
+    }
+    st[1] = 1;
+    return total;
+}
+
 // Wave-uniform mask decisions for a block [x0, x0 + n) of the other index, from
 // every lane's visible range; lanes with lane_ok false (rows past the sequence
 // end, never written) take no part.

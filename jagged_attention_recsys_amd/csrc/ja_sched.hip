@@ -224,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void ja_sched_kernel(SchedPair lists) {
         a.counters[kCtrPop] = 0;
         a.counters[kCtrPairs] = F;
     }
+    if (tid < kXcds) a.counters[kCtrQueue + tid * kCtrQueueStride] = 0;
 }
 
 __global__ void ja_copy_items_kernel(const int32_t* counters, const int32_t* items, int32_t* out,
