@@ -264,6 +264,20 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
                     }
                     __builtin_amdgcn_sched_barrier(0);
 
+                    // V^T fragments of O^T += V^T P^T, read ahead: the first RV before the
+                    // weights (whose vector work hides their LDS latency), each later one RV
+                    // products before its use. Left to itself the compiler reads each
+                    // fragment next to its product and waits for it every time.
+                    constexpr int NPV = C::NB * C::NT * C::ND, RV = 4;
+                    auto vread = [&](int i) __attribute__((always_inline)) {
+                        const int nb = i / (C::NT * C::ND), t = (i / C::ND) % C::NT, db = i % C::ND;
+                        return C::KVTile::read_tr(vl + (wk * C::NB + nb) * 32 * C::ROWB, t, voff, db);
+                    };
+                    frag vr[RV];
+#pragma unroll
+                    for (int i = 0; i < RV; ++i) vr[i] = vread(i);
+                    __builtin_amdgcn_sched_barrier(0);
+
                     const bool need_mask = wave_needs_mask(vis, row_ok, kw0, 32 * C::NB);
                     if (ACT == ACT_SOFTMAX) {
                         if (prescale) {
@@ -327,14 +341,13 @@ __global__ __launch_bounds__(NTHREADS, MINB) void ja_fwd_kernel(FwdArgs a) {
 #pragma unroll
                         for (int t = 0; t < C::NT; ++t) pf[nb][t] = to_frag<T>(sacc[nb], KP * t);
 #pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb) {
-                        const char* vblk = vl + (wk * C::NB + nb) * 32 * C::ROWB;
-#pragma unroll
-                        for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-                            for (int db = 0; db < C::ND; ++db)
-                                oacc[db] = M::run(C::KVTile::read_tr(vblk, t, voff, db), pf[nb][t], oacc[db]);
+                    for (int i = 0; i < NPV; ++i) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        const int nb = i / (C::NT * C::ND), t = (i / C::ND) % C::NT, db = i % C::ND;
+                        oacc[db] = M::run(vr[i % RV], pf[nb][t], oacc[db]);
+                        if (i + RV < NPV) vr[i % RV] = vread(i + RV);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             };
             auto stage = [&](int kt, const char* kl, const char* vl, char* kn, char* vn) {

@@ -335,18 +335,43 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
             const int kw0 = kt * kMxKT;
             const bool skip = wave_skips(vis, row_ok, kw0, kMxKT);
             if (!skip) {
+                // Matrix operands are read from LDS ahead of their products (K two
+                // products ahead; V's first two before the weights, whose vector work
+                // hides their latency): left to itself the compiler reads each operand
+                // next to its product and waits for it every time.
+                constexpr int NSK = kMxNKB * 2, RK = 2, NPV = kMxNKH * 4, RV = 2;
+                auto kread = [&](int i) __attribute__((always_inline)) {
+                    return read_k(kl + (i >> 1) * 32 * kMxRowB, koff[i & 1][0], koff[i & 1][1]);
+                };
+                auto vread = [&](int i) __attribute__((always_inline)) {
+                    const char* vh = vl + (i >> 2) * 64 * kMxRowB;
+                    const int db = i & 3;
+                    const i32x4 t01 = __builtin_shufflevector(read_tr8(vh + toff[db][0]), read_tr8(vh + toff[db][1]),
+                                                              0, 1, 2, 3);
+                    const i32x4 t23 = __builtin_shufflevector(read_tr8(vh + toff[db][2]), read_tr8(vh + toff[db][3]),
+                                                              0, 1, 2, 3);
+                    return (v8i)__builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
+                };
                 floatx16 sacc[kMxNKB];
 #pragma unroll
-                for (int nb = 0; nb < kMxNKB; ++nb) {
-                    sacc[nb] = floatx16{};
-                    const char* kblk = kl + nb * 32 * kMxRowB;
+                for (int nb = 0; nb < kMxNKB; ++nb) sacc[nb] = floatx16{};
+                v8i kr[RK];
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        const int ksb = (int)((ksc[nb] >> (8 * (2 * c + g))) & 0xff);
-                        sacc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            read_k(kblk, koff[c][0], koff[c][1]), qf[c], sacc[nb], 0, 0, 0, ksb, 0, qsc[c]);
-                    }
+                for (int i = 0; i < RK; ++i) kr[i] = kread(i);
+#pragma unroll
+                for (int i = 0; i < NSK; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int nb = i >> 1, c = i & 1;
+                    const int ksb = (int)((ksc[nb] >> (8 * (2 * c + g))) & 0xff);
+                    sacc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[i % RK], qf[c], sacc[nb], 0, 0, 0,
+                                                                               ksb, 0, qsc[c]);
+                    if (i + RK < NSK) kr[i % RK] = kread(i + RK);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                v8i vr[RV];
+#pragma unroll
+                for (int i = 0; i < RV; ++i) vr[i] = vread(i);
+                __builtin_amdgcn_sched_barrier(0);
                 // Wave-uniform branches around whole loops (not a select per score).
                 if (prescale) {
 #pragma unroll
@@ -396,20 +421,15 @@ __global__ __launch_bounds__(kMxThreads, 2) void ja_mx_fwd_kernel(MxFwdArgs a) {
                     }
                 l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 #pragma unroll
-                for (int kh = 0; kh < kMxNKH; ++kh) {
-                    const char* vh = vl + kh * 64 * kMxRowB;
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        const i32x4 t01 = __builtin_shufflevector(read_tr8(vh + toff[db][0]),
-                                                                  read_tr8(vh + toff[db][1]), 0, 1, 2, 3);
-                        const i32x4 t23 = __builtin_shufflevector(read_tr8(vh + toff[db][2]),
-                                                                  read_tr8(vh + toff[db][3]), 0, 1, 2, 3);
-                        const v8i va = __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
-                        const int vsb = (int)((vsc[kh] >> (8 * db)) & 0xff);
-                        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf[kh], oacc[db], 0, 0, 0, vsb,
-                                                                                    0, kPScale);
-                    }
+                for (int i = 0; i < NPV; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int kh = i >> 2, db = i & 3;
+                    const int vsb = (int)((vsc[kh] >> (8 * db)) & 0xff);
+                    oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr[i % RV], pf[kh], oacc[db], 0, 0, 0,
+                                                                                vsb, 0, kPScale);
+                    if (i + RV < NPV) vr[i % RV] = vread(i + RV);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
         };
