@@ -93,6 +93,15 @@ def test_ragged_cross_lengths(d, causal, window):
     check(case(lq, lk, H=3, d=d, seed=3 * d + window), causal, window, what="cross", bounds=True)
 
 
+@pytest.mark.parametrize("lq,H", [([5], 1), ([130, 7, 300], 3), ([1000], 2), ([64] * 9 + [129], 1)])
+@pytest.mark.parametrize("window", [37, 300])
+def test_window_queues_few_items(lq, H, window):
+    # Both passes pop from per-XCD queues under a window: few items, and item counts
+    # that are not a multiple of eight, exercise empty queues and stealing.
+    check(W.make_case(lq, None, H=H, d=128, dtype=W.BF16, seed=sum(lq) + H + window, with_dout=True), True,
+          window, what=f"queues {len(lq)} seqs", bounds=True)
+
+
 def test_workload5_bwd_every_pair():
     # The whole sliding-window batch (its longest sequences included), every
     # (sequence, head) pair of dQ, dK and dV. With fp32 gradients every element is

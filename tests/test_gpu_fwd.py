@@ -136,6 +136,20 @@ def test_workload1_fp32_softmax_and_silu():
     check_against_oracle(w, "silu", False, 0, what="w1 fwd silu", report=True)
 
 
+# Sliding-window batches (bf16, d = 128) pop from eight per-XCD queues, queue q holding
+# items 8k + q of the list. Few items leave queues empty from the start, and item counts
+# that are not a multiple of eight give queues of different lengths, so workgroups steal
+# from other queues and finish when every queue is empty.
+WINDOW_QUEUE_CASES = [([5], 1), ([130, 7, 300], 3), ([1000], 2), ([64] * 9 + [129], 1), ([2000, 3], 5)]
+
+
+@pytest.mark.parametrize("lq,H", WINDOW_QUEUE_CASES)
+@pytest.mark.parametrize("window", [37, 300])
+def test_window_queues_few_items(lq, H, window):
+    w = W.make_case(lq, None, H=H, d=128, dtype=W.BF16, seed=sum(lq) + H + window)
+    check_against_oracle(w, "softmax", True, window, what=f"queues {len(lq)} seqs", bounds=True)
+
+
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
 def test_full_workloads_every_pair(n):
     # The whole batch, every (sequence, head) pair, element by element, strict.
