@@ -3,7 +3,7 @@
 // code). The kernel launchers are replaced by stubs that launch nothing but check
 // what the layer hands them: every workspace region the plan gives a launch
 // (counters, per-sequence tile prefix, work lists, Di) must lie inside the
-// caller's workspace, and the regions of one call must not overlap. The driver
+// caller's workspace, and the regions of one call must not overlap. main()
 // calls every entry point over a sweep of sizes (empty, one, many and very long
 // sequences, every head dim, dtype, activation and mask) with aligned fake device
 // addresses that are never dereferenced, plus workspaces one byte short.
