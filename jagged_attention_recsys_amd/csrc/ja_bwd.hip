@@ -930,8 +930,9 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
         int ln = lane;
         asm volatile("" : "+v"(ln));
         // Every stage array is free (the last stage ended on a barrier). The next item's
-        // first query stage goes out first, into the first set of stage arrays; its K / V
-        // rows follow once the accumulators are in LDS (their registers are then free).
+        // K / V rows go out first, then its first query stage (into the first set of stage
+        // arrays), then this item's output. (Loaded after the stage loads, the rows made
+        // the compiler wait for those loads before it issued them.)
         Item nxt{};
         if (nx_ok) {
             // The record as wave-uniform scalars (LDS reads land in vector registers).
@@ -940,6 +941,7 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
             for (int i = 0; i < kItemInts; ++i) rec[i] = __builtin_amdgcn_readfirstlane(s_rec[i]);
             nxt = geometry(nxt_idx, item_from_record(rec, true, a.Tq, a.Tk));
         }
+        load_bf(nxt, ln);  // without a next item: zeros, no load
         if (nx_ok) first_stage(nxt);
         if (tid == 0) pend = xq_issue(a.k_counters, s_xq);  // the item after the next one (returns during the turnaround)
 
@@ -955,7 +957,6 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
             char* const wreg = pw ? (wave < 2 ? lds_q1 : lds_o1) + (wave & 1) * RT::BYTES
                                   : (char*)&xch[0][0][0][0] + (wave - 4) * RT::BYTES;
             RT::put_acc(wreg, acc, sc, ln);
-            if (nx_ok) load_bf(nxt, ln);
             RT::store((bf16*)dst + (ko + kw0) * rs + (int64_t)h * D, rs, Lk - kw0, wreg, ln);
         } else {
             if (key_ok) {
@@ -967,7 +968,6 @@ __global__ __launch_bounds__(kKv2Threads, 1) void ja_bwd_dkdv_kernel(BwdArgs a, 
                         store4<GT>(d + 32 * i + 8 * j, acc[i][4 * j] * sc, acc[i][4 * j + 1] * sc,
                                    acc[i][4 * j + 2] * sc, acc[i][4 * j + 3] * sc);
             }
-            if (nx_ok) load_bf(nxt, ln);
         }
         if (tid == 0) s_pop[it_n & 1] = xq_resolve(a.k_counters, s_xq, pend, total);
         // The turnaround regions are read back and the pop is in LDS before any wave
