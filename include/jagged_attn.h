@@ -63,7 +63,8 @@ extern "C" {
 typedef enum {
     JA_OK = 0,
     JA_ERR_INVALID_ARG = 1,     /* null pointer, bad size, window < 0, scale not finite, misalignment */
-    JA_ERR_UNSUPPORTED = 2,     /* d not in {32, 64, 128}, unknown dtype/act, bwd of fp32 */
+    JA_ERR_UNSUPPORTED = 2,     /* d not in {32, 64, 128}, unknown dtype/act, bwd of fp32, Tq or Tk
+                                   above 2^31 - 1, or token rows of more than 2^20 elements (H d) */
     JA_ERR_WORKSPACE = 3,       /* workspace smaller than the matching *_workspace_size() */
     JA_ERR_INVALID_OFFSETS = 4, /* ja_validate_offsets found malformed offsets */
     JA_ERR_HIP = 5,             /* a HIP runtime call or kernel launch failed */

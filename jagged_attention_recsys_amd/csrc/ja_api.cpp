@@ -52,11 +52,15 @@ int fwd_layout(int32_t B, int64_t Tq, int64_t Tk, int32_t dtype) {
     return kLayoutStandard;
 }
 
+// Token rows of at most 2^20 elements (H d): the kernels form 32-bit byte offsets of
+// up to 256 rows (4 bytes per element) inside a stage.
+constexpr int64_t kMaxRowElems = 1 << 20;
+
 ja_status_t check_common(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk, int32_t act,
                          int32_t window, float scale, int32_t dtype) {
     if (B < 0 || H < 1 || Tq < 0 || Tk < 0 || window < 0) return JA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return JA_ERR_INVALID_ARG;
-    if (Tq > INT32_MAX || Tk > INT32_MAX) return JA_ERR_UNSUPPORTED;
+    if (Tq > INT32_MAX || Tk > INT32_MAX || (int64_t)H * d > kMaxRowElems) return JA_ERR_UNSUPPORTED;
     if (!fwd_supported(dtype, d, act)) return JA_ERR_UNSUPPORTED;
     return JA_OK;
 }
@@ -495,6 +499,7 @@ ja_status_t ja_mxfp8_quantize(const void* x, int32_t dtype, const int32_t* offse
                               int64_t T, void* x8, void* scales, int32_t* scale_offsets, void* workspace,
                               size_t workspace_bytes, void* stream) {
     if (B < 0 || H < 1 || T < 0 || d < kMxBlock || d % kMxBlock != 0) return JA_ERR_INVALID_ARG;
+    if ((int64_t)H * d > kMaxRowElems) return JA_ERR_UNSUPPORTED;
     if (dtype != JA_BF16) return JA_ERR_UNSUPPORTED;
     if (T > INT32_MAX) return JA_ERR_UNSUPPORTED;
     if (!offsets || !scale_offsets || (T > 0 && (!x || !x8 || !scales)) || !workspace) return JA_ERR_INVALID_ARG;
@@ -522,6 +527,7 @@ ja_status_t ja_mxfp8_quantize(const void* x, int32_t dtype, const int32_t* offse
 
 size_t ja_fwd_mxfp8_workspace_size(int32_t B, int32_t H, int32_t d, int64_t Tq, int64_t Tk) {
     if (B < 0 || H < 1 || d != kMxD || Tq < 0 || Tk < 0 || Tq > INT32_MAX || Tk > INT32_MAX) return 0;
+    if ((int64_t)H * d > kMaxRowElems) return 0;
     const int64_t max_pairs = (Tq + kMxBM - 1) / kMxBM + B;
     if (max_pairs * (int64_t)H >= INT32_MAX) return 0;
     const size_t off_tbase = align_up(sizeof(int32_t) * kCtrCount);
@@ -537,7 +543,7 @@ ja_status_t jagged_attn_fwd_mxfp8(const void* q8, const void* q_scales, const in
                                   void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || H < 1 || Tq < 0 || Tk < 0 || window < 0 || !std::isfinite(scale)) return JA_ERR_INVALID_ARG;
     if (d != kMxD) return JA_ERR_UNSUPPORTED;
-    if (Tq > INT32_MAX || Tk > INT32_MAX) return JA_ERR_UNSUPPORTED;
+    if (Tq > INT32_MAX || Tk > INT32_MAX || (int64_t)H * d > kMaxRowElems) return JA_ERR_UNSUPPORTED;
     if (B == 0 || Tq == 0) return JA_OK;
     if (!q8 || !q_scales || !q_scale_offsets || !out || !q_offsets || !k_offsets || !k_scale_offsets || !workspace)
         return JA_ERR_INVALID_ARG;

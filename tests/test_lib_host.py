@@ -75,6 +75,8 @@ def test_fwd_rejects_host_visible_errors(lib):
     assert fwd(lib, q=FAKE + 2) == INVALID  # misaligned
     assert fwd(lib, ws_bytes=16) == WORKSPACE
     assert fwd(lib, Tq=1 << 40) == UNSUPPORTED
+    assert fwd(lib, H=(1 << 20) // 64 + 1) == UNSUPPORTED  # token rows beyond 2^20 elements
+    assert fwd(lib, H=(1 << 20) // 64) == WORKSPACE         # the largest accepted row
     # nothing to do: no launch, success
     assert fwd(lib, B=0, Tq=0) == OK
     assert fwd(lib, Tq=0) == OK
@@ -103,6 +105,7 @@ def test_bwd_rejects_host_visible_errors(lib):
     assert bwd(lib, ws_bytes=16) == WORKSPACE
     assert bwd(lib, gdtype=0, ws_bytes=16) == WORKSPACE   # fp32 gradients accepted
     assert bwd(lib, B=0) == OK
+    assert bwd(lib, H=(1 << 20) // 64 + 1) == UNSUPPORTED
 
 
 def test_noalloc_rejects_sizes_beyond_its_buffer(lib):
