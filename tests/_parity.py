@@ -15,6 +15,11 @@ Tolerances:
     the bound plus 2e-3 instead of 2e-2; every other element stays at 2e-2.
   * the pointwise backward (gradients that are unnormalised sums over up to Lq
     terms) is also held to the rounding bound on every element (bounded=True).
+  * the mean bound 2e-3 is the stated one for the named workloads. Random batches
+    (mean_rounding=True) may hold gradients summed over hundreds of terms with
+    weights of order one (a handful of keys under many queries), where rounding the
+    exact result to bf16 alone costs a mean error near 2e-3; they are held to 2e-3
+    plus the mean of their elements' rounding bounds 2^-9 (terms + |ref|).
 
 Every comparison is recorded in STATS; the session summary (tests/conftest.py)
 prints the ones a test marks with report=True (the named workloads at full size).
@@ -149,7 +154,7 @@ def _record(what, stats, report):
 
 def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.ndarray | None = None,
             terms: np.ndarray | None = None, bounded: bool = False, report: bool = False,
-            terms_at=None) -> dict:
+            terms_at=None, mean_rounding: bool = False) -> dict:
     """Assert the tolerance for `dtype` ("f32" or "bf16"); returns the error statistics.
 
     sel: [T, H] rows to compare (None: all). terms: per-element sum |w_j u_j| (term_sums);
@@ -175,8 +180,12 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.nda
         assert rel <= F32_REL, f"{what}: relative error {rel:.3e} > {F32_REL} ({stats})"
         return stats
     limited = np.zeros(g.size, dtype=bool)
+    mean_tol = BF16_MEAN
     if terms is not None:
         lim = BF16_ULP * (terms[sel].reshape(-1) + np.abs(r))
+        if mean_rounding:
+            mean_tol = BF16_MEAN + float(lim.mean())
+            stats["mean_tol"] = mean_tol
         limited = lim > 0.5 * BF16_MAX
         allowed = 2.0 * lim + 2e-3
         check = limited | bounded
@@ -204,7 +213,7 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, sel: np.nda
         f"{what}: max abs error {stats['max_abs_strict']:.4e} > {BF16_MAX} ({stats})"
     if terms is not None:
         assert stats["max_err_over_bound"] <= 1.0, f"{what}: error exceeds the bf16 rounding bound ({stats})"
-    assert stats["mean_abs"] <= BF16_MEAN, f"{what}: mean abs error {stats['mean_abs']:.4e} > {BF16_MEAN}"
+    assert stats["mean_abs"] <= mean_tol, f"{what}: mean abs error {stats['mean_abs']:.4e} > {mean_tol:.4e}"
     return stats
 
 

@@ -65,7 +65,7 @@ def run_block(w, block, causal, bwd=True):
     return out, lse, (dq, dk, dv)
 
 
-def check(w, block, causal, bwd=True, pair_mask=None, what="", report=False):
+def check(w, block, causal, bwd=True, pair_mask=None, what="", report=False, mean_rounding=False):
     say(f"[block] {what} B={w.B} H={w.H} d={w.d} T={w.q.shape[0]} block={block} causal={causal} "
         f"dtype={w.dtype} bwd={bwd}")
     out, lse, grads = run_block(w, block, causal, bwd)
@@ -84,7 +84,8 @@ def check(w, block, causal, bwd=True, pair_mask=None, what="", report=False):
             t_out, tq, tk, tv = term_sums(w, "softmax", causal, 0, block=block, pair_mask=pair_mask, grads=True)
         else:
             t_out = term_sums(w, "softmax", causal, 0, block=block, pair_mask=pair_mask)
-    stats["out"] = compare(to_host64(out), ro, w.dtype, f"{what} out", sel, terms=t_out, report=report)
+    stats["out"] = compare(to_host64(out), ro, w.dtype, f"{what} out", sel, terms=t_out, report=report,
+                           mean_rounding=mean_rounding)
     gl = to_host64(lse)[sel]
     assert np.all(np.isfinite(gl)), "every row sees at least its own key"
     lse_err = float(np.max(np.abs(gl - rl[sel]))) if gl.size else 0.0
@@ -92,7 +93,8 @@ def check(w, block, causal, bwd=True, pair_mask=None, what="", report=False):
     assert lse_err <= lse_tol, f"lse {what}: {lse_err} > {lse_tol}"
     if bwd:
         for name, got, ref, terms in (("dq", grads[0], rq, tq), ("dk", grads[1], rk, tk), ("dv", grads[2], rv, tv)):
-            stats[name] = compare(to_host64(got), ref, w.dtype, f"{what} {name}", sel, terms=terms, report=report)
+            stats[name] = compare(to_host64(got), ref, w.dtype, f"{what} {name}", sel, terms=terms, report=report,
+                                  mean_rounding=mean_rounding)
     say(f"      ok lse_err={lse_err:.2e} {stats}")
 
 

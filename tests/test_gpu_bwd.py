@@ -49,7 +49,8 @@ def run_fwd_bwd(w, causal, window, dout=None, act="softmax", grad_dtype=None):
     return dq, dk, dv
 
 
-def check(w, causal, window, pair_mask=None, what="", act="softmax", bounds=False, report=False):
+def check(w, causal, window, pair_mask=None, what="", act="softmax", bounds=False, report=False,
+          mean_rounding=False):
     """Strict bf16 bound on every gradient element. The pointwise backward is also held to
     its per-element rounding bound everywhere (its gradients are unnormalised sums over
     up to Lq terms). bounds (softmax): the edge-case batches pass their term sums, so that
@@ -68,7 +69,7 @@ def check(w, causal, window, pair_mask=None, what="", act="softmax", bounds=Fals
     stats = {}
     for name, got, ref, terms, sel in (("dq", dq, rq, tq, selq), ("dk", dk, rk, tk, selk), ("dv", dv, rv, tv, selk)):
         stats[name] = compare(to_host64(got), ref, w.dtype, f"{what} {name}", sel, terms=terms, bounded=pointwise,
-                              report=report)
+                              report=report, mean_rounding=mean_rounding)
     say(f"      ok {stats}")
 
 

@@ -46,7 +46,8 @@ def run_fwd(w, act=None, causal=None, window=None, guard=True):
     return out, lse
 
 
-def check_against_oracle(w, act, causal, window, pair_mask=None, what="", bounds=False, report=False):
+def check_against_oracle(w, act, causal, window, pair_mask=None, what="", bounds=False, report=False,
+                         mean_rounding=False):
     """Strict bf16 / fp32 bound on every compared element. bounds: the edge-case batches
     (rows with few visible keys) pass their term sums, so that elements whose own bf16
     rounding bound exceeds half the tolerance are held to that bound instead."""
@@ -58,7 +59,8 @@ def check_against_oracle(w, act, causal, window, pair_mask=None, what="", bounds
     sel = rows_of_pairs(w.q_offsets, w.H, pair_mask)
     got = to_host64(out)
     terms = term_sums(w, act, causal, window, pair_mask=pair_mask) if bounds and w.dtype == "bf16" else None
-    stats = compare(got, ref_out, w.dtype, f"out {what}", sel, terms=terms, report=report)
+    stats = compare(got, ref_out, w.dtype, f"out {what}", sel, terms=terms, report=report,
+                    mean_rounding=mean_rounding)
     if act == "softmax":
         gl = to_host64(lse)
         fin = np.isfinite(ref_lse) & sel
