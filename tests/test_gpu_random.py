@@ -14,6 +14,7 @@ from jagged_attention_recsys_amd import workloads as W
 from test_gpu_block import check as check_block
 from test_gpu_bwd import check as check_bwd
 from test_gpu_fwd import check_against_oracle
+from test_gpu_mxfp8 import check as check_mx
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +73,12 @@ def test_random_block_attention(seed):
     d = int(rng.choice([32, 64, 128]))
     w = W.make_case(L, None, H=int(rng.integers(1, 4)), d=d, dtype=W.BF16, seed=seed, with_dout=True)
     check_block(w, block, causal, what=f"random block {seed} block={block}", mean_rounding=True)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_mxfp8_fwd(seed):
+    # MXFP8 forward (d = 128, softmax) on random ragged self and cross batches, held to
+    # the derived bound of the MXFP8 tests.
+    c = draw(300 + seed)
+    w = W.make_case(c["lq"], c["lk"], H=c["H"], d=128, dtype=W.BF16, seed=seed)
+    check_mx(w, c["causal"], c["window"], what=f"random mxfp8 {seed} {c['kind']}")
