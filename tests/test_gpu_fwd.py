@@ -116,6 +116,26 @@ def test_short_queries_split_layout(d, act, causal, window):
     check_against_oracle(w, act, causal, window, what="split", bounds=True)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("act,causal,window", [("softmax", True, 0), ("softmax", False, 300), ("silu", True, 0),
+                                               ("gelu", False, 0)])
+def test_mixed_batch_long_queries_split_layout(d, act, causal, window):
+    # The layout follows from the batch's totals: a few long query sequences among
+    # many short ones keep the mean query length short, so the long ones also run
+    # through the split layout's 32-row items (query tiles far past the first,
+    # diagonal and window stages across many key slices, a ragged last tile).
+    rng = np.random.default_rng(7 * d + window)
+    lq = rng.integers(0, 9, size=100)
+    lk = rng.integers(0, 400, size=100)
+    lq[5], lk[5] = 1500, 1500  # self-attention-like
+    lq[40], lk[40] = 1111, 1700  # Lq != Lk
+    lq[41], lk[41] = 700, 0  # no keys
+    w = W.make_case(lq, lk, H=2, d=d, dtype=W.BF16, seed=d + window)
+    bm, bn = ja.fwd_tile_shape(w.B, d, w.q.shape[0], w.k.shape[0], act)
+    assert bm == 32, "mean query length <= 48 should take the split layout"
+    check_against_oracle(w, act, causal, window, what="mixed-split", bounds=True)
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("act,causal,window", [("silu", False, 0), ("gelu", False, 0), ("softmax", False, 0),
                                                ("softmax", True, 0), ("silu", True, 30), ("softmax", False, 50)])
