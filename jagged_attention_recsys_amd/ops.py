@@ -6,6 +6,8 @@ points in include/jagged_attn.h.
 """
 from __future__ import annotations
 
+import functools
+import inspect
 import math
 
 import torch
@@ -32,6 +34,26 @@ def _stream(device: torch.device, stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return int(stream.cuda_stream)
+
+
+def _on_stream(fn):
+    """Run an entry point with `stream` (a torch.cuda.Stream, when given) as torch's
+    current stream, so that the tensors it allocates (workspace, outputs) belong to
+    the stream its kernels run on: freed on return, a workspace is not handed to other
+    work on another stream while those kernels still use it, and any fill of such a
+    tensor is ordered before them. Inputs produced on another stream are the caller's
+    to order, as for any torch operation."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+
+    return wrapper
 
 
 def _check(name: str, t, dtype=None, shape=None, dim=None, device=None) -> None:
@@ -73,6 +95,7 @@ def fwd_workspace_size(B, H, d, Tq, Tk, act="softmax", causal=False, window=0, d
                                                  DTYPE[dtype]))
 
 
+@_on_stream
 def jagged_attn_fwd(q, k, v, q_offsets, k_offsets, act="softmax", causal=False, window=0, scale=None,
                     out=None, lse=None, workspace=None, stream=None):
     """Jagged attention forward. q: [Tq,H,d]; k, v: [Tk,H,d]; offsets: int32 [B+1] on the GPU.
@@ -120,6 +143,7 @@ def jagged_attn_fwd(q, k, v, q_offsets, k_offsets, act="softmax", causal=False, 
     return out, (lse if a == 0 else None)
 
 
+@_on_stream
 def jagged_attn_fwd_noalloc(q, k, v, q_offsets, k_offsets, out, lse=None, act="softmax", causal=False, window=0,
                             scale=None, stream=None):
     """jagged_attn_fwd without a workspace: the library uses its fixed per-GPU device
@@ -162,6 +186,7 @@ def bwd_workspace_size(B, H, d, Tq, Tk, act="softmax", causal=False, window=0, d
                                                  DTYPE[dtype]))
 
 
+@_on_stream
 def jagged_attn_bwd(q, k, v, out, dout, lse, q_offsets, k_offsets, act="softmax", causal=False, window=0,
                     scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None, grad_dtype=None):
     """Backward of jagged_attn_fwd. Returns (dq, dk, dv), of q's dtype or of
@@ -227,6 +252,7 @@ def block_attn_workspace_size(B, H, d, T, block, causal=False, dtype=torch.bfloa
     return int(_lib.load().ja_block_attn_workspace_size(B, H, d, T, int(block), int(bool(causal)), DTYPE[dtype]))
 
 
+@_on_stream
 def jagged_block_attn_fwd(q, k, v, offsets, block, causal=False, scale=None, out=None, lse=None,
                           workspace=None, stream=None, return_lse=True):
     """Block-diagonal self-attention forward (softmax): each block of ``block`` tokens
@@ -269,6 +295,7 @@ def jagged_block_attn_fwd(q, k, v, offsets, block, causal=False, scale=None, out
     return out, lse
 
 
+@_on_stream
 def jagged_block_attn_bwd(q, k, v, out, dout, lse, offsets, block, causal=False, scale=None, dq=None, dk=None,
                           dv=None, workspace=None, stream=None):
     """Backward of jagged_block_attn_fwd. Returns (dq, dk, dv).
@@ -313,6 +340,7 @@ def jagged_block_attn_bwd(q, k, v, out, dout, lse, offsets, block, causal=False,
     return dq, dk, dv
 
 
+@_on_stream
 def mxfp8_quantize(x, offsets, stream=None):
     """MXFP8 quantization with [32, 32] blocks (32 tokens of one sequence x 32 channels
     of one head). x: bf16 [T,H,d] (d a multiple of 32); offsets: int32 [B+1].
@@ -341,6 +369,7 @@ def mxfp8_quantize(x, offsets, stream=None):
     return x8, scales, soff
 
 
+@_on_stream
 def jagged_attn_fwd_mxfp8(q8, q_scales, q_scale_offsets, k8, k_scales, k_scale_offsets, v8, v_scales, q_offsets,
                           k_offsets, causal=False, window=0, scale=None, out=None, lse=None, workspace=None,
                           stream=None, return_lse=True):
@@ -406,6 +435,7 @@ def fwd_tile_shape(B, d, Tq, Tk, act="softmax", dtype=torch.bfloat16):
     return bm.value, bn.value
 
 
+@_on_stream
 def fwd_schedule(q_offsets, k_offsets, H, d, Tq, Tk, act="softmax", causal=False, window=0,
                  dtype=torch.bfloat16, stream=None):
     """Run only the forward's tile scheduler; returns the (sequence, tile) pairs as an int32 [n,2] GPU tensor."""
@@ -431,6 +461,7 @@ def fwd_schedule(q_offsets, k_offsets, H, d, Tq, Tk, act="softmax", causal=False
     return items[:n]
 
 
+@_on_stream
 def validate_offsets(offsets, T, stream=None) -> bool:
     if not isinstance(offsets, torch.Tensor) or offsets.dim() != 1 or offsets.numel() < 1:
         raise ValueError("offsets must be an int32 [B+1] tensor")
