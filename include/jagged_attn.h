@@ -41,7 +41,12 @@
  * library allocates nothing per call and keeps no pointer after returning. All
  * work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
  * the call returns without synchronising: inputs must stay valid and outputs
- * untouched until the stream has passed the call.
+ * untouched until the stream has passed the call. Outputs and the workspace must
+ * not share memory with any input or with each other (inputs may share memory
+ * with each other): kernels of one call read inputs after others have written
+ * outputs (the backward's dK/dV pass reads Q and dO after its dQ pass has written
+ * dQ), so overlapping buffers give undefined results. The library does not check
+ * this; the Python binding refuses such calls.
  *
  * Errors. Status codes only: no exceptions cross the ABI, nothing aborts or
  * prints. Problems visible on the host (null pointers, unsupported d or dtype,

@@ -74,6 +74,23 @@ def _check(name: str, t, dtype=None, shape=None, dim=None, device=None) -> None:
         raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
+def _span(t):
+    n = t.numel() * t.element_size()
+    return (t.data_ptr(), t.data_ptr() + n) if n else None
+
+
+def _disjoint(writes: dict, reads: dict) -> None:
+    """Raise ValueError if a buffer the call writes shares memory with another buffer of
+    the call (outputs may not alias inputs or each other: the backward's dK/dV pass,
+    for one, reads Q and dO after its dQ pass has written dQ)."""
+    w = [(n, _span(t)) for n, t in writes.items() if t is not None]
+    r = [(n, _span(t)) for n, t in reads.items() if t is not None]
+    for i, (n, a) in enumerate(w):
+        for m, b in w[i + 1:] + r:
+            if a and b and a[0] < b[1] and b[0] < a[1]:
+                raise ValueError(f"{n} overlaps {m}: outputs must not share memory with inputs or other outputs")
+
+
 def _on_gpu(name: str, t) -> None:
     """The last check before a launch: every other tensor is on t's device."""
     if not t.is_cuda:
@@ -134,6 +151,7 @@ def jagged_attn_fwd(q, k, v, q_offsets, k_offsets, act="softmax", causal=False, 
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
+    _disjoint(dict(out=out, lse=lse, workspace=workspace), dict(q=q, k=k, v=v, q_offsets=q_offsets, k_offsets=k_offsets))
     _on_gpu("q", q)
     status = lib.jagged_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(k_offsets), B, H, d, Tq, Tk,
                                  a, int(bool(causal)), int(window), float(scale), DTYPE[dtype], _ptr(out),
@@ -173,6 +191,7 @@ def jagged_attn_fwd_noalloc(q, k, v, q_offsets, k_offsets, out, lse=None, act="s
         _check("lse", lse, torch.float32, shape=(Tq, H), device=dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _disjoint(dict(out=out, lse=lse), dict(q=q, k=k, v=v, q_offsets=q_offsets, k_offsets=k_offsets))
     _on_gpu("q", q)
     status = lib.jagged_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(k_offsets), B, H, d, Tq,
                                          Tk, a, int(bool(causal)), int(window), float(scale), DTYPE[dtype],
@@ -239,6 +258,7 @@ def jagged_attn_bwd(q, k, v, out, dout, lse, q_offsets, k_offsets, act="softmax"
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
+    _disjoint(dict(dq=dq, dk=dk, dv=dv, workspace=workspace), dict(q=q, k=k, v=v, out=out, dout=dout, lse=lse, q_offsets=q_offsets, k_offsets=k_offsets))
     _on_gpu("q", q)
     status = lib.jagged_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(q_offsets),
                                  _ptr(k_offsets), B, H, d, Tq, Tk, a, int(bool(causal)), int(window),
@@ -287,6 +307,7 @@ def jagged_block_attn_fwd(q, k, v, offsets, block, causal=False, scale=None, out
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
+    _disjoint(dict(out=out, lse=lse, workspace=workspace), dict(q=q, k=k, v=v, offsets=offsets))
     _on_gpu("q", q)
     status = lib.jagged_block_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, d, T, int(block),
                                        int(bool(causal)), float(scale), DTYPE[dtype], _ptr(out), _ptr(lse),
@@ -331,6 +352,7 @@ def jagged_block_attn_bwd(q, k, v, out, dout, lse, offsets, block, causal=False,
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
+    _disjoint(dict(dq=dq, dk=dk, dv=dv, workspace=workspace), dict(q=q, k=k, v=v, out=out, dout=dout, lse=lse, offsets=offsets))
     _on_gpu("q", q)
     status = lib.jagged_block_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                        _ptr(offsets), B, H, d, T, int(block), int(bool(causal)), float(scale),
@@ -413,6 +435,7 @@ def jagged_attn_fwd_mxfp8(q8, q_scales, q_scale_offsets, k8, k_scales, k_scale_o
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
+    _disjoint(dict(out=out, lse=lse, workspace=workspace), dict(q8=q8, q_scales=q_scales, k8=k8, k_scales=k_scales, v8=v8, v_scales=v_scales, q_offsets=q_offsets, k_offsets=k_offsets, q_scale_offsets=q_scale_offsets, k_scale_offsets=k_scale_offsets))
     _on_gpu("q8", q8)
     status = lib.jagged_attn_fwd_mxfp8(_ptr(q8), _ptr(q_scales), _ptr(q_scale_offsets), _ptr(k8), _ptr(k_scales),
                                        _ptr(k_scale_offsets), _ptr(v8), _ptr(v_scales), _ptr(q_offsets),

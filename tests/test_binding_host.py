@@ -87,3 +87,25 @@ def test_mxfp8_shapes():
     raises("must be a GPU tensor", f, q8, qs, qo, k8, ks, ko, v8, vs, qo, ko)
     raises("d must be a positive multiple of 32", ja.mxfp8_quantize, torch.zeros(5, 1, 48, dtype=BF), offs(0, 5))
     raises("x must be torch.bfloat16", ja.mxfp8_quantize, torch.zeros(5, 1, 64), offs(0, 5))
+
+
+def test_outputs_must_not_alias():
+    # A written buffer that shares memory with an input or another output is refused
+    # before anything is launched (checked on CPU tensors, before the device check).
+    q, k, v = qkv()
+    o, do, lse = torch.zeros_like(q), torch.zeros_like(q), torch.zeros(10, 2)
+    raises("out overlaps q", ja.jagged_attn_fwd, q, k, v, QO, KO, out=q)
+    raises("dq overlaps q", ja.jagged_attn_bwd, q, k, v, o, do, lse, QO, KO, dq=q)
+    dkv = torch.zeros_like(k)
+    raises("dk overlaps dv", ja.jagged_attn_bwd, q, k, v, o, do, lse, QO, KO, dk=dkv, dv=dkv)
+    raises("dv overlaps v", ja.jagged_attn_bwd, q, k, v, o, do, lse, QO, KO, dv=v)
+    # a view into the middle of an input counts as well
+    big = torch.zeros(12, 2, 64, dtype=BF)
+    raises("out overlaps q", ja.jagged_attn_fwd, big[2:], k, v, QO, KO, out=big[:10])
+    ob = offs(0, 4, 10)
+    raises("dq overlaps dout", ja.jagged_block_attn_bwd, q, k[:10], v[:10], None, do, None, ob, 64, dq=do)
+    raises("out overlaps k", ja.jagged_block_attn_fwd, q, k[:10], v[:10], ob, 64, out=k[:10])
+    raises("out overlaps q", ja.jagged_attn_fwd_noalloc, q, k, v, QO, KO, q)
+    # disjoint views of one buffer are fine (the device check comes next)
+    raises("must be a GPU tensor", ja.jagged_attn_bwd, q, k, v, o, do, lse, QO, KO, dk=big[:12].clone(),
+           dv=torch.zeros_like(v))
