@@ -43,11 +43,11 @@ def _on_stream(fn):
     work on another stream while those kernels still use it, and any fill of such a
     tensor is ordered before them. Inputs produced on another stream are the caller's
     to order, as for any torch operation."""
-    sig = inspect.signature(fn)
+    pos = list(inspect.signature(fn).parameters).index("stream")
 
     @functools.wraps(fn)
     def wrapper(*args, **kwargs):
-        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        stream = args[pos] if len(args) > pos else kwargs.get("stream")
         if stream is None:
             return fn(*args, **kwargs)
         with torch.cuda.stream(stream):
