@@ -151,7 +151,8 @@ def jagged_attn_fwd(q, k, v, q_offsets, k_offsets, act="softmax", causal=False, 
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
-    _disjoint(dict(out=out, lse=lse, workspace=workspace), dict(q=q, k=k, v=v, q_offsets=q_offsets, k_offsets=k_offsets))
+    _disjoint(dict(out=out, lse=lse, workspace=workspace),
+              dict(q=q, k=k, v=v, q_offsets=q_offsets, k_offsets=k_offsets))
     _on_gpu("q", q)
     status = lib.jagged_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(k_offsets), B, H, d, Tq, Tk,
                                  a, int(bool(causal)), int(window), float(scale), DTYPE[dtype], _ptr(out),
@@ -258,7 +259,8 @@ def jagged_attn_bwd(q, k, v, out, dout, lse, q_offsets, k_offsets, act="softmax"
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
-    _disjoint(dict(dq=dq, dk=dk, dv=dv, workspace=workspace), dict(q=q, k=k, v=v, out=out, dout=dout, lse=lse, q_offsets=q_offsets, k_offsets=k_offsets))
+    _disjoint(dict(dq=dq, dk=dk, dv=dv, workspace=workspace),
+              dict(q=q, k=k, v=v, out=out, dout=dout, lse=lse, q_offsets=q_offsets, k_offsets=k_offsets))
     _on_gpu("q", q)
     status = lib.jagged_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(q_offsets),
                                  _ptr(k_offsets), B, H, d, Tq, Tk, a, int(bool(causal)), int(window),
@@ -352,7 +354,8 @@ def jagged_block_attn_bwd(q, k, v, out, dout, lse, offsets, block, causal=False,
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
-    _disjoint(dict(dq=dq, dk=dk, dv=dv, workspace=workspace), dict(q=q, k=k, v=v, out=out, dout=dout, lse=lse, offsets=offsets))
+    _disjoint(dict(dq=dq, dk=dk, dv=dv, workspace=workspace),
+              dict(q=q, k=k, v=v, out=out, dout=dout, lse=lse, offsets=offsets))
     _on_gpu("q", q)
     status = lib.jagged_block_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                        _ptr(offsets), B, H, d, T, int(block), int(bool(causal)), float(scale),
@@ -435,7 +438,9 @@ def jagged_attn_fwd_mxfp8(q8, q_scales, q_scale_offsets, k8, k_scales, k_scale_o
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     else:
         _check_workspace(workspace, ws_bytes, dev)
-    _disjoint(dict(out=out, lse=lse, workspace=workspace), dict(q8=q8, q_scales=q_scales, k8=k8, k_scales=k_scales, v8=v8, v_scales=v_scales, q_offsets=q_offsets, k_offsets=k_offsets, q_scale_offsets=q_scale_offsets, k_scale_offsets=k_scale_offsets))
+    _disjoint(dict(out=out, lse=lse, workspace=workspace),
+              dict(q8=q8, q_scales=q_scales, k8=k8, k_scales=k_scales, v8=v8, v_scales=v_scales, q_offsets=q_offsets,
+                   k_offsets=k_offsets, q_scale_offsets=q_scale_offsets, k_scale_offsets=k_scale_offsets))
     _on_gpu("q8", q8)
     status = lib.jagged_attn_fwd_mxfp8(_ptr(q8), _ptr(q_scales), _ptr(q_scale_offsets), _ptr(k8), _ptr(k_scales),
                                        _ptr(k_scale_offsets), _ptr(v8), _ptr(v_scales), _ptr(q_offsets),
