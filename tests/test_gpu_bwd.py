@@ -194,6 +194,35 @@ def test_unseen_keys_get_zero_gradients():
     check(w, True, 0, what="unseen")
 
 
+@pytest.mark.parametrize("act", ["softmax", "silu"])
+def test_batch_without_keys(act):
+    # Every sequence has queries but no keys (Tk = 0): out is 0 (lse -inf for softmax),
+    # and so are the query gradients; there is no key gradient to write.
+    w = case([5, 40, 0, 130], [0, 0, 0, 0], H=2, d=64, seed=12)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    qo, ko = to_dev(w.q_offsets), to_dev(w.k_offsets)
+    out, lse = ja.jagged_attn_fwd(q, k, v, qo, ko, act=act, causal=True)
+    torch.cuda.synchronize()
+    assert k.shape[0] == 0 and torch.count_nonzero(out).item() == 0
+    if act == "softmax":
+        assert torch.isneginf(lse).all()
+    dq, dk, dv = run_fwd_bwd(w, True, 0, act=act)
+    assert torch.count_nonzero(dq).item() == 0 and dk.shape[0] == 0 and dv.shape[0] == 0
+
+
+def test_batch_without_queries():
+    # Sequences with keys but no queries (Tq = 0): nothing to compute or write; the key
+    # gradients are zero.
+    w = case([0, 0, 0], [7, 300, 0], H=2, d=128, seed=13)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    qo, ko = to_dev(w.q_offsets), to_dev(w.k_offsets)
+    out, lse = ja.jagged_attn_fwd(q, k, v, qo, ko, causal=False)
+    assert out.shape[0] == 0 and lse.shape[0] == 0
+    dq, dk, dv = run_fwd_bwd(w, False, 0)
+    assert dq.shape[0] == 0
+    assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
+
+
 def test_bitwise_determinism_and_permutation():
     lq = np.array([300, 0, 129, 64, 17, 700])
     w = case(lq, d=128, seed=8)
