@@ -145,6 +145,34 @@ def term_sums(w, act, causal, window, block=0, pair_mask=None, grads=False):
     return (t_out, t_dq, t_dk, t_dv) if grads else t_out
 
 
+def stored_out_terms(w, causal, window, got_out, ref_out):
+    """Per gradient element, a bound on what the softmax backward's D_i = dO_i . O_i moves
+    when O is the forward's stored output (bf16) rather than the exact one: with
+    e_i = sum_c |dO_ic| |O_stored,ic - O_exact,ic|, dS_ij moves by at most P_ij e_i, so
+    dQ_ic by scale e_i sum_j P_ij |K_jc| and dK_jc by scale sum_i P_ij e_i |Q_ic| (dV does
+    not use D). got_out, ref_out: [Tq, H, d] fp64. Returns (ext_dq, ext_dk)."""
+    ext_dq = np.zeros(w.q.shape, dtype=np.float64)
+    ext_dk = np.zeros(w.k.shape, dtype=np.float64)
+    for b in range(w.B):
+        q0, q1 = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+        k0, k1 = int(w.k_offsets[b]), int(w.k_offsets[b + 1])
+        Lq, Lk = q1 - q0, k1 - k0
+        if Lq == 0 or Lk == 0:
+            continue
+        vis = _visible(Lq, Lk, causal, window, 0)
+        for h in range(w.H):
+            qb, kb = _f64(w.q[q0:q1, h]), _f64(w.k[k0:k1, h])
+            zm = np.where(vis, w.scale * qb @ kb.T, -np.inf)
+            m = zm.max(axis=1, keepdims=True)
+            p = np.where(vis, np.exp(zm - np.where(np.isfinite(m), m, 0.0)), 0.0)
+            l = p.sum(axis=1, keepdims=True)
+            p = p / np.where(l > 0, l, 1.0)
+            e = (np.abs(_f64(w.dout[q0:q1, h])) * np.abs(got_out[q0:q1, h] - ref_out[q0:q1, h])).sum(axis=1)
+            ext_dq[q0:q1, h] = w.scale * e[:, None] * (p @ np.abs(kb))
+            ext_dk[k0:k1, h] = w.scale * (p * e[:, None]).T @ np.abs(qb)
+    return ext_dq, ext_dk
+
+
 def _record(what, stats, report):
     stats = dict(stats)
     stats["what"] = what

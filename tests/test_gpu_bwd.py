@@ -17,7 +17,8 @@ import torch
 import jagged_attention_recsys_amd as ja
 import oracle
 from jagged_attention_recsys_amd import workloads as W
-from _parity import compare, rows_of_pairs, say, softmax_grad_terms_at, term_sums, to_dev, to_host64
+from _parity import (compare, rows_of_pairs, say, softmax_grad_terms_at, stored_out_terms, term_sums, to_dev,
+                     to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -177,6 +178,41 @@ def test_workload3_silu_cross_bwd_every_pair():
 def test_workload4_gelu_pooled_bwd_every_pair():
     w = W.with_upstream_gradient(W.workload(4), 44)
     check(w, w.causal, w.window, what="w4 bwd", act=w.act, report=True)
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 100)])
+def test_peaky_softmax_large_logits(causal, window):
+    # Scale 0.5 at d = 128 (score standard deviation near 6): nearly one-hot weights. The
+    # backward forms D_i = dO_i . O_i from the stored bf16 output, as the pages define it;
+    # with one dominant key, dP_ij - D_i cancels to a small difference of two terms near
+    # 10, so O's rounding (about sqrt(d) 2^-9 |O| in D_i) reaches dQ and dK at 1e-1 where
+    # the gradients are near 18. Every element is held to its bf16 rounding bound plus
+    # that derived term (stored_out_terms); dV, which does not use D, to its rounding
+    # bound alone.
+    w = case([300, 700, 64, 1], H=2, d=128, seed=79 + window)
+    w.attn_scale = 0.5
+    say(f"[bwd] peaky B={w.B} H={w.H} d={w.d} causal={causal} window={window} scale={w.scale}")
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    qo, ko = to_dev(w.q_offsets), to_dev(w.k_offsets)
+    out, lse = ja.jagged_attn_fwd(q, k, v, qo, ko, causal=causal, window=window, scale=w.scale)
+    dq, dk, dv = ja.jagged_attn_bwd(q, k, v, out, to_dev(w.dout), lse, qo, ko, causal=causal, window=window,
+                                    scale=w.scale)
+    torch.cuda.synchronize()
+    ref_out, _ = oracle.fwd(w.q, w.k, w.v, w.q_offsets, w.k_offsets, "softmax", causal, window, w.scale)
+    _, _, rq, rk, rv = oracle.bwd(w.q, w.k, w.v, w.dout, w.q_offsets, w.k_offsets, "softmax", causal, window,
+                                  w.scale)
+    _, tq, tk, tv = term_sums(w, "softmax", causal, window, grads=True)
+    eq, ek = stored_out_terms(w, causal, window, to_host64(out), ref_out)
+    for name, got, ref, terms, extra in (("dq", dq, rq, tq, eq), ("dk", dk, rk, tk, ek), ("dv", dv, rv, tv, 0.0)):
+        err = np.abs(to_host64(got) - ref)
+        lim = 2.0 ** -9 * (terms + np.abs(ref))
+        tol = 2.0 * lim + 2e-3 + 1.01 * extra
+        assert np.all(np.isfinite(err)), name
+        worst = float(np.max(err / tol))
+        say(f"      {name}: max abs {err.max():.3e} (|ref| up to {np.abs(ref).max():.1f}), mean abs {err.mean():.3e}, "
+            f"max error / bound {worst:.3f}")
+        assert worst <= 1.0, f"peaky {name}: error {worst:.3f} x its bound"
+        assert err.mean() <= 2e-3 + float(np.mean(lim + extra)), f"peaky {name}: mean {err.mean():.3e}"
 
 
 def test_identical_keys_give_zero_dq():

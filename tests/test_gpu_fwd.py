@@ -152,6 +152,16 @@ def test_short_keys_chunked_layout(d, act, causal, window):
     check_against_oracle(w, act, causal, window, what="chunked", bounds=True)
 
 
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 100)])
+def test_peaky_softmax_large_logits(causal, window):
+    # Scale 1 at d = 128: scores with a standard deviation near 11 and row maxima near
+    # 35, so the weights are nearly one-hot, the running max rises in large steps and
+    # most weights underflow.
+    w = W.make_case([300, 700, 64, 1], H=2, d=128, dtype=W.BF16, seed=77 + window)
+    w.attn_scale = 1.0
+    check_against_oracle(w, "softmax", causal, window, what="peaky")
+
+
 def test_workload1_fp32_softmax_and_silu():
     w = W.workload(1)
     check_against_oracle(w, "softmax", False, 0, what="w1 fwd", report=True)
