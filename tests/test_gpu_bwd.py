@@ -20,6 +20,8 @@ from jagged_attention_recsys_amd import workloads as W
 from _parity import (compare, rows_of_pairs, say, softmax_grad_terms_at, stored_out_terms, term_sums, to_dev,
                      to_host64)
 
+from test_gpu_fwd import check_against_oracle
+
 pytestmark = pytest.mark.gpu
 
 GUARD = 2
@@ -213,6 +215,16 @@ def test_peaky_softmax_large_logits(causal, window):
             f"max error / bound {worst:.3f}")
         assert worst <= 1.0, f"peaky {name}: error {worst:.3f} x its bound"
         assert err.mean() <= 2e-3 + float(np.mean(lim + extra)), f"peaky {name}: mean {err.mean():.3e}"
+
+
+@pytest.mark.parametrize("H,d,window", [(16, 64, 0), (33, 32, 50), (12, 128, 200)])
+def test_many_heads(H, d, window):
+    # Head counts beyond the named workloads, odd ones included: row strides of H d
+    # elements, per-head offsets, and work lists whose (sequence, head) items no longer
+    # map onto the XCD-local queues one head per queue.
+    w = case([130, 1, 0, 257, 64], H=H, d=d, seed=H + d)
+    check_against_oracle(w, "softmax", True, window, what=f"H={H}", bounds=True)
+    check(w, True, window, what=f"H={H}", bounds=True)
 
 
 def test_identical_keys_give_zero_dq():
